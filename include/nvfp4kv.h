@@ -1,0 +1,166 @@
+/*
+ * nvfp4kv.h -- C ABI of the MI355X (gfx950) NVFP4 KV-cache chunk-attention library.
+ *
+ * Sources of the operations (pages: "LongLive-2.0: An NVFP4 Parallel Infrastructure
+ * for Long Video Generation", the paper text and a reading note on it):
+ *   - NVFP4 format: paper section 2.2 "NVFP4 Training" (16-element blocks, E4M3 block
+ *     scale with max 448, E2M1 elements with max 6) and the reading note, section II
+ *     "The NVFP4 quantization format" (one FP32 tensor scale x one E4M3 scale per 16
+ *     elements x the E2M1 element).
+ *   - Per-chunk KV quantization and in-kernel dequantization: paper section 1 and the
+ *     reading note, "The inference infrastructure" (frame-chunk granularity,
+ *     9/8 T_c H d bytes for K and V, dequantization inside the attention kernel).
+ *   - Sink + window cache: paper section 4.2 "Inference with Multi-Shot Attention Sink"
+ *     (sliding window of W chunks, global sink of the first S_g frames, effective key
+ *     set = sink U window with duplicates removed).
+ *   - Chunk attention: paper section 2.1 (a noisy chunk attends to the clean history
+ *     and to its own tokens) with section 4.2's cache as the history.
+ *
+ * Conventions for every entry point:
+ *   - Pointers are device pointers owned by the caller unless marked "host".  The
+ *     library never allocates device memory (no hipMalloc); callers bring inputs,
+ *     outputs, cache storage and workspace.
+ *   - bf16 tensors are passed as their uint16 bit patterns; all tensors are dense and
+ *     row-major in the order of their stated shape.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the default stream).  Every
+ *     call validates its arguments on the host first, then enqueues work on `stream`
+ *     and returns without synchronizing.  An argument error returns a negative status
+ *     before anything is enqueued.  A HIP launch error returns NVFP4KV_EHIP; a device
+ *     fault shows at the caller's next synchronization.
+ *   - Return value: 0 (NVFP4KV_OK) or a negative nvfp4kv_status.  No exceptions, no
+ *     abort, no printing.
+ *   - A kvcache handle must not be used by two threads, or from two streams whose work
+ *     may overlap, at the same time.
+ */
+#ifndef NVFP4KV_H
+#define NVFP4KV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  NVFP4KV_OK = 0,
+  NVFP4KV_EINVAL = -1,    /* null pointer, non-positive or unsupported size        */
+  NVFP4KV_ESHAPE = -2,    /* shapes inconsistent with the cache configuration      */
+  NVFP4KV_ECAPACITY = -3, /* request does not fit (workspace, window, frame count) */
+  NVFP4KV_ESTATE = -4,    /* e.g. evicting more frames than the window holds       */
+  NVFP4KV_EHIP = -5       /* HIP runtime / launch error                            */
+} nvfp4kv_status;
+
+/* Static, NUL-terminated description of a status code (host). */
+const char *nvfp4kv_strerror(int status);
+
+/* Library version as "major.minor.patch" (host, static string). */
+const char *nvfp4kv_version(void);
+
+/* ------------------------------------------------------------------------------
+ * Standalone NVFP4 codec of one tensor (paper section 2.2; reading note section II).
+ *
+ *   x            bf16 [H, T, D], D % 32 == 0, H, T >= 1 (T may be odd).
+ *   codes        uint8 [H, T, D/2]: element 2i in the low nibble, 2i+1 in the high
+ *                nibble; nibble = sign << 3 | E2M1 magnitude code.
+ *   scales       uint8 [H, T, D/16]: raw E4M3FN bytes of the block scales.
+ *   tensor_scale float[1]: s_t = amax(|x|) / (6 * 448) over the whole tensor.
+ * Recipe (fp32, round-to-nearest-even, no fast math): block scale
+ *   bs = (block amax / 6) / s_t rounded to E4M3 (saturating at 448), element code =
+ *   E2M1(|x| / (E4M3(bs) * s_t)) (saturating at 6); a block whose E4M3(bs) * s_t is 0
+ *   gets all-zero magnitudes with the element signs kept.  x must be finite.
+ *   workspace    device scratch of >= nvfp4_quantize_workspace_bytes() bytes, zero-
+ *                filled by the caller before its first use; every call leaves it
+ *                ready for the next one.  Calls that share a workspace must not run
+ *                concurrently.
+ * Errors: EINVAL (null pointer, H/T/D out of range, D % 32 != 0), ECAPACITY (workspace
+ * too small), EHIP.
+ * ------------------------------------------------------------------------------ */
+size_t nvfp4_quantize_workspace_bytes(void);
+int nvfp4_quantize_kv(const uint16_t *x, int64_t H, int64_t T, int64_t D, uint8_t *codes,
+                      uint8_t *scales, float *tensor_scale, void *workspace,
+                      size_t workspace_bytes, void *stream);
+
+/* ------------------------------------------------------------------------------
+ * Paged sink + window KV cache (paper section 4.2; reading note "The inference
+ * infrastructure").
+ *
+ * A frame slot holds one latent frame (tokens_per_frame tokens, all heads) of K and V
+ * in NVFP4.  Slots [0, sink_frames) hold the global sink: the first sink_frames frames
+ * ever appended, kept for the life of the cache.  The other window_frames slots form a
+ * FIFO ring of the most recent frames.  Eviction only changes host metadata.
+ *
+ * Supported: n_heads >= 1; head_dim 64 or 128; tokens_per_frame >= 8 and a multiple
+ * of 8; sink_frames >= 0; window_frames >= 1; sink_frames + window_frames <= 64.
+ * ------------------------------------------------------------------------------ */
+typedef struct {
+  int32_t n_heads;
+  int32_t head_dim;
+  int32_t tokens_per_frame;
+  int32_t sink_frames;
+  int32_t window_frames;
+} kvcache_config;
+
+typedef struct kvcache kvcache; /* opaque host object */
+
+/* Device bytes the cache needs: 9/16 byte per cached K or V element (codes + block
+ * scales, i.e. 9/8 T H d for K and V together), plus a per-chunk tensor-scale table
+ * and the quantizer's workspace.  Returns 0 for an unsupported configuration. */
+size_t kvcache_storage_bytes(const kvcache_config *cfg);
+
+/* Creates the host object over caller-owned device storage (>= kvcache_storage_bytes,
+ * 256-byte aligned).  Zero-fills the storage's control words with a blocking copy on
+ * the current device.  Errors: EINVAL, ECAPACITY (storage too small), EHIP. */
+int kvcache_create(const kvcache_config *cfg, void *storage, size_t storage_bytes,
+                   kvcache **out /* host */);
+
+/* Frees the host object only; the storage stays the caller's.  NULL is accepted. */
+int kvcache_destroy(kvcache *c);
+
+/* Appends one chunk of n_frames frames.  k, v: bf16 [H, n_frames * tokens_per_frame, D]
+ * (finite).  K and V each get one FP32 tensor scale computed over the whole chunk (all
+ * heads), then are quantized straight into their frame slots in one kernel.  The first
+ * sink_frames frames ever appended become sinks; each later frame enters the window,
+ * and when the window is full the oldest window frame is evicted first (FIFO).
+ * Errors: EINVAL (null, n_frames < 1), ECAPACITY (more than window_frames frames of
+ * this chunk would enter the window), EHIP. */
+int kvcache_append(kvcache *c, const uint16_t *k, const uint16_t *v, int32_t n_frames,
+                   void *stream);
+
+/* Drops the oldest n_frames window frames (never sinks); metadata only.
+ * Errors: EINVAL (n_frames < 0), ESTATE (fewer than n_frames window frames). */
+int kvcache_evict(kvcache *c, int32_t n_frames);
+
+/* Number of cached tokens in the sink and in the window (host outputs). */
+int kvcache_tokens(const kvcache *c, int64_t *sink_tokens, int64_t *window_tokens);
+
+/* Number of chunks appended so far (the next chunk's index) (host output). */
+int kvcache_chunk_count(const kvcache *c, int32_t *n_chunks);
+
+/* Noisy-chunk attention (paper sections 2.1 and 4.2): for every head,
+ *   out = softmax(q K^T * softmax_scale) V,  K = [cache K ; k_own],  V = [cache V ; v_own]
+ * over all cached tokens (sink and window, NVFP4, dequantized inside the kernel) and
+ * the chunk's own n_q bf16 tokens, with no mask (bidirectional inside the chunk).
+ *   q, k_own, v_own  bf16 [H, n_q, D] (finite; |v_own| < 65504);
+ *   out              fp32 [H, n_q, D];  n_q >= 1;  softmax_scale > 0 and finite.
+ * Errors: EINVAL, EHIP. */
+int chunk_attention(const kvcache *c, const uint16_t *q, const uint16_t *k_own,
+                    const uint16_t *v_own, int64_t n_q, float softmax_scale, float *out,
+                    void *stream);
+
+/* Copies chunk `chunk_index` (0-based append order), which must be fully resident,
+ * out of the cache in the codec's layout: k_codes / v_codes uint8 [H, n*T_f, D/2],
+ * k_scales / v_scales uint8 [H, n*T_f, D/16], k_scale / v_scale float[1] (device),
+ * with n the chunk's frame count.  Device-to-device, on `stream`.
+ * Errors: EINVAL (null), ESTATE (chunk unknown or not fully resident), EHIP. */
+int kvcache_export_chunk(const kvcache *c, int32_t chunk_index, uint8_t *k_codes,
+                         uint8_t *k_scales, uint8_t *v_codes, uint8_t *v_scales,
+                         float *k_scale, float *v_scale, void *stream);
+
+/* Frame count of a resident chunk (host output); ESTATE if not resident. */
+int kvcache_chunk_frames(const kvcache *c, int32_t chunk_index, int32_t *n_frames);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* NVFP4KV_H */

@@ -1,0 +1,374 @@
+// C ABI of libnvfp4kv: argument checks, the sink + window cache metadata, and the
+// hand-off to the gfx950 kernels.  Declared in include/nvfp4kv.h.
+//
+// Cache semantics follow the paper text, section 4.2 "Inference with Multi-Shot
+// Attention Sink": a sliding window of recent frames plus a global sink made of
+// the first S_g frames, kept permanently; the effective key set is their union,
+// each frame stored once.  The reading note's "The inference infrastructure"
+// fixes the per-chunk NVFP4 quantization of K and V (one tensor scale each).
+
+#include <string.h>
+
+#include <map>
+#include <new>
+
+#include "../../include/nvfp4kv.h"
+#include "nvfp4kv_internal.h"
+
+using namespace nvfp4kv;
+
+namespace {
+
+constexpr size_t kAlign = 256;
+
+size_t round_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+struct Layout {
+  int64_t rows;   // token capacity per head
+  size_t kcodes, kscales, vcodes, vscales, table, ws, total;
+};
+
+bool config_ok(const kvcache_config *c) {
+  if (!c) return false;
+  if (c->n_heads < 1 || c->n_heads > 4096) return false;
+  if (c->head_dim != 64 && c->head_dim != 128) return false;
+  if (c->tokens_per_frame < 8 || c->tokens_per_frame % 8 != 0 ||
+      c->tokens_per_frame > (1 << 20))
+    return false;
+  if (c->sink_frames < 0 || c->window_frames < 1) return false;
+  if (c->sink_frames + c->window_frames > kMaxFrames) return false;
+  return true;
+}
+
+bool make_layout(const kvcache_config *c, Layout *L) {
+  if (!config_ok(c)) return false;
+  const int64_t H = c->n_heads, D = c->head_dim;
+  L->rows = int64_t(c->sink_frames + c->window_frames) * c->tokens_per_frame;
+  if (H * L->rows * D > (int64_t(1) << 40)) return false;
+  size_t off = 0;
+  L->kcodes = off;  off = round_up(off + size_t(H * L->rows * D / 2));
+  L->kscales = off; off = round_up(off + size_t(H * L->rows * D / 16));
+  L->vcodes = off;  off = round_up(off + size_t(H * L->rows * D / 2));
+  L->vscales = off; off = round_up(off + size_t(H * L->rows * D / 16));
+  L->table = off;   off = round_up(off + sizeof(float) * 2 * kScaleSlots);
+  L->ws = off;      off = round_up(off + sizeof(QuantWorkspace));
+  L->total = off;
+  return true;
+}
+
+struct FrameRec {
+  int32_t chunk;
+  int32_t frame_in_chunk;
+};
+
+struct ChunkRec {
+  int32_t scale_slot;
+  int32_t n_frames;
+  int32_t resident;
+  int32_t slot[kMaxFrames];   // slot of each frame, -1 once evicted
+};
+
+struct State {
+  int32_t sink_used = 0;
+  int32_t win_head = 0;       // ring position of the oldest window frame
+  int32_t win_count = 0;
+  int32_t next_chunk = 0;
+  FrameRec slot_frame[kMaxFrames];
+  int32_t scale_ref[kScaleSlots] = {0};
+  std::map<int32_t, ChunkRec> chunks;   // resident chunks only
+};
+
+}  // namespace
+
+struct kvcache {
+  kvcache_config cfg;
+  Layout L;
+  uint8_t *base;
+  State st;
+
+  uint8_t *kcodes() const { return base + L.kcodes; }
+  uint8_t *kscales() const { return base + L.kscales; }
+  uint8_t *vcodes() const { return base + L.vcodes; }
+  uint8_t *vscales() const { return base + L.vscales; }
+  float *table() const { return reinterpret_cast<float *>(base + L.table); }
+  QuantWorkspace *ws() const { return reinterpret_cast<QuantWorkspace *>(base + L.ws); }
+  int32_t window_slot(const State &s, int32_t i) const {
+    return cfg.sink_frames + (s.win_head + i) % cfg.window_frames;
+  }
+};
+
+namespace {
+
+// Drops the oldest n window frames of `s` (metadata only).
+void evict_oldest(const kvcache *c, State &s, int32_t n) {
+  for (int32_t i = 0; i < n; ++i) {
+    const int32_t slot = c->window_slot(s, 0);
+    const FrameRec fr = s.slot_frame[slot];
+    auto it = s.chunks.find(fr.chunk);
+    if (it != s.chunks.end()) {
+      ChunkRec &rec = it->second;
+      rec.slot[fr.frame_in_chunk] = -1;
+      rec.resident -= 1;
+      s.scale_ref[rec.scale_slot] -= 1;
+      if (rec.resident == 0) s.chunks.erase(it);
+    }
+    s.win_head = (s.win_head + 1) % c->cfg.window_frames;
+    s.win_count -= 1;
+  }
+}
+
+// Resident frames in effective-key order: sinks, then the window oldest first.
+int collect_frames(const kvcache *c, int32_t *slots) {
+  int n = 0;
+  for (int32_t i = 0; i < c->st.sink_used; ++i) slots[n++] = i;
+  for (int32_t i = 0; i < c->st.win_count; ++i) slots[n++] = c->window_slot(c->st, i);
+  return n;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *nvfp4kv_strerror(int status) {
+  switch (status) {
+    case NVFP4KV_OK: return "ok";
+    case NVFP4KV_EINVAL: return "invalid argument (null pointer or unsupported size)";
+    case NVFP4KV_ESHAPE: return "shape inconsistent with the cache configuration";
+    case NVFP4KV_ECAPACITY: return "request exceeds capacity (workspace, window or frame count)";
+    case NVFP4KV_ESTATE: return "operation not valid in the current cache state";
+    case NVFP4KV_EHIP: return "HIP runtime or kernel launch error";
+    default: return "unknown status";
+  }
+}
+
+const char *nvfp4kv_version(void) { return "0.1.0"; }
+
+size_t nvfp4_quantize_workspace_bytes(void) { return sizeof(QuantWorkspace); }
+
+int nvfp4_quantize_kv(const uint16_t *x, int64_t H, int64_t T, int64_t D, uint8_t *codes,
+                      uint8_t *scales, float *tensor_scale, void *workspace,
+                      size_t workspace_bytes, void *stream) {
+  if (!x || !codes || !scales || !tensor_scale || !workspace) return NVFP4KV_EINVAL;
+  if (H < 1 || T < 1 || D < 32 || D % 32 != 0 || D > 4096) return NVFP4KV_EINVAL;
+  if (H * T * D >= (int64_t(1) << 40) || T > (int64_t(1) << 30) || H > (1 << 20))
+    return NVFP4KV_EINVAL;
+  if (workspace_bytes < sizeof(QuantWorkspace)) return NVFP4KV_ECAPACITY;
+  QuantArgs a;
+  memset(&a, 0, sizeof(a));
+  a.t[0].src = x;
+  a.t[0].codes = codes;
+  a.t[0].scales = scales;
+  a.t[0].tensor_scale = tensor_scale;
+  a.t[0].transposed = 0;
+  a.n_tensors = 1;
+  a.H = int32_t(H);
+  a.T = int32_t(T);
+  a.D = int32_t(D);
+  a.tokens_per_frame = int32_t(T);
+  a.n_frames = 1;
+  a.rows = T;
+  a.frame_slot[0] = 0;
+  a.ws = reinterpret_cast<QuantWorkspace *>(workspace);
+  return launch_quantize(a, stream);
+}
+
+size_t kvcache_storage_bytes(const kvcache_config *cfg) {
+  Layout L;
+  if (!make_layout(cfg, &L)) return 0;
+  return L.total;
+}
+
+int kvcache_create(const kvcache_config *cfg, void *storage, size_t storage_bytes,
+                   kvcache **out) {
+  if (!out) return NVFP4KV_EINVAL;
+  *out = nullptr;
+  Layout L;
+  if (!storage || !make_layout(cfg, &L)) return NVFP4KV_EINVAL;
+  if (reinterpret_cast<uintptr_t>(storage) % kAlign != 0) return NVFP4KV_EINVAL;
+  if (storage_bytes < L.total) return NVFP4KV_ECAPACITY;
+  kvcache *c = new (std::nothrow) kvcache;
+  if (!c) return NVFP4KV_ECAPACITY;
+  c->cfg = *cfg;
+  c->L = L;
+  c->base = static_cast<uint8_t *>(storage);
+  // tensor-scale table and quantizer workspace start zeroed
+  int rc = zero_device_bytes_blocking(c->base + L.table, L.total - L.table);
+  if (rc != NVFP4KV_OK) {
+    delete c;
+    return rc;
+  }
+  *out = c;
+  return NVFP4KV_OK;
+}
+
+int kvcache_destroy(kvcache *c) {
+  delete c;
+  return NVFP4KV_OK;
+}
+
+int kvcache_append(kvcache *c, const uint16_t *k, const uint16_t *v, int32_t n_frames,
+                   void *stream) {
+  if (!c || !k || !v) return NVFP4KV_EINVAL;
+  if (n_frames < 1 || n_frames > kMaxFrames) return NVFP4KV_EINVAL;
+  const kvcache_config &cfg = c->cfg;
+  if (int64_t(n_frames) * cfg.tokens_per_frame > (int64_t(1) << 30)) return NVFP4KV_EINVAL;
+  State s = c->st;   // planned state, committed only if the launch succeeds
+  const int32_t to_sink = n_frames < cfg.sink_frames - s.sink_used
+                              ? n_frames
+                              : cfg.sink_frames - s.sink_used;
+  const int32_t to_win = n_frames - to_sink;
+  if (to_win > cfg.window_frames) return NVFP4KV_ECAPACITY;
+  const int32_t overflow = s.win_count + to_win - cfg.window_frames;
+  if (overflow > 0) evict_oldest(c, s, overflow);
+
+  int32_t sslot = -1;
+  for (int32_t i = 0; i < kScaleSlots; ++i)
+    if (s.scale_ref[i] == 0) {
+      sslot = i;
+      break;
+    }
+  if (sslot < 0) return NVFP4KV_ESTATE;   // unreachable: slots > frames
+
+  const int32_t cid = s.next_chunk;
+  ChunkRec rec;
+  rec.scale_slot = sslot;
+  rec.n_frames = n_frames;
+  rec.resident = n_frames;
+  QuantArgs a;
+  memset(&a, 0, sizeof(a));
+  for (int32_t f = 0; f < n_frames; ++f) {
+    int32_t slot;
+    if (f < to_sink) {
+      slot = s.sink_used++;
+    } else {
+      slot = c->window_slot(s, s.win_count);
+      s.win_count += 1;
+    }
+    s.slot_frame[slot] = FrameRec{cid, f};
+    rec.slot[f] = slot;
+    a.frame_slot[f] = slot;
+  }
+  s.scale_ref[sslot] = n_frames;
+  s.chunks[cid] = rec;
+  s.next_chunk = cid + 1;
+
+  float *tab = c->table();
+  a.t[0] = QuantTensor{k, c->kcodes(), c->kscales(), tab + 2 * sslot, 0, 0};
+  a.t[1] = QuantTensor{v, c->vcodes(), c->vscales(), tab + 2 * sslot + 1, 1, 0};
+  a.n_tensors = 2;
+  a.H = cfg.n_heads;
+  a.T = n_frames * cfg.tokens_per_frame;
+  a.D = cfg.head_dim;
+  a.tokens_per_frame = cfg.tokens_per_frame;
+  a.n_frames = n_frames;
+  a.rows = c->L.rows;
+  a.ws = c->ws();
+  const int rc = launch_quantize(a, stream);
+  if (rc != NVFP4KV_OK) return rc;
+  c->st = s;
+  return NVFP4KV_OK;
+}
+
+int kvcache_evict(kvcache *c, int32_t n_frames) {
+  if (!c || n_frames < 0) return NVFP4KV_EINVAL;
+  if (n_frames > c->st.win_count) return NVFP4KV_ESTATE;
+  evict_oldest(c, c->st, n_frames);
+  return NVFP4KV_OK;
+}
+
+int kvcache_tokens(const kvcache *c, int64_t *sink_tokens, int64_t *window_tokens) {
+  if (!c || !sink_tokens || !window_tokens) return NVFP4KV_EINVAL;
+  *sink_tokens = int64_t(c->st.sink_used) * c->cfg.tokens_per_frame;
+  *window_tokens = int64_t(c->st.win_count) * c->cfg.tokens_per_frame;
+  return NVFP4KV_OK;
+}
+
+int kvcache_chunk_count(const kvcache *c, int32_t *n_chunks) {
+  if (!c || !n_chunks) return NVFP4KV_EINVAL;
+  *n_chunks = c->st.next_chunk;
+  return NVFP4KV_OK;
+}
+
+int kvcache_chunk_frames(const kvcache *c, int32_t chunk_index, int32_t *n_frames) {
+  if (!c || !n_frames) return NVFP4KV_EINVAL;
+  auto it = c->st.chunks.find(chunk_index);
+  if (it == c->st.chunks.end()) return NVFP4KV_ESTATE;
+  *n_frames = it->second.n_frames;
+  return NVFP4KV_OK;
+}
+
+int chunk_attention(const kvcache *c, const uint16_t *q, const uint16_t *k_own,
+                    const uint16_t *v_own, int64_t n_q, float softmax_scale, float *out,
+                    void *stream) {
+  if (!c || !q || !k_own || !v_own || !out) return NVFP4KV_EINVAL;
+  if (n_q < 1 || n_q > (int64_t(1) << 24)) return NVFP4KV_EINVAL;
+  if (!(softmax_scale > 0.0f) || softmax_scale > 3.0e38f) return NVFP4KV_EINVAL;
+  AttnArgs a;
+  memset(&a, 0, sizeof(a));
+  a.q = q;
+  a.k_own = k_own;
+  a.v_own = v_own;
+  a.out = out;
+  a.kcodes = c->kcodes();
+  a.kscales = c->kscales();
+  a.vcodes = c->vcodes();
+  a.vscales = c->vscales();
+  a.scale_table = c->table();
+  a.rows = c->L.rows;
+  a.H = c->cfg.n_heads;
+  a.D = c->cfg.head_dim;
+  a.n_q = int32_t(n_q);
+  a.sm_scale_log2 = softmax_scale * 1.4426950408889634f;
+  int32_t slots[kMaxFrames];
+  const int nf = collect_frames(c, slots);
+  const int32_t T_f = c->cfg.tokens_per_frame;
+  int ns = 0;
+  for (int i = 0; i < nf; ++i) {
+    const FrameRec fr = c->st.slot_frame[slots[i]];
+    const int32_t ss = c->st.chunks.at(fr.chunk).scale_slot;
+    const int32_t tok0 = slots[i] * T_f;
+    if (ns > 0 && a.seg[ns - 1].scale_slot == ss &&
+        a.seg[ns - 1].tok0 + a.seg[ns - 1].ntok == tok0) {
+      a.seg[ns - 1].ntok += T_f;
+    } else {
+      a.seg[ns] = Segment{tok0, T_f, ss, 0};
+      ++ns;
+    }
+  }
+  a.n_seg = ns;
+  return launch_attention(a, stream);
+}
+
+int kvcache_export_chunk(const kvcache *c, int32_t chunk_index, uint8_t *k_codes,
+                         uint8_t *k_scales, uint8_t *v_codes, uint8_t *v_scales,
+                         float *k_scale, float *v_scale, void *stream) {
+  if (!c || !k_codes || !k_scales || !v_codes || !v_scales || !k_scale || !v_scale)
+    return NVFP4KV_EINVAL;
+  auto it = c->st.chunks.find(chunk_index);
+  if (it == c->st.chunks.end()) return NVFP4KV_ESTATE;
+  const ChunkRec &rec = it->second;
+  if (rec.resident != rec.n_frames) return NVFP4KV_ESTATE;
+  ExportArgs a;
+  memset(&a, 0, sizeof(a));
+  a.kcodes = c->kcodes();
+  a.kscales = c->kscales();
+  a.vcodes = c->vcodes();
+  a.vscales = c->vscales();
+  a.scale_table = c->table();
+  a.scale_slot = rec.scale_slot;
+  a.H = c->cfg.n_heads;
+  a.D = c->cfg.head_dim;
+  a.T_f = c->cfg.tokens_per_frame;
+  a.n_frames = rec.n_frames;
+  a.rows = c->L.rows;
+  a.k_codes_out = k_codes;
+  a.k_scales_out = k_scales;
+  a.v_codes_out = v_codes;
+  a.v_scales_out = v_scales;
+  a.k_scale_out = k_scale;
+  a.v_scale_out = v_scale;
+  for (int32_t f = 0; f < rec.n_frames; ++f) a.frame_slot[f] = rec.slot[f];
+  return launch_export(a, stream);
+}
+
+}  // extern "C"

@@ -1,0 +1,96 @@
+// Internal interface between the host library (cache manager, argument checks)
+// and the gfx950 kernels.  Plain C++ types only: the host side also builds with g++
+// (for CPU tests of the cache metadata) against a recording stand-in of these
+// launch functions.
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+
+namespace nvfp4kv {
+
+constexpr int kMaxFrames = 64;            // sink + window frame slots
+constexpr int kScaleSlots = kMaxFrames + 1;
+constexpr int kMaxSegments = kMaxFrames;  // one per resident frame at worst
+constexpr int kMaxQuantGrid = 2048;       // workgroups of one quantize launch
+constexpr int kQuantThreads = 256;
+
+// Grid-barrier state and per-workgroup partial maxima of the single-pass quantizer.
+// `count` returns to 0 at the end of every launch and `gen` only grows, so the
+// block stays valid across calls once it has been zero-filled.
+struct QuantWorkspace {
+  uint32_t count;
+  uint32_t gen;
+  uint32_t timeout;   // set if a barrier wait ever gave up (never expected)
+  uint32_t pad;
+  uint32_t partial[2][kMaxQuantGrid];   // |x| maxima as fp32 bit patterns
+};
+
+// One tensor of a quantize launch.  Source: bf16 [H][T][D].  Destination, canonical
+// layout: codes [H][rows][D/2], scales [H][rows][D/16]; transposed layout (V in the
+// cache): codes [H][D][rows/2] (token 2i in the low nibble), scales [H][D/16][rows].
+struct QuantTensor {
+  const uint16_t *src;
+  uint8_t *codes;
+  uint8_t *scales;
+  float *tensor_scale;   // receives s_t
+  int32_t transposed;
+  int32_t pad;
+};
+
+struct QuantArgs {
+  QuantTensor t[2];
+  int32_t n_tensors;
+  int32_t H, T, D;
+  int32_t tokens_per_frame;   // T_f; source token t is frame t / T_f
+  int32_t n_frames;
+  int64_t rows;               // destination tokens per head
+  int32_t tile_tokens;        // tokens per workgroup tile
+  int32_t tiles_per_frame;
+  int32_t total_tiles;
+  int32_t items;              // tiles per workgroup (>= ceil(total_tiles / grid))
+  QuantWorkspace *ws;
+  int32_t frame_slot[kMaxFrames];   // destination slot of each source frame
+};
+
+struct Segment {
+  int32_t tok0;        // first token (slot * T_f) in the cache rows
+  int32_t ntok;
+  int32_t scale_slot;  // index into the tensor-scale table
+  int32_t pad;
+};
+
+struct AttnArgs {
+  const uint16_t *q, *k_own, *v_own;
+  float *out;
+  const uint8_t *kcodes, *kscales, *vcodes, *vscales;   // cache planes
+  const float *scale_table;                               // [slot][2] = {s_K, s_V}
+  int64_t rows;                                           // cache tokens per head
+  int32_t H, D, n_q;
+  float sm_scale_log2;                                    // softmax_scale * log2(e)
+  int32_t n_seg;
+  int32_t pad;
+  Segment seg[kMaxSegments];
+};
+
+struct ExportArgs {
+  const uint8_t *kcodes, *kscales, *vcodes, *vscales;
+  const float *scale_table;
+  int32_t scale_slot;
+  int32_t H, D, T_f, n_frames;
+  int64_t rows;
+  uint8_t *k_codes_out, *k_scales_out, *v_codes_out, *v_scales_out;
+  float *k_scale_out, *v_scale_out;
+  int32_t frame_slot[kMaxFrames];
+};
+
+// Launchers: return 0 or a negative nvfp4kv_status (EHIP).  `stream` is hipStream_t.
+int launch_quantize(const QuantArgs &a, void *stream);
+int launch_attention(const AttnArgs &a, void *stream);
+int launch_export(const ExportArgs &a, void *stream);
+int zero_device_bytes_blocking(void *ptr, size_t bytes);
+int zero_device_bytes_async(void *ptr, size_t bytes, void *stream);
+// Largest co-resident grid of the quantize kernel for `items` tiles per workgroup.
+int quantize_max_grid(int items, int *grid);
+
+}  // namespace nvfp4kv

@@ -1,0 +1,141 @@
+"""GPU parity of chunk attention over the NVFP4 cache: the oracle builds its own
+cache from the same seeded chunks (its own quantizer) and computes float64
+softmax attention; the GPU's fp32 output must agree within max-abs 1e-2 and
+relative-L2 5e-3.  Small cases compare every output; the full-size Wan-shaped
+workloads compare sampled query rows of every head (the GPU computes all)."""
+
+import numpy as np
+import pytest
+
+from oracle import CacheModel, chunk_attention_ref
+from nvfp4_kv_cache_amd import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def ops(gpu):
+    from nvfp4_kv_cache_amd import ops as _ops
+    return _ops
+
+
+def build_both(ops, H, D, T_f, sink, window, chunks):
+    """GPU cache and oracle cache fed with the same list of (k_bits, v_bits)."""
+    from gpu_util import dev
+    cache = ops.KVCache(H, D, T_f, sink, window)
+    model = CacheModel(H, D, T_f, sink, window)
+    for k, v in chunks:
+        nf = k.shape[1] // T_f
+        cache.append(dev(k), dev(v), nf)
+        model.append(k, v)
+    return cache, model
+
+
+def run_case(ops, cache, model, q, ko, vo, scale, rows=None, what=""):
+    from gpu_util import dev, host, check_attention
+    print(f"[{what}] n_q={q.shape[1]} cache_tokens={model.n_tokens()}", flush=True)
+    out = host(cache.attention(dev(q), dev(ko), dev(vo), scale))
+    ck, cv = model.dequantized_kv()
+    want = chunk_attention_ref(q, ko, vo, ck, cv, scale, rows=rows)
+    got = out if rows is None else out[:, rows]
+    return check_attention(got, want, what)
+
+
+def test_tiny_workload(ops):
+    wl = W.WORKLOADS["tiny"]
+    cache, model = build_both(ops, wl.n_heads, wl.head_dim, wl.tokens_per_frame, wl.sink_frames,
+                              wl.window_frames, [W.clean_chunk(wl, 0)])
+    assert model.n_tokens() == 256
+    q, ko, vo = W.noisy_chunk(wl, 1)
+    run_case(ops, cache, model, q, ko, vo, wl.softmax_scale, what="tiny")
+
+
+def rand_bits(rng, shape, outliers=True):
+    x = rng.standard_normal(shape).astype(np.float32)
+    if outliers:
+        m = rng.random(shape) < 0.02
+        x[m] = rng.standard_t(4, size=int(m.sum())).astype(np.float32)
+    return W.f32_to_bf16_bits(x)
+
+
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("n_q", [1, 100, 257])
+def test_ragged_multi_segment(ops, D, n_q):
+    """Several chunks with their own scales, a window that wraps (so segments are
+    split and reordered), 40-token frames (ragged 64-key tiles) and ragged query
+    counts."""
+    rng = np.random.default_rng(D + n_q)
+    H, T_f, sink, window = 3, 40, 2, 5
+    chunks = []
+    for nf in (3, 2, 1, 3, 2):
+        chunks.append((rand_bits(rng, (H, nf * T_f, D)) , rand_bits(rng, (H, nf * T_f, D))))
+    cache, model = build_both(ops, H, D, T_f, sink, window, chunks)
+    q, ko, vo = (rand_bits(rng, (H, n_q, D)) for _ in range(3))
+    run_case(ops, cache, model, q, ko, vo, 1.0 / np.sqrt(D), what=f"ragged D{D} nq{n_q}")
+
+
+def test_empty_cache_is_plain_self_attention(ops):
+    rng = np.random.default_rng(3)
+    H, D = 2, 128
+    cache = ops.KVCache(H, D, 64, 1, 3)
+    model = CacheModel(H, D, 64, 1, 3)
+    q, ko, vo = (rand_bits(rng, (H, 77, D)) for _ in range(3))
+    run_case(ops, cache, model, q, ko, vo, 0.0884, what="empty cache")
+
+
+def test_evicted_frames_are_not_attended(ops):
+    rng = np.random.default_rng(4)
+    H, D, T_f = 2, 128, 32
+    chunks = [(rand_bits(rng, (H, 2 * T_f, D)), rand_bits(rng, (H, 2 * T_f, D))) for _ in range(3)]
+    cache, model = build_both(ops, H, D, T_f, 1, 4, chunks)
+    cache.evict(2)
+    model.evict(2)
+    q, ko, vo = (rand_bits(rng, (H, 50, D)) for _ in range(3))
+    run_case(ops, cache, model, q, ko, vo, 0.1, what="after evict")
+
+
+def test_large_logits_and_zero_chunk(ops):
+    """A chunk of all-zero K/V (s_t = 0) and queries aligned with one key so that
+    a single key dominates its rows."""
+    rng = np.random.default_rng(5)
+    H, D, T_f = 1, 128, 64
+    k0 = np.zeros((H, T_f, D), dtype=np.uint16)
+    k1 = rand_bits(rng, (H, 2 * T_f, D))
+    v1 = rand_bits(rng, (H, 2 * T_f, D))
+    cache, model = build_both(ops, H, D, T_f, 1, 3, [(k0, k0), (k1, v1)])
+    q = rand_bits(rng, (H, 64, D), outliers=False)
+    kf = W.f32_to_bf16_bits(np.zeros((H, 64, D), dtype=np.float32))
+    x = np.zeros((H, 64, D), dtype=np.float32)
+    x[0, :, :] = 0.0
+    qf = (q.astype(np.uint32) << 16).view(np.float32)
+    x[0, 10] = qf[0, 3] * 4.0                        # own key 10 dominates query 3's row
+    ko = W.f32_to_bf16_bits(x)
+    vo = rand_bits(rng, (H, 64, D))
+    run_case(ops, cache, model, q, ko, vo, 1.0, what="dominant key")
+
+
+@pytest.mark.parametrize("name", ["wan13b", "wan5b"])
+def test_wan_shaped_workloads_sampled_rows(ops, name):
+    wl = W.WORKLOADS[name]
+    chunks = [W.clean_chunk(wl, c) for c in range(wl.n_cache_chunks)]
+    cache, model = build_both(ops, wl.n_heads, wl.head_dim, wl.tokens_per_frame, wl.sink_frames,
+                              wl.window_frames, chunks)
+    assert model.n_tokens() == (wl.sink_frames + wl.window_frames) * wl.tokens_per_frame
+    q, ko, vo = W.noisy_chunk(wl, wl.n_cache_chunks)
+    rng = np.random.default_rng(0)
+    n_q = wl.n_q
+    rows = np.unique(np.concatenate([rng.choice(n_q, 48, replace=False),
+                                     [0, 1, 127, 128, n_q - 1]]))
+    run_case(ops, cache, model, q, ko, vo, wl.softmax_scale, rows=rows, what=name)
+
+
+def test_attention_deterministic(ops):
+    from gpu_util import dev, host
+    rng = np.random.default_rng(6)
+    H, D, T_f = 2, 128, 48
+    chunks = [(rand_bits(rng, (H, 3 * T_f, D)), rand_bits(rng, (H, 3 * T_f, D)))]
+    cache, _ = build_both(ops, H, D, T_f, 1, 2, chunks)
+    q, ko, vo = (dev(rand_bits(rng, (H, 200, D))) for _ in range(3))
+    a = host(cache.attention(q, ko, vo, 0.1))
+    b = host(cache.attention(q, ko, vo, 0.1))
+    assert np.array_equal(a, b)

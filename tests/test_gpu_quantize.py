@@ -1,0 +1,120 @@
+"""GPU parity of the NVFP4 codec and of the cache append path: codes, scale bytes
+and fp32 tensor scales must equal the oracle's bit for bit."""
+
+import json
+import os
+
+import numpy as np
+import pytest
+
+from oracle import quantize_ref
+from nvfp4_kv_cache_amd import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "nvfp4_hand_example.json")
+
+
+@pytest.fixture(scope="module")
+def ops(gpu):
+    from nvfp4_kv_cache_amd import ops as _ops
+    return _ops
+
+
+@pytest.fixture(scope="module")
+def ws(ops):
+    return ops.quantize_workspace()
+
+
+def codec_gpu(ops, ws, bits):
+    from gpu_util import dev, host
+    c, s, t = ops.quantize_kv(dev(bits), ws)
+    return host(c), host(s), host(t)[0]
+
+
+def assert_codec_equal(got, want, what):
+    from gpu_util import f32_bits
+    gc, gs, gt = got
+    wc, ws_, wt = want
+    print(f"[{what}] s_t gpu={gt!r} oracle={wt!r}", flush=True)
+    assert f32_bits(gt) == f32_bits(wt), what
+    assert np.array_equal(gs, ws_), f"{what}: {np.count_nonzero(gs != ws_)} scale bytes differ"
+    assert np.array_equal(gc, wc), f"{what}: {np.count_nonzero(gc != wc)} code bytes differ"
+
+
+def t4_bits(rng, shape, scale=1.0):
+    return W.f32_to_bf16_bits((rng.standard_t(4, size=shape) * scale).astype(np.float32))
+
+
+def test_codec_golden(ops, ws):
+    for case in json.load(open(GOLDEN))["cases"]:
+        vals = [[-0.0 if v == "-0" else float(v) for v in row] for row in case["x"]]
+        bits = W.f32_to_bf16_bits(np.array(vals, dtype=np.float32)).reshape(case["shape"])
+        got = codec_gpu(ops, ws, bits)
+        assert_codec_equal(got, quantize_ref(bits), case["name"])
+
+
+@pytest.mark.parametrize("shape,scale", [((3, 50, 64), 1.0), ((2, 37, 128), 3.0), ((1, 1, 32), 1.0),
+                                         ((5, 129, 96), 1e-3), ((2, 300, 256), 1e4)])
+def test_codec_random(ops, ws, shape, scale):
+    rng = np.random.default_rng(hash(shape) % 1000)
+    bits = t4_bits(rng, shape, scale)
+    assert_codec_equal(codec_gpu(ops, ws, bits), quantize_ref(bits), f"t4 {shape} x{scale}")
+
+
+def test_codec_special_values(ops, ws):
+    """Zeros of both signs, bf16 subnormals, values on E2M1 thresholds after
+    scaling, and a block far below the tensor amax (subnormal E4M3 scales)."""
+    rng = np.random.default_rng(1)
+    x = rng.standard_normal((2, 64, 64)).astype(np.float32)
+    x[0, 0, :16] = 0.0
+    x[0, 1, :16] = -0.0
+    x[0, 2, :] *= 1e-6
+    x[0, 3, :] = np.float32(2.0 ** -130) * rng.integers(-50, 50, 64)   # bf16 subnormals
+    x[1, 5, 0] = 4096.0                                                  # tensor amax
+    x[1, 6, :16] = np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5, 6] * 2) * 1.5
+    bits = W.f32_to_bf16_bits(x)
+    assert_codec_equal(codec_gpu(ops, ws, bits), quantize_ref(bits), "special")
+    zero = np.zeros((1, 8, 32), dtype=np.uint16)
+    zero[0, ::2] = 0x8000
+    assert_codec_equal(codec_gpu(ops, ws, zero), quantize_ref(zero), "all zero")
+    tiny = np.full((1, 16, 32), 0x0001, dtype=np.uint16)                 # smallest subnormal
+    assert_codec_equal(codec_gpu(ops, ws, tiny), quantize_ref(tiny), "min subnormal")
+
+
+def test_codec_workspace_reuse_is_deterministic(ops, ws):
+    rng = np.random.default_rng(2)
+    bits = t4_bits(rng, (4, 500, 128))
+    first = codec_gpu(ops, ws, bits)
+    for _ in range(3):
+        again = codec_gpu(ops, ws, bits)
+        assert_codec_equal(again, first, "repeat")
+
+
+@pytest.mark.parametrize("name", ["tiny", "quantize"])
+def test_codec_workload_tensors(ops, ws, name):
+    wl = W.WORKLOADS[name]
+    k, v = W.clean_chunk(wl, 0)
+    for bits, what in ((k, "K"), (v, "V")):
+        assert_codec_equal(codec_gpu(ops, ws, bits), quantize_ref(bits), f"{name} {what}")
+
+
+def test_append_quantize_workload_steady_state(ops):
+    """Quantize-only workload: K, V [12, 4680, 128] appended as one 3-frame chunk
+    into a full 3 sink + 9 window cache; exported codes must equal the oracle's
+    codec of the same tensors, and the sink chunk must be untouched."""
+    from gpu_util import dev, host
+    wl = W.WORKLOADS["quantize"]
+    cache = ops.KVCache(wl.n_heads, wl.head_dim, wl.tokens_per_frame, wl.sink_frames,
+                        wl.window_frames)
+    chunks = [W.clean_chunk(wl, c) for c in range(5)]
+    for c, (k, v) in enumerate(chunks):
+        cache.append(dev(k), dev(v), wl.chunk_frames)
+    assert cache.tokens() == (3 * 1560, 9 * 1560)
+    for c in (0, 4):
+        kc, ks, vc, vs, sk, sv = cache.export_chunk(c)
+        k, v = chunks[c]
+        assert_codec_equal((host(kc), host(ks), host(sk)[0]), quantize_ref(k), f"chunk {c} K")
+        assert_codec_equal((host(vc), host(vs), host(sv)[0]), quantize_ref(v), f"chunk {c} V")
+    with pytest.raises(ops.NVFP4KVError):
+        cache.export_chunk(1)          # evicted by chunk 4

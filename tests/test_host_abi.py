@@ -1,0 +1,238 @@
+"""CPU tests of the C ABI: every declared symbol is exported by the built
+library; argument errors return status codes before any device work; and the
+cache metadata (slot assignment, FIFO eviction, sink retention, segment lists)
+matches the oracle's frame-list model, using a build of the host code whose
+kernel launchers only record their arguments (tests/host_stub)."""
+
+import ctypes
+import os
+import re
+import subprocess
+
+import numpy as np
+import pytest
+
+from oracle import CacheModel
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "nvfp4kv.h")
+LIB = os.path.join(ROOT, "nvfp4_kv_cache_amd", "libnvfp4kv.so")
+STUB = os.path.join(ROOT, "nvfp4_kv_cache_amd", "libnvfp4kv_hoststub.so")
+
+OK, EINVAL, ESHAPE, ECAPACITY, ESTATE, EHIP = 0, -1, -2, -3, -4, -5
+
+
+class Cfg(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in
+                ("n_heads", "head_dim", "tokens_per_frame", "sink_frames", "window_frames")]
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"\b([a-z_][a-z0-9_]*)\s*\(", text)
+    skip = {"if", "defined", "sizeof"}
+    return sorted({n for n in names if n not in skip and not n.startswith("_")})
+
+
+def test_header_declares_the_boundary():
+    fns = declared_functions()
+    for need in ["nvfp4_quantize_kv", "nvfp4_quantize_workspace_bytes", "kvcache_storage_bytes",
+                 "kvcache_create", "kvcache_destroy", "kvcache_append", "kvcache_evict",
+                 "kvcache_tokens", "chunk_attention", "kvcache_export_chunk", "nvfp4kv_strerror"]:
+        assert need in fns
+
+
+@pytest.fixture(scope="module")
+def real():
+    if not os.path.exists(LIB):
+        pytest.fail("libnvfp4kv.so is not built (run __graft_entry__.build())")
+    return ctypes.CDLL(LIB)
+
+
+def test_library_exports_every_declared_symbol(real):
+    out = subprocess.run(["nm", "-D", "--defined-only", LIB], capture_output=True, text=True).stdout
+    exported = set(re.findall(r"\s[TW]\s(\S+)$", out, flags=re.M))
+    missing = [f for f in declared_functions() if f not in exported]
+    assert not missing, missing
+
+
+def test_error_paths_before_device_work(real):
+    P = ctypes.c_void_p
+    real.nvfp4_quantize_kv.argtypes = [P, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, P, P, P, P,
+                                       ctypes.c_size_t, P]
+    dummy = P(0x10000)
+    ws = real.nvfp4_quantize_workspace_bytes()
+    assert real.nvfp4_quantize_kv(None, 1, 1, 64, dummy, dummy, dummy, dummy, ws, None) == EINVAL
+    assert real.nvfp4_quantize_kv(dummy, 1, 1, 48, dummy, dummy, dummy, dummy, ws, None) == EINVAL
+    assert real.nvfp4_quantize_kv(dummy, 0, 1, 64, dummy, dummy, dummy, dummy, ws, None) == EINVAL
+    assert real.nvfp4_quantize_kv(dummy, 1, 1, 64, dummy, dummy, dummy, dummy, ws - 1, None) == ECAPACITY
+    real.kvcache_storage_bytes.restype = ctypes.c_size_t
+    real.kvcache_storage_bytes.argtypes = [ctypes.POINTER(Cfg)]
+    for bad in [Cfg(1, 96, 64, 1, 3), Cfg(1, 128, 60, 1, 3), Cfg(0, 128, 64, 1, 3),
+                Cfg(1, 128, 64, -1, 3), Cfg(1, 128, 64, 1, 0), Cfg(1, 128, 64, 40, 30)]:
+        assert real.kvcache_storage_bytes(ctypes.byref(bad)) == 0
+    h = P()
+    real.kvcache_create.argtypes = [ctypes.POINTER(Cfg), P, ctypes.c_size_t, ctypes.POINTER(P)]
+    good = Cfg(2, 128, 64, 1, 3)
+    n = real.kvcache_storage_bytes(ctypes.byref(good))
+    assert real.kvcache_create(ctypes.byref(good), None, n, ctypes.byref(h)) == EINVAL
+    assert real.kvcache_create(ctypes.byref(good), P(0x10001), n, ctypes.byref(h)) == EINVAL
+    assert real.kvcache_create(ctypes.byref(good), P(0x10000), n - 1, ctypes.byref(h)) == ECAPACITY
+    real.chunk_attention.argtypes = [P, P, P, P, ctypes.c_int64, ctypes.c_float, P, P]
+    assert real.chunk_attention(None, dummy, dummy, dummy, 4, 0.1, dummy, None) == EINVAL
+    real.kvcache_append.argtypes = [P, P, P, ctypes.c_int32, P]
+    assert real.kvcache_append(None, dummy, dummy, 1, None) == EINVAL
+    real.nvfp4kv_strerror.restype = ctypes.c_char_p
+    assert b"invalid" in real.nvfp4kv_strerror(EINVAL)
+
+
+def test_storage_bytes_budget(real):
+    """9/16 byte per cached element for each of K and V (reading note: 9/8 T_c H d
+    bytes for K and V), plus a small fixed table and workspace."""
+    real.kvcache_storage_bytes.restype = ctypes.c_size_t
+    real.kvcache_storage_bytes.argtypes = [ctypes.POINTER(Cfg)]
+    cfg = Cfg(12, 128, 1560, 3, 9)
+    n = real.kvcache_storage_bytes(ctypes.byref(cfg))
+    elems = 12 * 128 * 1560 * 12
+    assert 2 * elems * 9 // 16 <= n <= 2 * elems * 9 // 16 + 64 * 1024
+
+
+# ------------------------------------------------------------ host stub
+
+
+@pytest.fixture(scope="module")
+def stub():
+    src = [os.path.join(ROOT, "nvfp4_kv_cache_amd", "csrc", "api.cpp"),
+           os.path.join(ROOT, "tests", "host_stub", "stub_launch.cpp")]
+    subprocess.run(["g++", "-O1", "-std=c++17", "-fPIC", "-shared", "-o", STUB] + src, check=True)
+    L = ctypes.CDLL(STUB)
+    P = ctypes.c_void_p
+    L.kvcache_storage_bytes.restype = ctypes.c_size_t
+    L.kvcache_storage_bytes.argtypes = [ctypes.POINTER(Cfg)]
+    L.kvcache_create.argtypes = [ctypes.POINTER(Cfg), P, ctypes.c_size_t, ctypes.POINTER(P)]
+    L.kvcache_append.argtypes = [P, P, P, ctypes.c_int32, P]
+    L.kvcache_evict.argtypes = [P, ctypes.c_int32]
+    L.kvcache_destroy.argtypes = [P]
+    L.chunk_attention.argtypes = [P, P, P, P, ctypes.c_int64, ctypes.c_float, P, P]
+    L.kvcache_tokens.argtypes = [P, ctypes.POINTER(ctypes.c_int64), ctypes.POINTER(ctypes.c_int64)]
+    L.kvcache_export_chunk.argtypes = [P, ctypes.c_int32] + [P] * 7
+    L.stub_last_segments.argtypes = [ctypes.POINTER(ctypes.c_int32), ctypes.c_int]
+    L.stub_last_quant_slots.argtypes = [ctypes.POINTER(ctypes.c_int32), ctypes.c_int,
+                                        ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_int64)]
+    L.stub_last_scale_ptr.restype = ctypes.c_int64
+    L.stub_last_export_slot.argtypes = [ctypes.POINTER(ctypes.c_int32), ctypes.c_int]
+    return L
+
+
+class StubCache:
+    BASE = 1 << 32
+
+    def __init__(self, L, cfg):
+        self.L, self.cfg = L, cfg
+        n = L.kvcache_storage_bytes(ctypes.byref(cfg))
+        assert n > 0
+        self.h = ctypes.c_void_p()
+        assert L.kvcache_create(ctypes.byref(cfg), ctypes.c_void_p(self.BASE), n, ctypes.byref(self.h)) == OK
+
+    def append(self, n_frames):
+        d = ctypes.c_void_p(0x1000)
+        return self.L.kvcache_append(self.h, d, d, n_frames, None)
+
+    def segments(self):
+        d = ctypes.c_void_p(0x1000)
+        assert self.L.chunk_attention(self.h, d, d, d, 8, 0.125, d, None) == OK
+        buf = (ctypes.c_int32 * 192)()
+        n = self.L.stub_last_segments(buf, 64)
+        return [tuple(buf[3 * i:3 * i + 3]) for i in range(n)]
+
+    def quant_slots(self):
+        buf = (ctypes.c_int32 * 64)()
+        nt, rows = ctypes.c_int32(), ctypes.c_int64()
+        n = self.L.stub_last_quant_slots(buf, 64, ctypes.byref(nt), ctypes.byref(rows))
+        return list(buf[:n]), nt.value, rows.value
+
+
+@pytest.mark.parametrize("seed", range(10))
+def test_cache_metadata_matches_frame_list_model(stub, seed):
+    """Random append/evict sequences: the tokens the attention kernel would read
+    (segment list, in order) are exactly the frames of the oracle's cache model,
+    each frame's slot being where its chunk's quantize launch wrote it, and each
+    segment carrying its chunk's tensor-scale slot."""
+    rng = np.random.default_rng(seed)
+    sink, window = int(rng.integers(0, 4)), int(rng.integers(1, 8))
+    T_f = 8 * int(rng.integers(1, 5))
+    c = StubCache(stub, Cfg(1, 64, T_f, sink, window))
+    model = CacheModel(1, 64, T_f, sink, window)
+    where = {}          # (chunk, frame) -> slot
+    scale_of = {}       # chunk -> table offset of its K scale
+    chunk = 0
+    for step in range(40):
+        if rng.random() < 0.2 and len(model.window) > 0:
+            e = int(rng.integers(1, len(model.window) + 1))
+            assert stub.kvcache_evict(c.h, e) == OK
+            model.evict(e)
+        nf = int(rng.integers(1, window + 1))
+        assert c.append(nf) == OK
+        slots, nt, rows = c.quant_slots()
+        assert nt == 2 and rows == (sink + window) * T_f and len(slots) == nf
+        for f, s in enumerate(slots):
+            where[(chunk, f)] = s
+        scale_of[chunk] = stub.stub_last_scale_ptr(0) - StubCache.BASE
+        assert stub.stub_last_scale_ptr(1) - stub.stub_last_scale_ptr(0) == 4
+        zeros = np.zeros((1, nf * T_f, 64), dtype=np.uint16)
+        model.append(zeros, zeros)
+        chunk += 1
+        # expected token runs from the model, in key order
+        want_tokens = []
+        for fr in model.frames():
+            s = where[(fr.chunk_id, fr.frame_in_chunk)]
+            want_tokens += [(t, fr.chunk_id) for t in range(s * T_f, (s + 1) * T_f)]
+        got_tokens = []
+        seg_scale = {}
+        for tok0, ntok, sslot in c.segments():
+            for t in range(tok0, tok0 + ntok):
+                got_tokens.append(t)
+            seg_scale.setdefault(sslot, set()).update(range(tok0, tok0 + ntok))
+        assert got_tokens == [t for t, _ in want_tokens]
+        # all tokens of a segment belong to chunks sharing that scale slot
+        tok_chunk = dict(want_tokens)
+        for sslot, toks in seg_scale.items():
+            chunks = {tok_chunk[t] for t in toks}
+            assert len(chunks) == 1
+        # slots in use are distinct
+        occupied = [where[(fr.chunk_id, fr.frame_in_chunk)] for fr in model.frames()]
+        assert len(set(occupied)) == len(occupied)
+        # sink frames sit in slots [0, sink)
+        for i, fr in enumerate(model.sinks):
+            assert where[(fr.chunk_id, fr.frame_in_chunk)] == i
+        s_tok, w_tok = ctypes.c_int64(), ctypes.c_int64()
+        stub.kvcache_tokens(c.h, ctypes.byref(s_tok), ctypes.byref(w_tok))
+        assert s_tok.value == len(model.sinks) * T_f and w_tok.value == len(model.window) * T_f
+    stub.kvcache_destroy(c.h)
+
+
+def test_cache_errors_and_rollback(stub):
+    c = StubCache(stub, Cfg(2, 128, 16, 1, 3))
+    assert c.append(5) == ECAPACITY          # 4 frames would enter a 3-frame window
+    assert c.append(0) == EINVAL
+    assert stub.kvcache_evict(c.h, 1) == ESTATE
+    assert c.append(4) == OK                 # 1 sink + 3 window
+    stub.stub_fail_next(EHIP)
+    assert c.append(2) == EHIP               # a failed launch leaves the state unchanged
+    assert c.segments() == [(0, 64, 0)]
+    assert stub.kvcache_evict(c.h, 4) == ESTATE
+    assert stub.kvcache_evict(c.h, 2) == OK
+    assert c.segments() == [(0, 16, 0), (48, 16, 0)]
+    d = ctypes.c_void_p(0x1000)
+    # chunk 0 lost two frames: not fully resident, cannot be exported
+    assert stub.kvcache_export_chunk(c.h, 0, d, d, d, d, d, d, None) == ESTATE
+    assert stub.kvcache_export_chunk(c.h, 7, d, d, d, d, d, d, None) == ESTATE
+    assert c.append(2) == OK
+    segs = c.segments()
+    assert segs[0] == (0, 16, 0) and segs[1] == (48, 16, 0) and segs[2][1] == 32
+    assert segs[2][2] != 0
+    buf = (ctypes.c_int32 * 64)()
+    assert stub.kvcache_export_chunk(c.h, 1, d, d, d, d, d, d, None) == OK
+    assert stub.stub_last_export_slot(buf, 64) == segs[2][2]
+    stub.kvcache_destroy(c.h)
