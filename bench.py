@@ -1,0 +1,293 @@
+#!/usr/bin/env python3
+"""Benchmark of the NVFP4 KV-cache chunk-attention hot path on one MI355X.
+
+One step = one chunk of the streaming rollout (12 heads, head_dim 128, 1560
+tokens per latent frame, 3-frame chunks, cache of 3 sink + 9 window frames):
+four chunk-attention calls of the noisy chunk over the NVFP4 cache plus its
+own bf16 K/V (4 denoising steps), then quantize + append of the clean chunk.
+`--warmup W` chunks run first (W >= 4 fills the cache, so every timed step
+sees the steady-state 18720 cache tokens); `--steps K` chunks are timed.
+Inputs are resident on the device before timing starts.
+
+Prints progress on stderr and ONE JSON line on stdout:
+  value          chunk-attention TFLOP/s over the timed rollout steps (the time
+                 includes the appends);  latent_frames_per_s alongside
+  roofline       the attention kernel alone: FLOPs per launch / mean launch time
+                 (HIP events on the launch stream) vs the 2516.6 TFLOP/s bf16
+                 dense MFMA peak
+  quantize       the append (quantize + pack) kernel on the quantize-only
+                 workload, cache-cold inputs: algorithmic GB/s vs 8 TB/s HBM
+  configs        the other workloads (tiny, 1.3B-shaped, 5B-shaped)
+  cpu_baseline   the CPU oracle on a bounded sample of the same attention
+"""
+
+import argparse
+import json
+import os
+import platform
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+MFMA_BF16_PEAK_TFLOPS = 2516.6     # MI355X dense bf16 (fp16 is the same)
+HBM_PEAK_GBPS = 8000.0             # MI355X HBM3E
+METRIC = "NVFP4-KV chunk attention TFLOP/s + latent frames/s; KV-quantize GB/s"
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=36)
+    p.add_argument("--warmup", type=int, default=4)
+    p.add_argument("--reps", type=int, default=30, help="launches per kernel microbenchmark")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-rows", type=int, default=768, help="query rows per head in the CPU sample")
+    p.add_argument("--skip-configs", action="store_true", help="rollout + roofline legs only")
+    return p.parse_args()
+
+
+def timed(fn, reps, torch):
+    """Mean ms per call of fn() over `reps` back-to-back calls, HIP events on
+    the current stream."""
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    fn()
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(reps):
+        fn()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / reps
+
+
+def dev_bits(torch, bits, device):
+    import numpy as np
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(device)
+
+
+def rollout(args, torch, ops, W, device):
+    wl = W.WORKLOADS["rollout"]
+    n_chunks = args.warmup + args.steps
+    S = wl.steps_per_chunk
+    log(f"rollout: drawing {n_chunks} chunks x ({S} noisy steps + clean append) on device")
+    inputs = []
+    for c in range(n_chunks):
+        noisy = [tuple(W.draw_device_normal(wl, c, s, t, device) for t in (W.Q_ID, W.K_ID, W.V_ID))
+                 for s in range(S)]
+        clean = tuple(W.draw_device_normal(wl, c, W.APPEND_STEP, t, device) for t in (W.K_ID, W.V_ID))
+        inputs.append((noisy, clean))
+    cache = ops.KVCache(wl.n_heads, wl.head_dim, wl.tokens_per_frame, wl.sink_frames,
+                        wl.window_frames, device=device)
+    out = torch.empty((wl.n_heads, wl.n_q, wl.head_dim), dtype=torch.float32, device=device)
+    scale = wl.softmax_scale
+
+    def step(c):
+        noisy, (kc, vc) = inputs[c]
+        for q, k, v in noisy:
+            cache.attention(q, k, v, scale, out=out)
+        cache.append(kc, vc, wl.chunk_frames)
+
+    for c in range(args.warmup):
+        step(c)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record()
+    for c in range(args.warmup, n_chunks):
+        step(c)
+    e1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = e0.elapsed_time(e1)
+    n_k = wl.cache_frames_for_chunk(args.warmup) * wl.tokens_per_frame + wl.n_q
+    steady = wl.cache_frames_for_chunk(args.warmup) == wl.sink_frames + wl.window_frames
+    flops_step = S * W.attention_flops(wl.n_heads, wl.n_q, n_k, wl.head_dim)
+    res = {
+        "ms_per_step": ms / args.steps,
+        "wall_ms_per_step": 1e3 * wall / args.steps,
+        "tflops": flops_step * args.steps / (ms * 1e-3) / 1e12,
+        "frames_per_s": wl.chunk_frames * args.steps / (ms * 1e-3),
+        "cache_tokens": n_k - wl.n_q,
+        "steady_state": steady,
+    }
+    # attention kernel alone, on the steady-state cache
+    q, k, v = inputs[-1][0][0]
+    ams = timed(lambda: cache.attention(q, k, v, scale, out=out), args.reps, torch)
+    flops = W.attention_flops(wl.n_heads, wl.n_q, cache.tokens()[0] + cache.tokens()[1] + wl.n_q,
+                              wl.head_dim)
+    res["attn_ms"] = ams
+    res["attn_flops"] = flops
+    res["attn_tflops"] = flops / (ams * 1e-3) / 1e12
+    return res
+
+
+def quantize_leg(args, torch, ops, W, device):
+    """Append of one 3-frame chunk of K and V [12, 4680, 128] into a full cache,
+    cycling 10 distinct input sets (287.5 MB > the 256 MB Infinity Cache)."""
+    wl = W.WORKLOADS["quantize"]
+    n_sets = 10
+    log(f"quantize: drawing {n_sets} Student-t input sets on the host")
+    sets = [tuple(dev_bits(torch, b, device) for b in W.clean_chunk(wl, c)) for c in range(n_sets)]
+    cache = ops.KVCache(wl.n_heads, wl.head_dim, wl.tokens_per_frame, wl.sink_frames,
+                        wl.window_frames, device=device)
+    for c in range(4):
+        cache.append(*sets[c], wl.chunk_frames)
+    it = [0]
+
+    def app():
+        k, v = sets[it[0] % n_sets]
+        it[0] += 1
+        cache.append(k, v, wl.chunk_frames)
+
+    reps = max(args.reps, 50)
+    ms = timed(app, reps, torch)
+    elems = wl.n_heads * wl.chunk_tokens * wl.head_dim
+    nbytes = 2 * W.quantize_bytes(elems)
+    gbps = nbytes / (ms * 1e-3) / 1e9
+    return {"us_per_append": ms * 1e3, "bytes_per_append": nbytes, "GB_per_s": gbps,
+            "roofline": {"bound": "hbm", "achieved": gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                         "frac": gbps / HBM_PEAK_GBPS, "traffic": None}}
+
+
+def attention_config(name, args, torch, ops, W, device):
+    wl = W.WORKLOADS[name]
+    log(f"{name}: building the cache from {wl.n_cache_chunks} host-drawn chunks")
+    cache = ops.KVCache(wl.n_heads, wl.head_dim, wl.tokens_per_frame, wl.sink_frames,
+                        wl.window_frames, device=device)
+    for c in range(wl.n_cache_chunks):
+        k, v = W.clean_chunk(wl, c)
+        cache.append(dev_bits(torch, k, device), dev_bits(torch, v, device), wl.chunk_frames)
+    q, ko, vo = (dev_bits(torch, b, device) for b in W.noisy_chunk(wl, wl.n_cache_chunks))
+    out = torch.empty((wl.n_heads, wl.n_q, wl.head_dim), dtype=torch.float32, device=device)
+    reps = args.reps if name != "tiny" else 200
+    ms = timed(lambda: cache.attention(q, ko, vo, wl.softmax_scale, out=out), reps, torch)
+    s, w = cache.tokens()
+    flops = W.attention_flops(wl.n_heads, wl.n_q, s + w + wl.n_q, wl.head_dim)
+    tf = flops / (ms * 1e-3) / 1e12
+    return {"us": ms * 1e3, "cache_tokens": s + w, "n_q": wl.n_q, "tflops": tf,
+            "frac_mfma_peak": tf / MFMA_BF16_PEAK_TFLOPS}
+
+
+def cpu_baseline(args, W):
+    """The oracle, untuned, on a bounded sample: chunk attention of the
+    1.3B-shaped workload (same shape as the steady-state rollout step) for
+    `cpu_rows` query rows of every head over all 23400 keys; plus the oracle
+    codec on one K tensor [12, 4680, 128]."""
+    import numpy as np
+    from oracle import CacheModel, chunk_attention_ref, quantize_ref
+    wl = W.WORKLOADS["wan13b"]
+    model = CacheModel(wl.n_heads, wl.head_dim, wl.tokens_per_frame, wl.sink_frames, wl.window_frames)
+    for c in range(wl.n_cache_chunks):
+        model.append(*W.clean_chunk(wl, c))
+    ck, cv = model.dequantized_kv()
+    q, ko, vo = W.noisy_chunk(wl, wl.n_cache_chunks)
+    rows = np.arange(min(args.cpu_rows, wl.n_q))
+    t0 = time.perf_counter()
+    chunk_attention_ref(q, ko, vo, ck, cv, wl.softmax_scale, rows=rows)
+    dt = time.perf_counter() - t0
+    n_k = ck.shape[1] + wl.n_q
+    flops = W.attention_flops(wl.n_heads, len(rows), n_k, wl.head_dim)
+    k, _ = W.clean_chunk(W.WORKLOADS["quantize"], 0)
+    t1 = time.perf_counter()
+    quantize_ref(k)
+    dq = time.perf_counter() - t1
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [os.cpu_count()])
+    except Exception:
+        cores = os.cpu_count()
+    cpu_model = ""
+    try:
+        for ln in open("/proc/cpuinfo"):
+            if ln.startswith("model name"):
+                cpu_model = ln.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+            "sample": f"float64 chunk attention, 1.3B-shaped cache (12 heads x {len(rows)} query rows x "
+                      f"{n_k} keys x D128), {dt:.1f} s; numpy BLAS threads={cores}; {cpu_model}",
+            "seconds": dt, "host_cpus": os.cpu_count(),
+            "quantize_GB_per_s": W.quantize_bytes(k.size) / dq / 1e9, "quantize_seconds": dq}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(this path is single-GPU; see DESIGN.md for how it would shard)", file=sys.stderr)
+        sys.exit(2)
+    if args.warmup < 4:
+        log("note: warmup < 4 chunks, so the timed steps do not all see the full cache")
+    import torch
+    from nvfp4_kv_cache_amd import ops, workloads as W
+    assert torch.cuda.is_available(), "needs a GPU"
+    device = torch.device("cuda:0")
+    ops.lib()
+    log(f"device: {torch.cuda.get_device_name(0)}")
+
+    r = rollout(args, torch, ops, W, device)
+    log(f"rollout: {r['ms_per_step']:.3f} ms/step, {r['tflops']:.1f} TFLOP/s, "
+        f"{r['frames_per_s']:.1f} frames/s; attention kernel {r['attn_ms']*1e3:.1f} us "
+        f"= {r['attn_tflops']:.1f} TFLOP/s")
+    qz = quantize_leg(args, torch, ops, W, device)
+    log(f"quantize: {qz['us_per_append']:.2f} us/append = {qz['GB_per_s']:.1f} GB/s")
+    configs = {}
+    if not args.skip_configs:
+        for name in ("tiny", "wan13b", "wan5b"):
+            configs[name] = attention_config(name, args, torch, ops, W, device)
+            log(f"{name}: {configs[name]['us']:.1f} us, {configs[name]['tflops']:.1f} TFLOP/s")
+    configs["quantize"] = {k: qz[k] for k in ("us_per_append", "GB_per_s", "bytes_per_append")}
+    configs["quantize"]["frac_hbm_peak"] = qz["roofline"]["frac"]
+
+    wl = W.WORKLOADS["rollout"]
+    result = {
+        "metric": METRIC,
+        "value": r["tflops"],
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": r["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": "streaming rollout, steady state: 12 heads, head_dim 128, 1560 tokens/frame, "
+                        "3-frame chunks (4680 queries) over an NVFP4 cache of 3 sink + 9 window frames "
+                        "(18720 tokens) + 4680 own bf16 tokens; 4 attention calls + 1 append per step",
+            "n_heads": wl.n_heads, "head_dim": wl.head_dim, "tokens_per_frame": wl.tokens_per_frame,
+            "chunk_frames": wl.chunk_frames, "sink_frames": wl.sink_frames,
+            "window_frames": wl.window_frames, "attention_calls_per_step": wl.steps_per_chunk,
+            "cache_tokens": r["cache_tokens"], "steady_state": r["steady_state"],
+        },
+        "latent_frames_per_s": r["frames_per_s"],
+        "wall_ms_per_step": r["wall_ms_per_step"],
+        "roofline": {"bound": "mfma", "kernel": "chunk_attention_kernel<128>",
+                     "achieved": r["attn_tflops"], "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": r["attn_tflops"] / MFMA_BF16_PEAK_TFLOPS, "traffic": None,
+                     "launch_us": r["attn_ms"] * 1e3, "flops_per_launch": r["attn_flops"]},
+        "quantize": qz,
+        "configs": configs,
+        "cpu_baseline": None,
+        "host": platform.node(),
+    }
+    if not args.no_cpu_baseline:
+        log("cpu baseline: running the oracle on a bounded sample")
+        cb = cpu_baseline(args, W)
+        log(f"cpu baseline: {cb['value']*1e3:.2f} GFLOP/s in {cb['seconds']:.1f} s")
+        result["cpu_baseline"] = cb
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -60,7 +60,7 @@ const char *nvfp4kv_version(void);
 /* ------------------------------------------------------------------------------
  * Standalone NVFP4 codec of one tensor (paper section 2.2; reading note section II).
  *
- *   x            bf16 [H, T, D], D % 32 == 0, H, T >= 1 (T may be odd).
+ *   x            bf16 [H, T, D], D % 16 == 0 (16 <= D <= 4096), H, T >= 1 (T may be odd).
  *   codes        uint8 [H, T, D/2]: element 2i in the low nibble, 2i+1 in the high
  *                nibble; nibble = sign << 3 | E2M1 magnitude code.
  *   scales       uint8 [H, T, D/16]: raw E4M3FN bytes of the block scales.
@@ -73,7 +73,7 @@ const char *nvfp4kv_version(void);
  *                filled by the caller before its first use; every call leaves it
  *                ready for the next one.  Calls that share a workspace must not run
  *                concurrently.
- * Errors: EINVAL (null pointer, H/T/D out of range, D % 32 != 0), ECAPACITY (workspace
+ * Errors: EINVAL (null pointer, H/T/D out of range, D % 16 != 0), ECAPACITY (workspace
  * too small), EHIP.
  * ------------------------------------------------------------------------------ */
 size_t nvfp4_quantize_workspace_bytes(void);

@@ -149,7 +149,7 @@ int nvfp4_quantize_kv(const uint16_t *x, int64_t H, int64_t T, int64_t D, uint8_
                       uint8_t *scales, float *tensor_scale, void *workspace,
                       size_t workspace_bytes, void *stream) {
   if (!x || !codes || !scales || !tensor_scale || !workspace) return NVFP4KV_EINVAL;
-  if (H < 1 || T < 1 || D < 32 || D % 32 != 0 || D > 4096) return NVFP4KV_EINVAL;
+  if (H < 1 || T < 1 || D < 16 || D % 16 != 0 || D > 4096) return NVFP4KV_EINVAL;
   if (H * T * D >= (int64_t(1) << 40) || T > (int64_t(1) << 30) || H > (1 << 20))
     return NVFP4KV_EINVAL;
   if (workspace_bytes < sizeof(QuantWorkspace)) return NVFP4KV_ECAPACITY;

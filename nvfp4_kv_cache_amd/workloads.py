@@ -141,3 +141,22 @@ def quantize_bytes(n_elements):
     """Algorithmic bytes of quantizing one tensor: 2 B read, 1/2 B of codes
     and 1/16 B of scale written per element, plus the 4-byte tensor scale."""
     return n_elements * (2.0 + 0.5 + 1.0 / 16.0) + 4.0
+
+
+def device_seed(seed, chunk, step, tensor_id):
+    """64-bit seed for a device-side generator, derived from the same
+    (cfg_seed, chunk, step, tensor_id) key as the host draws."""
+    return int(np.random.SeedSequence([seed, chunk, step, tensor_id]).generate_state(1, np.uint64)[0]
+               & np.uint64(0x7FFFFFFFFFFFFFFF))
+
+
+def draw_device_normal(wl, chunk, step, tensor_id, device, n_tokens=None):
+    """N(0,1) bf16 draw made on the device with torch's seeded generator (used
+    for the long streaming workload, whose hundreds of tensors would take
+    minutes to draw on the host).  Returns an int16 tensor of bf16 bits."""
+    import torch
+    n = wl.chunk_tokens if n_tokens is None else n_tokens
+    g = torch.Generator(device=device)
+    g.manual_seed(device_seed(wl.seed, chunk, step, tensor_id))
+    x = torch.randn((wl.n_heads, n, wl.head_dim), generator=g, device=device, dtype=torch.float32)
+    return x.to(torch.bfloat16).view(torch.int16)

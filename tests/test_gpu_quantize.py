@@ -55,6 +55,7 @@ def test_codec_golden(ops, ws):
 
 
 @pytest.mark.parametrize("shape,scale", [((3, 50, 64), 1.0), ((2, 37, 128), 3.0), ((1, 1, 32), 1.0),
+                                         ((4, 1000, 16), 1.0), ((1, 3, 48), 2.0),
                                          ((5, 129, 96), 1e-3), ((2, 300, 256), 1e4)])
 def test_codec_random(ops, ws, shape, scale):
     rng = np.random.default_rng(hash(shape) % 1000)

@@ -64,7 +64,7 @@ def test_error_paths_before_device_work(real):
     dummy = P(0x10000)
     ws = real.nvfp4_quantize_workspace_bytes()
     assert real.nvfp4_quantize_kv(None, 1, 1, 64, dummy, dummy, dummy, dummy, ws, None) == EINVAL
-    assert real.nvfp4_quantize_kv(dummy, 1, 1, 48, dummy, dummy, dummy, dummy, ws, None) == EINVAL
+    assert real.nvfp4_quantize_kv(dummy, 1, 1, 40, dummy, dummy, dummy, dummy, ws, None) == EINVAL
     assert real.nvfp4_quantize_kv(dummy, 0, 1, 64, dummy, dummy, dummy, dummy, ws, None) == EINVAL
     assert real.nvfp4_quantize_kv(dummy, 1, 1, 64, dummy, dummy, dummy, dummy, ws - 1, None) == ECAPACITY
     real.kvcache_storage_bytes.restype = ctypes.c_size_t
