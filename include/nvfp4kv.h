@@ -69,11 +69,11 @@ const char *nvfp4kv_version(void);
  *   bs = (block amax / 6) / s_t rounded to E4M3 (saturating at 448), element code =
  *   E2M1(|x| / (E4M3(bs) * s_t)) (saturating at 6); a block whose E4M3(bs) * s_t is 0
  *   gets all-zero magnitudes with the element signs kept.  x must be finite.
- *   workspace    device scratch of >= nvfp4_quantize_workspace_bytes() bytes, zero-
- *                filled by the caller before its first use; every call leaves it
- *                ready for the next one.  Calls that share a workspace must not run
- *                concurrently.
- * Errors: EINVAL (null pointer, H/T/D out of range, D % 16 != 0), ECAPACITY (workspace
+ *   workspace    device scratch of >= nvfp4_quantize_workspace_bytes() bytes (per-
+ *                workgroup partial maxima; needs no initialization).  Calls that
+ *                share a workspace must not run concurrently.
+ * Alignment: x 16 bytes, codes 8 bytes, tensor_scale 4 bytes.
+ * Errors: EINVAL (null or misaligned pointer, H/T/D out of range, D % 16 != 0), ECAPACITY (workspace
  * too small), EHIP.
  * ------------------------------------------------------------------------------ */
 size_t nvfp4_quantize_workspace_bytes(void);
@@ -92,6 +92,7 @@ int nvfp4_quantize_kv(const uint16_t *x, int64_t H, int64_t T, int64_t D, uint8_
  *
  * Supported: n_heads >= 1; head_dim 64 or 128; tokens_per_frame >= 8 and a multiple
  * of 8; sink_frames >= 0; window_frames >= 1; sink_frames + window_frames <= 64.
+ * Every bf16 / fp32 tensor argument must be 16-byte aligned.
  * ------------------------------------------------------------------------------ */
 typedef struct {
   int32_t n_heads;
@@ -122,7 +123,7 @@ int kvcache_destroy(kvcache *c);
  * heads), then are quantized straight into their frame slots in one kernel.  The first
  * sink_frames frames ever appended become sinks; each later frame enters the window,
  * and when the window is full the oldest window frame is evicted first (FIFO).
- * Errors: EINVAL (null, n_frames < 1), ECAPACITY (more than window_frames frames of
+ * Errors: EINVAL (null or misaligned, n_frames < 1), ECAPACITY (more than window_frames frames of
  * this chunk would enter the window), EHIP. */
 int kvcache_append(kvcache *c, const uint16_t *k, const uint16_t *v, int32_t n_frames,
                    void *stream);
@@ -143,7 +144,7 @@ int kvcache_chunk_count(const kvcache *c, int32_t *n_chunks);
  * the chunk's own n_q bf16 tokens, with no mask (bidirectional inside the chunk).
  *   q, k_own, v_own  bf16 [H, n_q, D] (finite; |v_own| < 65504);
  *   out              fp32 [H, n_q, D];  n_q >= 1;  softmax_scale > 0 and finite.
- * Errors: EINVAL, EHIP. */
+ * Errors: EINVAL (null or misaligned pointer, bad size or scale), EHIP. */
 int chunk_attention(const kvcache *c, const uint16_t *q, const uint16_t *k_own,
                     const uint16_t *v_own, int64_t n_q, float softmax_scale, float *out,
                     void *stream);

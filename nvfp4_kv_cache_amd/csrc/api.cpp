@@ -23,6 +23,8 @@ constexpr size_t kAlign = 256;
 
 size_t round_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
+bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
 struct Layout {
   int64_t rows;   // token capacity per head
   size_t kcodes, kscales, vcodes, vscales, table, ws, total;
@@ -37,6 +39,10 @@ bool config_ok(const kvcache_config *c) {
     return false;
   if (c->sink_frames < 0 || c->window_frames < 1) return false;
   if (c->sink_frames + c->window_frames > kMaxFrames) return false;
+  // per-head planes are addressed with 32-bit offsets
+  if (int64_t(c->sink_frames + c->window_frames) * c->tokens_per_frame * c->head_dim >=
+      (int64_t(1) << 31))
+    return false;
   return true;
 }
 
@@ -149,6 +155,8 @@ int nvfp4_quantize_kv(const uint16_t *x, int64_t H, int64_t T, int64_t D, uint8_
                       uint8_t *scales, float *tensor_scale, void *workspace,
                       size_t workspace_bytes, void *stream) {
   if (!x || !codes || !scales || !tensor_scale || !workspace) return NVFP4KV_EINVAL;
+  if (!aligned(x, 16) || !aligned(codes, 8) || !aligned(tensor_scale, 4) || !aligned(workspace, 4))
+    return NVFP4KV_EINVAL;
   if (H < 1 || T < 1 || D < 16 || D % 16 != 0 || D > 4096) return NVFP4KV_EINVAL;
   if (H * T * D >= (int64_t(1) << 40) || T > (int64_t(1) << 30) || H > (1 << 20))
     return NVFP4KV_EINVAL;
@@ -209,6 +217,7 @@ int kvcache_destroy(kvcache *c) {
 int kvcache_append(kvcache *c, const uint16_t *k, const uint16_t *v, int32_t n_frames,
                    void *stream) {
   if (!c || !k || !v) return NVFP4KV_EINVAL;
+  if (!aligned(k, 16) || !aligned(v, 16)) return NVFP4KV_EINVAL;
   if (n_frames < 1 || n_frames > kMaxFrames) return NVFP4KV_EINVAL;
   const kvcache_config &cfg = c->cfg;
   if (int64_t(n_frames) * cfg.tokens_per_frame > (int64_t(1) << 30)) return NVFP4KV_EINVAL;
@@ -301,6 +310,8 @@ int chunk_attention(const kvcache *c, const uint16_t *q, const uint16_t *k_own,
                     const uint16_t *v_own, int64_t n_q, float softmax_scale, float *out,
                     void *stream) {
   if (!c || !q || !k_own || !v_own || !out) return NVFP4KV_EINVAL;
+  if (!aligned(q, 16) || !aligned(k_own, 16) || !aligned(v_own, 16) || !aligned(out, 16))
+    return NVFP4KV_EINVAL;
   if (n_q < 1 || n_q > (int64_t(1) << 24)) return NVFP4KV_EINVAL;
   if (!(softmax_scale > 0.0f) || softmax_scale > 3.0e38f) return NVFP4KV_EINVAL;
   AttnArgs a;

@@ -8,23 +8,35 @@
 // inside the attention kernel).
 //
 // Design for CDNA4:
-//  * A workgroup owns 128 queries of one head (4 waves x 32).  Keys stream in tiles
-//    of 64.  Each tile's K and V are dequantized ONCE per workgroup into LDS (K as
-//    bf16, V as fp16) and shared by the 4 waves, so the dequantization VALU work is
-//    not repeated per wave.  E2M1 x E4M3 has at most 6 significant bits and lies in
-//    [2^-10, 2688], so both conversions are exact; the fp32 tensor scales stay
-//    outside the matrix cores (s_K folds into the logit scale, s_V into the units of
-//    the output accumulator).
-//  * S^T = K Q^T runs on v_mfma_f32_32x32x16_bf16 with K from LDS as the A operand
-//    and Q held in registers as the B operand.  The accumulator layout then gives
-//    each lane one query and 16 keys, which is exactly the lane layout of the B
-//    operand of the PV product O^T = V^T P^T; P never leaves registers.  V is
-//    stored in LDS as V^T with the keys of each 16-key group permuted to match.
-//  * PV runs on v_mfma_f32_32x32x16_f16: V^ is exact in fp16 and P in [0,1] keeps 11
-//    significant bits (bf16 would keep 8).  The own segment's bf16 V is converted to
-//    fp16 on staging (|v| < 65504 is required).
-//  * Online softmax in fp32 with exp2 (log2(e) folded into the logit scale).  Row
-//    sums are taken from the fp16-rounded probabilities that enter the PV product.
+//  * A workgroup owns 128 queries of one head (4 waves x 32); two workgroups share
+//    a CU, so each SIMD interleaves two waves: one wave's softmax and dequant VALU
+//    work runs while the other's MFMAs do (measured here: LDS delivers ~210 B/clk
+//    per CU with two waves per SIMD, enough for 32-query waves re-reading K/V from
+//    LDS).  Keys stream in tiles of 64.  Each tile is dequantized ONCE per
+//    workgroup into LDS, double-buffered, while the packed bytes of the next tile
+//    are already in flight to registers.
+//  * Dequantization uses the CDNA4 converts v_cvt_scalef32_pk_f16_fp4 and
+//    _pk_f16_fp8 with scale 1.0 (exact: E2M1 and E4M3 values are fp16 numbers) and
+//    one v_pk_mul_f16 per two elements.  E2M1 x E4M3 has at most 6 significant bits
+//    and lies in [2^-10, 2688], so the product is exact in fp16.  The fp32 tensor
+//    scales stay outside the matrix cores: s_K folds into the logit multiplier,
+//    s_V into the units of the output accumulator.
+//  * S^T = K Q^T on v_mfma_f32_32x32x16_f16: K from LDS as the A operand, Q in
+//    registers as the B operand.  Q is held in fp16 with a per-query power-of-two
+//    scale (row maximum mapped into [2^14, 2^15)); bf16 values map exactly unless an
+//    element is more than ~2^28 below its row maximum.  The scale folds into the
+//    per-query logit multiplier, which is a per-lane value: in this layout each lane
+//    owns one query column and 16 keys, which is also exactly the lane layout of the
+//    B operand of O^T = V^T P^T, so P never leaves registers.  V is stored in LDS as
+//    V^T with the keys of each 16-key group permuted to match.
+//  * The own segment runs after the cache with Q reloaded as bf16 and K_own in
+//    bf16 (v_mfma_f32_32x32x16_bf16); V_own is converted to fp16 for the PV product
+//    (|v| < 65504 required).
+//  * Online softmax in fp32 with exp2 (log2 e folded into the multiplier).  The
+//    running maximum is raised only when a tile's maximum exceeds it by more than
+//    8 (in log2 units), so the accumulator rescale is rare; probabilities are then
+//    bounded by 2^8, well inside fp16.  Row sums are taken from the fp16-rounded
+//    probabilities that enter the PV product.
 //  * Workgroups are numbered so that each XCD (own L2) runs a contiguous range of
 //    (head, query-tile) pairs, i.e. mostly one head's keys.
 
@@ -34,150 +46,334 @@ namespace nvfp4kv {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 namespace {
 
 constexpr int kBN = 64;        // keys per tile
 constexpr int kWaves = 4;
+constexpr int kThreads = kWaves * 64;
 constexpr int kQW = 32;        // queries per wave
 constexpr int kBM = kWaves * kQW;
+constexpr float kLazy = 8.0f;  // log2 headroom before the running max is raised
 
-// 16-key group permutation of V^T in LDS: physical position p holds key kk(p),
-// kk swaps bits 2 and 3 of p (an involution).
-__device__ __forceinline__ int vperm(int p) {
-  return (p & 3) | ((p & 4) << 1) | ((p & 8) >> 1);
-}
-
-// E2M1 magnitude code -> fp32 value.
-__device__ __forceinline__ float e2m1_value(uint32_t m) {
-  // 0, 0.5, 1, 1.5, 2, 3, 4, 6
-  const float lo = (m & 1u) ? 1.5f : 1.0f;
-  const uint32_t e = m >> 1;
-  return e == 0 ? ((m & 1u) ? 0.5f : 0.0f) : lo * __uint_as_float((126u + e) << 23);
-}
-
-__device__ __forceinline__ float nvfp4_value(uint32_t code, float scale) {
-  const float v = e2m1_value(code & 7u) * scale;
-  return (code & 8u) ? -v : v;
-}
-
-// Ks: [kBN][D] bf16, 16-byte chunks of each row XOR-swizzled by the row index.
+// ---------------------------------------------------------------- LDS layouts
+// Rows are padded by 16 bytes: for Ks (row stride 2D+16 B = 68 dwords at D=128) and
+// Vs (144 B = 36 dwords) the 16 lanes of one ds_read_b128 phase, which read 16
+// consecutive rows at the same column, land on 16 distinct 4-bank groups; and every
+// operand address is a per-lane base plus a compile-time offset.
+// Ks: [kBN][D + 8] 16-bit (K rows).
 template <int D>
 __device__ __forceinline__ int ks_off(int row, int chunk) {
-  return row * D + ((chunk ^ (row & (D / 8 - 1))) << 3);
+  return row * (D + 8) + (chunk << 3);
 }
-// Vs: [D][kBN] fp16 (V^T), 16-byte chunks swizzled by the row (d) index.
+template <int D>
+constexpr int kKsElems = kBN * (D + 8);
+// Vs: [D][kBN + 8] 16-bit (V^T rows).
 __device__ __forceinline__ int vs_off(int row, int chunk) {
-  return row * kBN + ((chunk ^ (row & 7)) << 3);
+  return row * (kBN + 8) + (chunk << 3);
+}
+template <int D>
+constexpr int kVsElems = D * (kBN + 8);
+
+__device__ __forceinline__ uint32_t as_u32(f16x2 v) { return __builtin_bit_cast(uint32_t, v); }
+
+// two fp32 -> packed fp16, round toward zero (exact for values fp16 represents)
+__device__ __forceinline__ f16x2 pkrtz(float a, float b) {
+  return __builtin_bit_cast(f16x2, __builtin_amdgcn_cvt_pkrtz(a, b));
+}
+
+// E2M1 pair (byte SEL of w) -> fp16x2, exact
+template <int SEL>
+__device__ __forceinline__ f16x2 fp4x2(uint32_t w) {
+  return __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, SEL);
+}
+// E4M3 pair (word HI of w) -> fp16x2, exact
+template <bool HI>
+__device__ __forceinline__ f16x2 fp8x2(uint32_t w) {
+  return __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, HI);
+}
+
+// Packed bytes of one cache tile held by one thread between its load and its
+// dequantization: kTasks (key, 16-element block) K tasks and kTasks (d, 16-key
+// group) V tasks.
+template <int D>
+struct Packed {
+  static constexpr int kTasks = kBN * (D / 16) / kThreads;
+  uint32_t kc[kTasks][2];    // 16 K codes
+  uint32_t ks[kTasks];       // K scale byte
+  uint32_t vc[kTasks][2];    // 16 V codes (keys 0-7, 8-15)
+  uint32_t vs[kTasks][4];    // 16 V scale bytes
+};
+
+struct TileRef {
+  int seg;           // segment index
+  int k0;            // first key of the tile within the segment
+};
+
+// One head's cache planes (uniform pointers: the loads below use a scalar base and
+// a 32-bit per-lane offset).
+struct HeadPlanes {
+  const uint8_t *kc, *ks, *vc, *vs;
+  uint32_t rows;
+};
+
+template <int D>
+__device__ __forceinline__ HeadPlanes head_planes(const AttnArgs &a, int h) {
+  constexpr int nb = D / 16;
+  HeadPlanes p;
+  p.rows = uint32_t(a.rows);
+  p.kc = a.kcodes + size_t(h) * a.rows * (D / 2);
+  p.ks = a.kscales + size_t(h) * a.rows * nb;
+  p.vc = a.vcodes + size_t(h) * D * (a.rows / 2);
+  p.vs = a.vscales + size_t(h) * nb * a.rows;
+  return p;
 }
 
 template <int D>
-__device__ __forceinline__ void stage_cache_tile(const AttnArgs &a, int h, int tok, int nval,
-                                                 uint16_t *Ks, uint16_t *Vs) {
+__device__ __forceinline__ void load_packed(const HeadPlanes &hp, uint32_t tok, int nval,
+                                            Packed<D> &p) {
   constexpr int nb = D / 16;
-  const int tid = threadIdx.x;
-  // ---- K: (key, block) tasks, 16 codes + 1 scale each -> 16 bf16
-  for (int task = tid; task < kBN * nb; task += kWaves * 64) {
-    const int key = task / nb, b = task % nb;
-    uint32_t c0 = 0, c1 = 0, sc = 0;
-    if (key < nval) {
-      const int64_t row = int64_t(h) * a.rows + tok + key;
-      const uint32_t *cp = reinterpret_cast<const uint32_t *>(a.kcodes + row * (D / 2) + b * 8);
-      c0 = cp[0];
-      c1 = cp[1];
-      sc = a.kscales[row * nb + b];
-    }
-    const float s = e4m3_value(sc);
-    uint32_t o[8];
 #pragma unroll
-    for (int e = 0; e < 16; e += 2) {
-      const uint32_t w = e < 8 ? c0 : c1;
-      const uint32_t n0 = (w >> (4 * (e & 7))) & 0xFu, n1 = (w >> (4 * ((e + 1) & 7))) & 0xFu;
-      // exact in bf16: truncating the fp32 bits loses nothing
-      const uint32_t b0 = __float_as_uint(nvfp4_value(n0, s)) >> 16;
-      const uint32_t b1 = __float_as_uint(nvfp4_value(n1, s)) >> 16;
-      o[e >> 1] = b0 | (b1 << 16);
+  for (int i = 0; i < Packed<D>::kTasks; ++i) {
+    const int t = threadIdx.x + i * kThreads;
+    // K task: (key, block) = (t / nb, t % nb)
+    {
+      const int key = t / nb, b = t % nb;
+      p.kc[i][0] = p.kc[i][1] = 0;
+      p.ks[i] = 0;
+      if (key < nval) {
+        const uint32_t row = tok + uint32_t(key);
+        const uint2 c = *reinterpret_cast<const uint2 *>(hp.kc + (row * (D / 2) + uint32_t(b) * 8));
+        p.kc[i][0] = c.x;
+        p.kc[i][1] = c.y;
+        p.ks[i] = hp.ks[row * nb + uint32_t(b)];
+      }
     }
-    *reinterpret_cast<uint4 *>(Ks + ks_off<D>(key, 2 * b)) = make_uint4(o[0], o[1], o[2], o[3]);
-    *reinterpret_cast<uint4 *>(Ks + ks_off<D>(key, 2 * b + 1)) = make_uint4(o[4], o[5], o[6], o[7]);
+    // V task: (d, 16-key group) = (t / 4, t % 4)
+    {
+      const int d = t >> 2, g = t & 3;
+      p.vc[i][0] = p.vc[i][1] = 0;
+      for (int j = 0; j < 4; ++j) p.vs[i][j] = 0;
+      const uint32_t c0 = uint32_t(d) * (hp.rows / 2) + (tok >> 1) + uint32_t(g) * 8;
+      const uint32_t s0 = uint32_t(d >> 4) * hp.rows + tok + uint32_t(g) * 16;
+      const uint32_t *cp = reinterpret_cast<const uint32_t *>(hp.vc + c0);
+      const uint32_t *sp = reinterpret_cast<const uint32_t *>(hp.vs + s0);
+      if (g * 16 < nval) {          // nval is a multiple of 8
+        p.vc[i][0] = cp[0];
+        p.vs[i][0] = sp[0];
+        p.vs[i][1] = sp[1];
+      }
+      if (g * 16 + 8 < nval) {
+        p.vc[i][1] = cp[1];
+        p.vs[i][2] = sp[2];
+        p.vs[i][3] = sp[3];
+      }
+    }
   }
-  // ---- V^T: (d, 16-key group) tasks, 16 codes + 16 scales each -> 16 fp16
-  for (int task = tid; task < D * (kBN / 16); task += kWaves * 64) {
-    const int d = task >> 2, g = task & 3;
-    uint32_t cw[2] = {0u, 0u}, sw[4] = {0u, 0u, 0u, 0u};
-    const int64_t crow = (int64_t(h) * D + d) * (a.rows / 2) + (tok >> 1) + g * 8;
-    const int64_t srow = (int64_t(h) * nb + (d >> 4)) * a.rows + tok + g * 16;
-    const uint32_t *cp = reinterpret_cast<const uint32_t *>(a.vcodes + crow);
-    const uint32_t *sp = reinterpret_cast<const uint32_t *>(a.vscales + srow);
-    if (g * 16 < nval) {      // nval is a multiple of 8
-      cw[0] = cp[0];
-      sw[0] = sp[0];
-      sw[1] = sp[1];
+}
+
+// 16 E2M1 codes (w0: keys/elements 0-7, w1: 8-15) times 8 fp16 scale pairs ->
+// 8 fp16 pairs in natural order.
+__device__ __forceinline__ void dequant16(uint32_t w0, uint32_t w1, const f16x2 (&s)[8],
+                                          uint32_t (&o)[8]) {
+  o[0] = as_u32(fp4x2<0>(w0) * s[0]);
+  o[1] = as_u32(fp4x2<1>(w0) * s[1]);
+  o[2] = as_u32(fp4x2<2>(w0) * s[2]);
+  o[3] = as_u32(fp4x2<3>(w0) * s[3]);
+  o[4] = as_u32(fp4x2<0>(w1) * s[4]);
+  o[5] = as_u32(fp4x2<1>(w1) * s[5]);
+  o[6] = as_u32(fp4x2<2>(w1) * s[6]);
+  o[7] = as_u32(fp4x2<3>(w1) * s[7]);
+}
+
+template <int D>
+__device__ __forceinline__ void dequant_store(const Packed<D> &p, uint16_t *Ks, uint16_t *Vs) {
+  constexpr int nb = D / 16;
+#pragma unroll
+  for (int i = 0; i < Packed<D>::kTasks; ++i) {
+    const int t = threadIdx.x + i * kThreads;
+    {
+      const int key = t / nb, b = t % nb;
+      const f16x2 s0 = fp8x2<false>(p.ks[i] | (p.ks[i] << 8));   // (s, s)
+      const f16x2 sa[8] = {s0, s0, s0, s0, s0, s0, s0, s0};
+      uint32_t o[8];
+      dequant16(p.kc[i][0], p.kc[i][1], sa, o);
+      *reinterpret_cast<uint4 *>(Ks + ks_off<D>(key, 2 * b)) = make_uint4(o[0], o[1], o[2], o[3]);
+      *reinterpret_cast<uint4 *>(Ks + ks_off<D>(key, 2 * b + 1)) = make_uint4(o[4], o[5], o[6], o[7]);
     }
-    if (g * 16 + 8 < nval) {
-      cw[1] = cp[1];
-      sw[2] = sp[2];
-      sw[3] = sp[3];
+    {
+      const int d = t >> 2, g = t & 3;
+      const f16x2 s[8] = {fp8x2<false>(p.vs[i][0]), fp8x2<true>(p.vs[i][0]), fp8x2<false>(p.vs[i][1]),
+                          fp8x2<true>(p.vs[i][1]), fp8x2<false>(p.vs[i][2]), fp8x2<true>(p.vs[i][2]),
+                          fp8x2<false>(p.vs[i][3]), fp8x2<true>(p.vs[i][3])};
+      uint32_t o[8];
+      dequant16(p.vc[i][0], p.vc[i][1], s, o);
+      // physical key order within the 16-key group: pairs {0,1,4,5} then {2,3,6,7}
+      *reinterpret_cast<uint4 *>(Vs + vs_off(d, 2 * g)) = make_uint4(o[0], o[1], o[4], o[5]);
+      *reinterpret_cast<uint4 *>(Vs + vs_off(d, 2 * g + 1)) = make_uint4(o[2], o[3], o[6], o[7]);
     }
-    _Float16 v[16];
+  }
+}
+
+// Own bf16 K/V tile -> LDS (K as bf16, V^T as fp16).
+template <int D>
+__device__ __forceinline__ void stage_own(const AttnArgs &a, int h, int tok, int nval,
+                                          uint16_t *Ks, uint16_t *Vs) {
+  const int t = threadIdx.x;
+  constexpr int qpr = D / 32;                    // 32-element quarters per key row
+  for (int task = t; task < kBN * qpr; task += kThreads) {
+    const int key = task / qpr, qd = task % qpr;
+    uint4 v[4] = {make_uint4(0, 0, 0, 0), make_uint4(0, 0, 0, 0), make_uint4(0, 0, 0, 0),
+                  make_uint4(0, 0, 0, 0)};
+    if (key < nval) {
+      const uint4 *src = reinterpret_cast<const uint4 *>(
+          a.k_own + size_t(h) * a.n_q * D + (uint32_t(tok + key) * D + uint32_t(qd) * 32));
+#pragma unroll
+      for (int i = 0; i < 4; ++i) v[i] = src[i];
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) *reinterpret_cast<uint4 *>(Ks + ks_off<D>(key, 4 * qd + i)) = v[i];
+  }
+  // V^T: thread = (d pair, 16-key group); one dword (d, d+1) per key
+  for (int task = t; task < (D / 2) * (kBN / 16); task += kThreads) {
+    const int dp = task % (D / 2), g = task / (D / 2);   // 2 groups of 16 keys
+    const int d = 2 * dp;
+    uint32_t w[16];
 #pragma unroll
     for (int k = 0; k < 16; ++k) {
-      const uint32_t code = (cw[k >> 3] >> (4 * (k & 7))) & 0xFu;
-      const uint32_t sb = (sw[k >> 2] >> (8 * (k & 3))) & 0xFFu;
-      v[k] = _Float16(nvfp4_value(code, e4m3_value(sb)));   // exact
+      const int key = g * 16 + k;
+      w[k] = 0;
+      if (key < nval)
+        w[k] = *reinterpret_cast<const uint32_t *>(a.v_own + size_t(h) * a.n_q * D +
+                                                   (uint32_t(tok + key) * D + uint32_t(d)));
     }
-    f16x8 lo, hi;
+    uint32_t lo[8], hi[8];   // fp16 pairs (key 2i, key 2i+1) of row d and of row d+1
 #pragma unroll
-    for (int p = 0; p < 8; ++p) {
-      lo[p] = v[vperm(p)];
-      hi[p] = v[vperm(p + 8)];
+    for (int i = 0; i < 8; ++i) {
+      lo[i] = as_u32(pkrtz(__uint_as_float(w[2 * i] << 16),
+                                                __uint_as_float(w[2 * i + 1] << 16)));
+      hi[i] = as_u32(pkrtz(__uint_as_float(w[2 * i] & 0xFFFF0000u),
+                                                __uint_as_float(w[2 * i + 1] & 0xFFFF0000u)));
     }
-    *reinterpret_cast<f16x8 *>(Vs + vs_off(d, 2 * g)) = lo;
-    *reinterpret_cast<f16x8 *>(Vs + vs_off(d, 2 * g + 1)) = hi;
+    *reinterpret_cast<uint4 *>(Vs + vs_off(d, 2 * g)) = make_uint4(lo[0], lo[1], lo[4], lo[5]);
+    *reinterpret_cast<uint4 *>(Vs + vs_off(d, 2 * g + 1)) = make_uint4(lo[2], lo[3], lo[6], lo[7]);
+    *reinterpret_cast<uint4 *>(Vs + vs_off(d + 1, 2 * g)) = make_uint4(hi[0], hi[1], hi[4], hi[5]);
+    *reinterpret_cast<uint4 *>(Vs + vs_off(d + 1, 2 * g + 1)) = make_uint4(hi[2], hi[3], hi[6], hi[7]);
   }
 }
 
-template <int D>
-__device__ __forceinline__ void stage_own_tile(const AttnArgs &a, int h, int tok, int nval,
-                                               uint16_t *Ks, uint16_t *Vs) {
-  constexpr int nb = D / 16;
-  const int tid = threadIdx.x;
-  for (int task = tid; task < kBN * nb; task += kWaves * 64) {
-    const int key = task / nb, b = task % nb;
-    uint4 k0 = make_uint4(0, 0, 0, 0), k1 = k0, v0 = k0, v1 = k0;
-    if (key < nval) {
-      const int64_t off = (int64_t(h) * a.n_q + tok + key) * D + b * 16;
-      const uint4 *kp = reinterpret_cast<const uint4 *>(a.k_own + off);
-      const uint4 *vp = reinterpret_cast<const uint4 *>(a.v_own + off);
-      k0 = kp[0];
-      k1 = kp[1];
-      v0 = vp[0];
-      v1 = vp[1];
-    }
-    *reinterpret_cast<uint4 *>(Ks + ks_off<D>(key, 2 * b)) = k0;
-    *reinterpret_cast<uint4 *>(Ks + ks_off<D>(key, 2 * b + 1)) = k1;
-    // V: bf16 -> fp16, scattered into V^T
-    const uint32_t vw[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
-    const int g = key >> 4, kk = key & 15;
-    const int p = vperm(kk);
-    const int chunk = 2 * g + (p >> 3);
+struct Softmax {
+  float m;      // running max (log2 units) of the lane's query
+  float l;      // partial row sum over this lane's keys
+};
+
+// One tile: S^T = K Q^T, online softmax, O^T += V^T P^T, for the wave's 32 queries.
+template <int D, bool BF16, bool MASK>
+__device__ __forceinline__ void compute_tile(const uint16_t *Ks, const uint16_t *Vs,
+                                             const u32x4 (&qr)[D / 16], float cmul, int nval,
+                                             Softmax &sm, f32x16 (&acc)[D / 32]) {
+  const int lane = threadIdx.x & 63, half = lane >> 5, l32 = lane & 31;
+  f32x16 s[2];   // [32-key block]
 #pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      const uint32_t hb = (e & 1) ? (vw[e >> 1] >> 16) : (vw[e >> 1] & 0xFFFFu);
-      const _Float16 hv = _Float16(bf16_bits_to_float(hb));
-      const int d = b * 16 + e;
-      Vs[vs_off(d, chunk) + (p & 7)] = __builtin_bit_cast(uint16_t, hv);
+  for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) s[kb][r] = 0.0f;
+    const int row = kb * 32 + l32;
+#pragma unroll
+    for (int st = 0; st < D / 16; ++st) {
+      const u32x4 kw = *reinterpret_cast<const u32x4 *>(Ks + ks_off<D>(row, 2 * st + half));
+      if constexpr (BF16)
+        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+            __builtin_bit_cast(bf16x8, kw), __builtin_bit_cast(bf16x8, qr[st]), s[kb], 0, 0, 0);
+      else
+        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
+            __builtin_bit_cast(f16x8, kw), __builtin_bit_cast(f16x8, qr[st]), s[kb], 0, 0, 0);
     }
   }
+  // keys past the end of the segment (only in a segment's last tile): excluded
+  // from the maximum here and given probability 0 below
+  if constexpr (MASK) {
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int key = kb * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
+        if (key >= nval) s[kb][r] = -INFINITY;
+      }
+  }
+  float mx = fmaxf(s[0][0], s[1][0]);
+#pragma unroll
+  for (int r = 1; r < 16; ++r) mx = fmaxf(mx, fmaxf(s[0][r], s[1][r]));
+  mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+  const float tmax = mx * cmul;
+  // raise the running max only when this tile exceeds it by more than kLazy
+  if (__any(tmax > sm.m + kLazy)) {
+    const float mnew = fmaxf(sm.m, tmax);
+    const float alpha = __builtin_amdgcn_exp2f(sm.m - mnew);
+    sm.m = mnew;
+    sm.l *= alpha;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) acc[db] *= alpha;
+  }
+  const float mneg = -sm.m;
+  float lsum = 0.0f;
+  f16x8 p[4];    // [16-key step]
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+      f16x8 v;
+#pragma unroll
+      for (int i = 0; i < 8; i += 2) {
+        float e0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][8 * hh + i], cmul, mneg));
+        float e1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][8 * hh + i + 1], cmul, mneg));
+        if constexpr (MASK) {
+          const int r0 = 8 * hh + i;
+          const int key0 = kb * 32 + 8 * (r0 >> 2) + 4 * half + (r0 & 3);
+          if (key0 >= nval) e0 = 0.0f;
+          if (key0 + 1 >= nval) e1 = 0.0f;
+        }
+        const f16x2 pr = pkrtz(e0, e1);
+        lsum = __builtin_amdgcn_fdot2(pr, f16x2{1.0f16, 1.0f16}, lsum, false);
+        v[i] = pr[0];
+        v[i + 1] = pr[1];
+      }
+      p[2 * kb + hh] = v;
+    }
+  sm.l += lsum;
+  // O^T += V^T P^T
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db) {
+    const int row = db * 32 + l32;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      const f16x8 vf = *reinterpret_cast<const f16x8 *>(Vs + vs_off(row, 2 * ks + half));
+      acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vf, p[ks], acc[db], 0, 0, 0);
+    }
+  }
+}
+
+// Loads the wave's 32 query rows as MFMA B operands (bf16 bits).
+template <int D>
+__device__ __forceinline__ void load_q(const AttnArgs &a, int h, int q0, u32x4 (&qr)[D / 16]) {
+  const int lane = threadIdx.x & 63, half = lane >> 5, l32 = lane & 31;
+  const int qi = q0 + l32;
+  const bool ok = qi < a.n_q;
+  const uint16_t *qp = a.q + (int64_t(h) * a.n_q + (ok ? qi : 0)) * D + 8 * half;
+#pragma unroll
+  for (int st = 0; st < D / 16; ++st)
+    qr[st] = ok ? *reinterpret_cast<const u32x4 *>(qp + 16 * st) : u32x4{0, 0, 0, 0};
 }
 
 }  // namespace
 
 template <int D>
-__global__ __launch_bounds__(kWaves * 64, 2) void chunk_attention_kernel(AttnArgs a) {
-  __shared__ __attribute__((aligned(16))) uint16_t Ks[kBN * D];
-  __shared__ __attribute__((aligned(16))) uint16_t Vs[D * kBN];
+__global__ __launch_bounds__(kThreads, 2) void chunk_attention_kernel(AttnArgs a) {
+  __shared__ __attribute__((aligned(16))) uint16_t Ks[2][kKsElems<D>];
+  __shared__ __attribute__((aligned(16))) uint16_t Vs[2][kVsElems<D>];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int half = lane >> 5, l32 = lane & 31;
 
@@ -188,109 +384,115 @@ __global__ __launch_bounds__(kWaves * 64, 2) void chunk_attention_kernel(AttnArg
   const int logical = xcd * (n >> 3) + min(xcd, n & 7) + (bid >> 3);
   const int qtiles = (a.n_q + kBM - 1) / kBM;
   const int h = logical / qtiles;
-  const int qt = logical - h * qtiles;
-  const int qi = qt * kBM + w * kQW + l32;   // this lane's query
-  const bool qok = qi < a.n_q;
+  const int q0 = (logical - h * qtiles) * kBM + w * kQW;
+  const int qi = q0 + l32;
 
-  bf16x8 qreg[D / 16];
+  // ---- Q as fp16 with a per-query power-of-two scale 2^sh (row max -> [2^14, 2^15))
+  u32x4 qr[D / 16];
+  load_q<D>(a, h, q0, qr);
+  float cq;
   {
-    const uint16_t *qp = a.q + (int64_t(h) * a.n_q + (qok ? qi : 0)) * D + 8 * half;
+    uint32_t mx = 0;
 #pragma unroll
-    for (int s = 0; s < D / 16; ++s) {
-      if (qok) qreg[s] = *reinterpret_cast<const bf16x8 *>(qp + 16 * s);
-      else
-        for (int e = 0; e < 8; ++e) qreg[s][e] = __bf16(0.0f);
-    }
+    for (int st = 0; st < D / 16; ++st)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const uint32_t v = qr[st][j] & 0x7FFF7FFFu;
+        mx = max(mx, max(v & 0xFFFFu, v >> 16));
+      }
+    mx = max(mx, uint32_t(__shfl_xor(int(mx), 32, 64)));
+    const int e = int(mx >> 7) - 127;   // floor(log2(row max)) (bf16 normals)
+    int sh = mx ? 14 - e : 0;
+    sh = max(-110, min(100, sh));
+    cq = __builtin_ldexpf(1.0f, -sh);
+#pragma unroll
+    for (int st = 0; st < D / 16; ++st)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const uint32_t v = qr[st][j];
+        qr[st][j] = as_u32(pkrtz(__builtin_ldexpf(__uint_as_float(v << 16), sh),
+                                 __builtin_ldexpf(__uint_as_float(v & 0xFFFF0000u), sh)));
+      }
   }
+
   f32x16 acc[D / 32];
 #pragma unroll
-  for (int i = 0; i < D / 32; ++i)
-    for (int r = 0; r < 16; ++r) acc[i][r] = 0.0f;
-  float m = -INFINITY, lsum = 0.0f, vunit = 1.0f;
+  for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[db][r] = 0.0f;
+  Softmax sm;
+  sm.m = -INFINITY;
+  sm.l = 0.0f;
+  float vunit = 1.0f;
 
-  for (int si = 0; si <= a.n_seg; ++si) {
-    const bool own = si == a.n_seg;
-    int tok0, ntok;
-    float sk = 1.0f, sv = 1.0f;
-    if (own) {
-      tok0 = 0;
-      ntok = a.n_q;
-    } else {
-      tok0 = a.seg[si].tok0;
-      ntok = a.seg[si].ntok;
-      sk = a.scale_table[2 * a.seg[si].scale_slot];
-      sv = a.scale_table[2 * a.seg[si].scale_slot + 1];
-    }
-    const float C = a.sm_scale_log2 * sk;
-    // keep the accumulator in units of this segment's s_V (an all-zero V chunk has
-    // s_V = 0 and contributes nothing, so it keeps the current units)
-    if (sv > 0.0f) {
-      const float r = vunit / sv;
+  // ---- cache segments (NVFP4), software-pipelined over tiles
+  if (a.n_seg > 0) {
+    int cs = 0, ck = 0;   // current tile: segment, first key
+    const HeadPlanes hp = head_planes<D>(a, h);
+    Packed<D> pk;
+    load_packed<D>(hp, uint32_t(a.seg[0].tok0), min(kBN, a.seg[0].ntok), pk);
+    int buf = 0;
+    int cur_seg = -1;
+    float cmul = 0.0f;
+    while (cs < a.n_seg) {
+      const Segment sg = a.seg[cs];
+      const int nval = min(kBN, sg.ntok - ck);
+      int ns = cs, nk = ck + kBN;
+      if (nk >= sg.ntok) {
+        ns += 1;
+        nk = 0;
+      }
+      dequant_store<D>(pk, Ks[buf], Vs[buf]);
+      if (ns < a.n_seg) {
+        const Segment sn = a.seg[ns];
+        load_packed<D>(hp, uint32_t(sn.tok0 + nk), min(kBN, sn.ntok - nk), pk);
+      }
+      if (cs != cur_seg) {
+        cur_seg = cs;
+        const float sk = a.scale_table[2 * sg.scale_slot];
+        const float sv = a.scale_table[2 * sg.scale_slot + 1];
+        cmul = a.sm_scale_log2 * sk * cq;
+        // accumulator in units of this segment's s_V (an all-zero V chunk has
+        // s_V = 0 and contributes nothing: keep the current units)
+        if (sv > 0.0f) {
+          const float r = vunit / sv;
 #pragma unroll
-      for (int i = 0; i < D / 32; ++i) acc[i] *= r;
-      vunit = sv;
-    }
-    for (int k0 = 0; k0 < ntok; k0 += kBN) {
-      const int nval = min(kBN, ntok - k0);
-      __syncthreads();
-      if (own) stage_own_tile<D>(a, h, k0, nval, Ks, Vs);
-      else stage_cache_tile<D>(a, h, tok0 + k0, nval, Ks, Vs);
-      __syncthreads();
-
-      // S^T = K Q^T for the wave's 32 queries: two 32-key blocks
-      f32x16 sacc[2];
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        for (int r = 0; r < 16; ++r) sacc[kb][r] = 0.0f;
-        const int row = kb * 32 + l32;
-#pragma unroll
-        for (int s = 0; s < D / 16; ++s) {
-          const bf16x8 kf = *reinterpret_cast<const bf16x8 *>(Ks + ks_off<D>(row, 2 * s + half));
-          sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qreg[s], sacc[kb], 0, 0, 0);
+          for (int db = 0; db < D / 32; ++db) acc[db] *= r;
+          vunit = sv;
         }
       }
-      // online softmax (lane = one query, 32 of the tile's keys; partner lane^32 has the rest)
-      float mx = -INFINITY;
+      __syncthreads();
+      if (nval < kBN) compute_tile<D, false, true>(Ks[buf], Vs[buf], qr, cmul, nval, sm, acc);
+      else compute_tile<D, false, false>(Ks[buf], Vs[buf], qr, cmul, nval, sm, acc);
+      buf ^= 1;
+      cs = ns;
+      ck = nk;
+    }
+    __syncthreads();
+  }
+
+  // ---- own segment (bf16 K/V of the chunk itself)
+  {
+    load_q<D>(a, h, q0, qr);   // plain bf16 Q
+    const float cmul = a.sm_scale_log2;
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = kb * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
-          if (key < nval) mx = fmaxf(mx, sacc[kb][r]);
-        }
-      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-      const float mnew = fmaxf(m, mx * C);
-      const float alpha = __builtin_amdgcn_exp2f(m - mnew);
-      m = mnew;
-      lsum *= alpha;
-#pragma unroll
-      for (int i = 0; i < D / 32; ++i) acc[i] *= alpha;
-      f16x8 pf[4];
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = kb * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
-          const float p = key < nval ? __builtin_amdgcn_exp2f(sacc[kb][r] * C - m) : 0.0f;
-          const _Float16 ph = _Float16(p);
-          lsum += float(ph);
-          pf[2 * kb + (r >> 3)][r & 7] = ph;
-        }
-      // O^T += V^T P^T
-#pragma unroll
-      for (int db = 0; db < D / 32; ++db) {
-        const int row = db * 32 + l32;
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
-          const f16x8 vf = *reinterpret_cast<const f16x8 *>(Vs + vs_off(row, 2 * ks + half));
-          acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vf, pf[ks], acc[db], 0, 0, 0);
-        }
-      }
+    for (int db = 0; db < D / 32; ++db) acc[db] *= vunit;   // to s_V = 1 units
+    vunit = 1.0f;
+    int buf = 0;
+    for (int k0 = 0; k0 < a.n_q; k0 += kBN) {
+      const int nval = min(kBN, a.n_q - k0);
+      stage_own<D>(a, h, k0, nval, Ks[buf], Vs[buf]);
+      __syncthreads();
+      if (nval < kBN) compute_tile<D, true, true>(Ks[buf], Vs[buf], qr, cmul, nval, sm, acc);
+      else compute_tile<D, true, false>(Ks[buf], Vs[buf], qr, cmul, nval, sm, acc);
+      buf ^= 1;
     }
   }
-  const float ltot = lsum + __shfl_xor(lsum, 32, 64);
+
+  // ---- epilogue: O = acc * s_V / l
+  const float ltot = sm.l + __shfl_xor(sm.l, 32, 64);
   const float fin = vunit / ltot;
-  if (qok) {
+  if (qi < a.n_q) {
     float *op = a.out + (int64_t(h) * a.n_q + qi) * D;
 #pragma unroll
     for (int db = 0; db < D / 32; ++db)
@@ -310,9 +512,9 @@ int launch_attention(const AttnArgs &a, void *stream) {
   const int64_t nblk = int64_t(qtiles) * a.H;
   if (nblk >= (int64_t(1) << 31)) return NVFP4KV_EINVAL;
   if (a.D == 128)
-    hipLaunchKernelGGL(chunk_attention_kernel<128>, dim3(unsigned(nblk)), dim3(kWaves * 64), 0, s, a);
+    hipLaunchKernelGGL(chunk_attention_kernel<128>, dim3(unsigned(nblk)), dim3(kThreads), 0, s, a);
   else if (a.D == 64)
-    hipLaunchKernelGGL(chunk_attention_kernel<64>, dim3(unsigned(nblk)), dim3(kWaves * 64), 0, s, a);
+    hipLaunchKernelGGL(chunk_attention_kernel<64>, dim3(unsigned(nblk)), dim3(kThreads), 0, s, a);
   else
     return NVFP4KV_EINVAL;
   return NVFP4KV_HIP_OK(hipGetLastError());

@@ -15,15 +15,10 @@ constexpr int kMaxSegments = kMaxFrames;  // one per resident frame at worst
 constexpr int kMaxQuantGrid = 2048;       // workgroups of one quantize launch
 constexpr int kQuantThreads = 256;
 
-// Grid-barrier state and per-workgroup partial maxima of the single-pass quantizer.
-// `count` returns to 0 at the end of every launch and `gen` only grows, so the
-// block stays valid across calls once it has been zero-filled.
+// Per-workgroup partial maxima of |x| (fp32 bit patterns) written by the amax
+// pass and read by the encode pass of the same call; no state survives a call.
 struct QuantWorkspace {
-  uint32_t count;
-  uint32_t gen;
-  uint32_t timeout;   // set if a barrier wait ever gave up (never expected)
-  uint32_t pad;
-  uint32_t partial[2][kMaxQuantGrid];   // |x| maxima as fp32 bit patterns
+  uint32_t partial[2][kMaxQuantGrid];
 };
 
 // One tensor of a quantize launch.  Source: bf16 [H][T][D].  Destination, canonical

@@ -2,28 +2,48 @@
 //
 // Format (paper text section 2.2; reading note section II "The NVFP4
 // quantization format"): 16-element blocks along head_dim, one E4M3 scale per
-// block, one fp32 scale per tensor, E2M1 elements.  Recipe: s_t = amax/2688,
-// bs = (block amax / 6) / s_t -> E4M3 (RNE, saturating), code = E2M1(|x| / (E4M3(bs)
-// * s_t)) (RNE, saturating), sign kept; fp32 throughout with IEEE division.
+// block, one fp32 scale per tensor, E2M1 elements.  Recipe, in fp32 with correctly
+// rounded operations: s_t = amax / 2688; bs = (block amax / 6) / s_t rounded to
+// E4M3 (nearest, ties to even, saturating at 448); eff = E4M3(bs) * s_t;
+// code = E2M1(|x| / eff) (nearest, ties to even, saturating at 6) with x's sign.
 //
-// The tensor scale needs the amax of the whole chunk tensor before any block can
-// be encoded.  The main kernel does it in ONE read of the input: every workgroup
-// loads its tiles into registers and reduces their maxima, all workgroups meet at
-// a grid barrier (cooperative launch, so all are co-resident), read the per-
-// workgroup partial maxima, and encode from registers.  Inputs too large to sit
-// in registers take a two-kernel path (amax pass, then an encode pass that re-reads
-// the input).
+// Two kernels.  The tensor scale needs the amax of the whole chunk tensor (all
+// heads) before any block can be encoded; a grid-wide barrier inside one kernel
+// would need a cooperative launch, which costs far more on this GPU than the whole
+// quantization, so:
+//   1. quantize_amax_kernel streams K and V once and writes one partial maximum
+//      per workgroup (no atomics);
+//   2. quantize_encode_kernel reduces the partials, then re-reads its tiles (the
+//      chunk, 28.8 MB for the 1.3B shape, is still in the 256 MB Infinity Cache)
+//      and writes codes and scales.
+//
+// Exact encoding without a division per element.  The gfx950 converts
+// v_cvt_scalef32_pk_fp4_f32 / _fp8_f32 (scale 1.0) round to nearest-even and
+// saturate exactly like the recipe for every finite fp32 input (fp8 needs a clamp
+// at 448, above which it returns NaN).  So the code of the correctly rounded
+// quotient q = RN(|x| / eff) is hw_fp4(q).  With r ~ 1/eff (v_rcp_f32, <= 1 ulp),
+// q_hi = x * r * (1 + 2^-20) and q_lo = x * r * (1 - 2^-20) bracket q (their error
+// is below 2^-22 relative); the E2M1 code is monotone in q, so when
+// hw_fp4(q_lo) == hw_fp4(q_hi) that is hw_fp4(q).  Otherwise -- q within ~2^-20 of a
+// rounding threshold, rare except for data built on the grid -- the element is
+// divided exactly.  The block scale uses the same bracket on (amax/6)/s_t with
+// hw_fp8, falling back to the two divisions.
 //
 // Work unit: a tile of (256 / (D/16)) token pairs x all D/16 blocks of one head of
 // one frame; thread (pair p, block b) owns 2 tokens x 16 elements.  Tiles never
 // straddle a frame, so each tile lands in one cache slot.  K (and the standalone
 // codec) are written in the codec layout [h][token][D/2]; V in the cache is written
-// transposed, [h][d][token/2], via an LDS transpose, so that the attention kernel
-// can read 8 consecutive keys of one d with one load.
+// transposed, [h][d][token/2], through LDS, so that the attention kernel can read 8
+// consecutive keys of one d with one load.  For the transposed layout a byte holds
+// tokens (2p, 2p+1) of one d, and the fp4 convert is fed exactly that pair.
 
 #include "device_common.h"
 
 namespace nvfp4kv {
+
+constexpr int kAmaxThreads = 1024;
+
+typedef short short2_ __attribute__((ext_vector_type(2)));
 
 namespace {
 
@@ -44,98 +64,182 @@ __device__ __forceinline__ TileInfo decode_tile(const QuantArgs &a, int tile) {
   return t;
 }
 
+// max of the 8 |bf16| in a uint4, as two packed 16-bit halves
+__device__ __forceinline__ uint32_t vmax4(uint4 u) {
+  const uint32_t a = u.x & 0x7FFF7FFFu, b = u.y & 0x7FFF7FFFu;
+  const uint32_t c = u.z & 0x7FFF7FFFu, d = u.w & 0x7FFF7FFFu;
+  auto pmax = [](uint32_t p, uint32_t q) {
+    return max(p & 0xFFFFu, q & 0xFFFFu) | (max(p >> 16, q >> 16) << 16);
+  };
+  return pmax(pmax(a, b), pmax(c, d));
+}
+
 // Loads the 2 x 16 bf16 of (pair tp, block b) of a tile; returns block maxima of
 // |x| as bf16 bit patterns packed (token 2tp in the low half).
 __device__ __forceinline__ uint32_t load_item(const QuantArgs &a, const TileInfo &t, int tp,
                                               int b, uint32_t (&x)[16]) {
   const int tin = t.ti * a.tile_tokens + 2 * tp;
   const int tok = t.f * a.tokens_per_frame + tin;
-  const uint16_t *src =
-      a.t[t.tensor].src + (int64_t(t.h) * a.T + tok) * a.D + b * 16;
-  uint32_t m0 = 0, m1 = 0;
+  const uint16_t *src = a.t[t.tensor].src + (int64_t(t.h) * a.T + tok) * a.D + b * 16;
 #pragma unroll
   for (int j = 0; j < 16; ++j) x[j] = 0;
+  uint4 u0 = make_uint4(0, 0, 0, 0), u1 = u0, u2 = u0, u3 = u0;
   if (tin < a.tokens_per_frame) {
     const uint4 *p = reinterpret_cast<const uint4 *>(src);
-    const uint4 u0 = p[0], u1 = p[1];
-    x[0] = u0.x; x[1] = u0.y; x[2] = u0.z; x[3] = u0.w;
-    x[4] = u1.x; x[5] = u1.y; x[6] = u1.z; x[7] = u1.w;
+    u0 = p[0];
+    u1 = p[1];
   }
   if (tin + 1 < a.tokens_per_frame) {
     const uint4 *p = reinterpret_cast<const uint4 *>(src + a.D);
-    const uint4 u0 = p[0], u1 = p[1];
-    x[8] = u0.x; x[9] = u0.y; x[10] = u0.z; x[11] = u0.w;
-    x[12] = u1.x; x[13] = u1.y; x[14] = u1.z; x[15] = u1.w;
+    u2 = p[0];
+    u3 = p[1];
   }
-#pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const uint32_t w = x[j] & 0x7FFF7FFFu;
-    m0 = max(m0, max(w & 0xFFFFu, w >> 16));
-    const uint32_t w1 = x[8 + j] & 0x7FFF7FFFu;
-    m1 = max(m1, max(w1 & 0xFFFFu, w1 >> 16));
-  }
-  return m0 | (m1 << 16);
+  x[0] = u0.x; x[1] = u0.y; x[2] = u0.z; x[3] = u0.w;
+  x[4] = u1.x; x[5] = u1.y; x[6] = u1.z; x[7] = u1.w;
+  x[8] = u2.x; x[9] = u2.y; x[10] = u2.z; x[11] = u2.w;
+  x[12] = u3.x; x[13] = u3.y; x[14] = u3.z; x[15] = u3.w;
+  const uint32_t m01 = vmax4(u0), m23 = vmax4(u2);
+  const uint32_t mA = max(vmax4(u1) & 0xFFFFu, m01 & 0xFFFFu);
+  const uint32_t mB = max(vmax4(u1) >> 16, m01 >> 16);
+  const uint32_t mC = max(vmax4(u3) & 0xFFFFu, m23 & 0xFFFFu);
+  const uint32_t mD = max(vmax4(u3) >> 16, m23 >> 16);
+  return max(mA, mB) | (max(mC, mD) << 16);
 }
 
-// Encodes the 16 elements of one token given the block maximum (bf16 bits) and
-// the tensor scale.  Returns the scale byte; codes go to c[0] (elements 0-7) and
-// c[1] (8-15), element e in nibble e % 8.
-__device__ __forceinline__ uint32_t encode_block(const uint32_t *x8, uint32_t bmax_bits,
-                                                 float st, uint32_t (&c)[2]) {
-  uint32_t sc = 0;
-  float eff = 0.0f;
-  if (st > 0.0f) {
-    const float bs = (bf16_bits_to_float(bmax_bits) / 6.0f) / st;
-    sc = e4m3_rne_sat(bs);
-    eff = e4m3_value(sc) * st;
-  }
-  c[0] = c[1] = 0;
-#pragma unroll
-  for (int e = 0; e < 16; ++e) {
-    const uint32_t w = x8[e >> 1];
-    const uint32_t hb = (e & 1) ? (w >> 16) : (w & 0xFFFFu);
-    uint32_t mag = 0;
-    if (eff > 0.0f) mag = e2m1_rne_sat(bf16_bits_to_float(hb & 0x7FFFu) / eff);
-    const uint32_t code = mag | ((hb >> 12) & 8u);
-    c[e >> 3] |= code << (4 * (e & 7));
-  }
-  return sc;
+// Per-tensor constants of the encoder.
+struct TensorConsts {
+  float st;       // s_t
+  float k;        // ~ 1 / (6 s_t), for the block-scale bracket
+  bool fast;      // s_t is a normal number well inside range: use the brackets
+};
+
+__device__ __forceinline__ TensorConsts tensor_consts(float st) {
+  TensorConsts c;
+  c.st = st;
+  c.fast = st >= 0x1p-120f && st <= 0x1p100f;
+  c.k = c.fast ? __builtin_amdgcn_rcpf(st) * (1.0f / 6.0f) : 0.0f;
+  return c;
 }
+
+// Block scale byte and the per-element multipliers of one 16-element block.
+struct BlockConsts {
+  uint32_t sc;    // E4M3 byte
+  float eff;      // E4M3(bs) * s_t
+  float rhi, rlo; // bracket multipliers for x / eff; 0 when eff == 0
+  bool exact;     // eff too small for the reciprocal bracket: divide every element
+};
+
+__device__ __forceinline__ BlockConsts block_consts(uint32_t bmax_bits, const TensorConsts &tc) {
+  BlockConsts bc;
+  const float amax = bf16_bits_to_float(bmax_bits);
+  uint32_t sc = 0;
+  if (tc.st > 0.0f) {
+    bool done = false;
+    if (tc.fast) {
+      const float bs = amax * tc.k;
+      const float lo = fminf(bs * (1.0f - 0x1p-19f), 448.0f);
+      const float hi = fminf(bs * (1.0f + 0x1p-19f), 448.0f);
+      short2_ p = {0, 0};
+      p = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(p, lo, hi, 1.0f, false);
+      const uint32_t w = uint32_t(uint16_t(p[0]));
+      if ((w & 0xFFu) == (w >> 8)) {
+        sc = w & 0xFFu;
+        done = true;
+      }
+    }
+    if (!done) sc = e4m3_rne_sat((amax / 6.0f) / tc.st);
+  }
+  bc.sc = sc;
+  bc.eff = __builtin_amdgcn_cvt_f32_fp8(sc, 0) * tc.st;
+  bc.exact = bc.eff > 0.0f && (bc.eff < 0x1p-120f || bc.eff > 0x1p110f);
+  const float r = (bc.eff > 0.0f && !bc.exact) ? __builtin_amdgcn_rcpf(bc.eff) : 0.0f;
+  bc.rhi = r * (1.0f + 0x1p-20f);
+  bc.rlo = r * (1.0f - 0x1p-20f);
+  return bc;
+}
+
+template <int SEL>
+__device__ __forceinline__ uint32_t cvt_fp4(uint32_t old, float a, float b) {
+  return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(old, a, b, 1.0f, SEL);
+}
+
+// Codes of 4 element pairs (xa[i], xb[i]) -> 4 bytes, pair i in byte i (a in the
+// low nibble).  ra/rb: the pair members' block multipliers.
+__device__ __forceinline__ uint32_t encode4(const float (&xa)[4], const float (&xb)[4],
+                                            const BlockConsts &ba, const BlockConsts &bb) {
+  uint32_t hi = 0, lo = 0;
+  hi = cvt_fp4<0>(hi, xa[0] * ba.rhi, xb[0] * bb.rhi);
+  lo = cvt_fp4<0>(lo, xa[0] * ba.rlo, xb[0] * bb.rlo);
+  hi = cvt_fp4<1>(hi, xa[1] * ba.rhi, xb[1] * bb.rhi);
+  lo = cvt_fp4<1>(lo, xa[1] * ba.rlo, xb[1] * bb.rlo);
+  hi = cvt_fp4<2>(hi, xa[2] * ba.rhi, xb[2] * bb.rhi);
+  lo = cvt_fp4<2>(lo, xa[2] * ba.rlo, xb[2] * bb.rlo);
+  hi = cvt_fp4<3>(hi, xa[3] * ba.rhi, xb[3] * bb.rhi);
+  lo = cvt_fp4<3>(lo, xa[3] * ba.rlo, xb[3] * bb.rlo);
+  if (hi != lo || ba.exact || bb.exact) {
+    // exact path: correctly rounded quotient, then the (exact) hardware rounding
+    // (an all-zero block, eff == 0, keeps only the signs; quotients are clamped far
+    // above 6 so that the convert never sees an infinity)
+    const float ea = ba.eff > 0.0f ? ba.eff : 1.0f, eb = bb.eff > 0.0f ? bb.eff : 1.0f;
+    const float za = ba.eff > 0.0f ? 1.0f : 0.0f, zb = bb.eff > 0.0f ? 1.0f : 0.0f;
+    auto q = [](float x, float e, float z) { return fminf(fmaxf(x / e, -1e30f), 1e30f) * z; };
+    hi = 0;
+    hi = cvt_fp4<0>(hi, q(xa[0], ea, za), q(xb[0], eb, zb));
+    hi = cvt_fp4<1>(hi, q(xa[1], ea, za), q(xb[1], eb, zb));
+    hi = cvt_fp4<2>(hi, q(xa[2], ea, za), q(xb[2], eb, zb));
+    hi = cvt_fp4<3>(hi, q(xa[3], ea, za), q(xb[3], eb, zb));
+  }
+  return hi;
+}
+
+__device__ __forceinline__ float lo_f(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float hi_f(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
 
 __device__ __forceinline__ void encode_store_item(const QuantArgs &a, const TileInfo &t, int tp,
-                                                  int b, const uint32_t (&x)[16],
-                                                  uint32_t bmax, float st, uint8_t *s_tr,
-                                                  int TP) {
+                                                  int b, const uint32_t (&x)[16], uint32_t bmax,
+                                                  const TensorConsts &tc, uint8_t *s_tr, int TP) {
   const QuantTensor &qt = a.t[t.tensor];
   const int nb = a.D >> 4;
   const int tin = t.ti * a.tile_tokens + 2 * tp;
   const bool v0 = tin < a.tokens_per_frame, v1 = tin + 1 < a.tokens_per_frame;
   const int64_t dtok = int64_t(a.frame_slot[t.f]) * a.tokens_per_frame + tin;
-  uint32_t c0[2], c1[2];
-  const uint32_t s0 = encode_block(x, bmax & 0xFFFFu, st, c0);
-  const uint32_t s1 = encode_block(x + 8, bmax >> 16, st, c1);
+  const BlockConsts b0 = block_consts(bmax & 0xFFFFu, tc);
+  const BlockConsts b1 = block_consts(bmax >> 16, tc);
   if (!qt.transposed) {
+    // token rows: pairs of consecutive elements of the same token
+    uint32_t c[4];
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {   // g: token (g >> 1), 8-element half (g & 1)
+      const uint32_t *w = x + 4 * g;
+      const float xa[4] = {lo_f(w[0]), lo_f(w[1]), lo_f(w[2]), lo_f(w[3])};
+      const float xb[4] = {hi_f(w[0]), hi_f(w[1]), hi_f(w[2]), hi_f(w[3])};
+      const BlockConsts &bc = (g < 2) ? b0 : b1;
+      c[g] = encode4(xa, xb, bc, bc);
+    }
     if (v0) {
       *reinterpret_cast<uint2 *>(qt.codes + (int64_t(t.h) * a.rows + dtok) * (a.D / 2) + b * 8) =
-          make_uint2(c0[0], c0[1]);
-      qt.scales[(int64_t(t.h) * a.rows + dtok) * nb + b] = uint8_t(s0);
+          make_uint2(c[0], c[1]);
+      qt.scales[(int64_t(t.h) * a.rows + dtok) * nb + b] = uint8_t(b0.sc);
     }
     if (v1) {
       *reinterpret_cast<uint2 *>(qt.codes + (int64_t(t.h) * a.rows + dtok + 1) * (a.D / 2) +
-                                 b * 8) = make_uint2(c1[0], c1[1]);
-      qt.scales[(int64_t(t.h) * a.rows + dtok + 1) * nb + b] = uint8_t(s1);
+                                 b * 8) = make_uint2(c[2], c[3]);
+      qt.scales[(int64_t(t.h) * a.rows + dtok + 1) * nb + b] = uint8_t(b1.sc);
     }
   } else {
-    // token pair -> one byte per d; staged in LDS as [d][pair]
+    // transposed: one byte per d holds (token 2tp, token 2tp+1)
 #pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      const uint32_t lo = (c0[e >> 3] >> (4 * (e & 7))) & 0xFu;
-      const uint32_t hi = (c1[e >> 3] >> (4 * (e & 7))) & 0xFu;
-      s_tr[(b * 16 + e) * TP + tp] = uint8_t(lo | (hi << 4));
+    for (int g = 0; g < 4; ++g) {   // d = 4g .. 4g+3 within the block
+      const uint32_t w0 = x[2 * g], w1 = x[2 * g + 1], u0 = x[8 + 2 * g], u1 = x[8 + 2 * g + 1];
+      const float xa[4] = {lo_f(w0), hi_f(w0), lo_f(w1), hi_f(w1)};
+      const float xb[4] = {lo_f(u0), hi_f(u0), lo_f(u1), hi_f(u1)};
+      const uint32_t c = encode4(xa, xb, b0, b1);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) s_tr[(b * 16 + 4 * g + i) * TP + tp] = uint8_t(c >> (8 * i));
     }
     if (v0) {
       *reinterpret_cast<uint16_t *>(qt.scales + (int64_t(t.h) * nb + b) * a.rows + dtok) =
-          uint16_t(s0 | (s1 << 8));
+          uint16_t(b0.sc | (b1.sc << 8));
     }
   }
 }
@@ -162,146 +266,77 @@ __device__ __forceinline__ void store_transposed_tile(const QuantArgs &a, const 
     if (col + 4 * j < nbytes) dst[j] = src[j];
 }
 
-__device__ __forceinline__ void block_reduce_max2(uint32_t &m0, uint32_t &m1, uint32_t *s_red) {
-  m0 = wave_max_u32(m0);
-  m1 = wave_max_u32(m1);
-  const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
-  if (l == 0) {
-    s_red[w] = m0;
-    s_red[8 + w] = m1;
-  }
-  __syncthreads();
-  m0 = 0;
-  m1 = 0;
-#pragma unroll
-  for (int i = 0; i < kQuantThreads / 64; ++i) {
-    m0 = max(m0, s_red[i]);
-    m1 = max(m1, s_red[8 + i]);
-  }
-  __syncthreads();
-}
-
-__device__ __forceinline__ uint32_t atomic_load_relaxed(const uint32_t *p) {
-  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
-// Reads the per-workgroup partial maxima of an amax pass of `g` workgroups and
-// returns both tensors' scales s_t = amax / 2688 via LDS.
+// Reduces the partial maxima of an amax pass of `g` workgroups; s_st[t] = amax_t / 2688.
 __device__ __forceinline__ void read_tensor_scales(const QuantArgs &a, int g, uint32_t *s_red,
                                                    float *s_st) {
   uint32_t m0 = 0, m1 = 0;
   for (int j = threadIdx.x; j < g; j += kQuantThreads) {
-    m0 = max(m0, atomic_load_relaxed(&a.ws->partial[0][j]));
-    m1 = max(m1, atomic_load_relaxed(&a.ws->partial[1][j]));
+    m0 = max(m0, a.ws->partial[0][j]);
+    m1 = max(m1, a.ws->partial[1][j]);
   }
-  block_reduce_max2(m0, m1, s_red);
+  m0 = wave_max_u32(m0);
+  m1 = wave_max_u32(m1);
+  const int w = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) == 0) {
+    s_red[w] = m0;
+    s_red[8 + w] = m1;
+  }
+  __syncthreads();
   if (threadIdx.x == 0) {
-    s_st[0] = __uint_as_float(m0) / 2688.0f;
-    s_st[1] = __uint_as_float(m1) / 2688.0f;
+    uint32_t r0 = 0, r1 = 0;
+    for (int i = 0; i < kQuantThreads / 64; ++i) {
+      r0 = max(r0, s_red[i]);
+      r1 = max(r1, s_red[8 + i]);
+    }
+    s_st[0] = __uint_as_float(r0) / 2688.0f;
+    s_st[1] = __uint_as_float(r1) / 2688.0f;
   }
   __syncthreads();
 }
 
 }  // namespace
 
-// Single pass: registers hold every tile of the workgroup across the grid barrier.
-template <int ITEMS>
-__global__ __launch_bounds__(kQuantThreads) void quantize_coop_kernel(QuantArgs a) {
-  __shared__ uint32_t s_red[16];
-  __shared__ float s_st[2];
-  __shared__ uint8_t s_tr[4096];
-  const int tid = threadIdx.x;
-  const int nb = a.D >> 4;
-  const int TP = kQuantThreads / nb;
-  const bool act = tid < TP * nb;
-  const int b = tid % nb, tp = tid / nb;
-
-  uint32_t x[ITEMS][16];
-  uint32_t bmax[ITEMS];
-  uint32_t tm[2] = {0u, 0u};
+// Pass 1: per-workgroup maxima of |x| over the flat K and V tensors (no atomics:
+// each workgroup owns one slot of the partials array).
+__global__ __launch_bounds__(kAmaxThreads) void quantize_amax_kernel(QuantArgs a) {
+  __shared__ uint32_t s_red[2][kAmaxThreads / 64];
+  const int64_t n16 = int64_t(a.H) * a.T * a.D / 8;   // uint4 vectors per tensor
+  const int64_t stride = int64_t(gridDim.x) * kAmaxThreads;
+  uint32_t m[2] = {0u, 0u};
 #pragma unroll
-  for (int i = 0; i < ITEMS; ++i) {
-    const int tile = blockIdx.x + i * gridDim.x;
-    bmax[i] = 0;
-    if (tile < a.total_tiles && act) {
-      const TileInfo t = decode_tile(a, tile);
-      bmax[i] = load_item(a, t, tp, b, x[i]);
-      const uint32_t m = max(bmax[i] & 0xFFFFu, bmax[i] >> 16);
-      if (t.tensor == 0) tm[0] = max(tm[0], m);
-      else tm[1] = max(tm[1], m);
+  for (int t = 0; t < 2; ++t) {
+    if (t >= a.n_tensors) break;
+    const uint4 *p = reinterpret_cast<const uint4 *>(a.t[t].src);
+    uint32_t acc = 0;
+    int64_t i = int64_t(blockIdx.x) * kAmaxThreads + threadIdx.x;
+    for (; i + 3 * stride < n16; i += 4 * stride) {
+      const uint4 u0 = p[i], u1 = p[i + stride], u2 = p[i + 2 * stride], u3 = p[i + 3 * stride];
+      const uint32_t q0 = vmax4(u0), q1 = vmax4(u1), q2 = vmax4(u2), q3 = vmax4(u3);
+      acc = max(acc, max(max(q0 & 0xFFFFu, q0 >> 16), max(q1 & 0xFFFFu, q1 >> 16)));
+      acc = max(acc, max(max(q2 & 0xFFFFu, q2 >> 16), max(q3 & 0xFFFFu, q3 >> 16)));
     }
+    for (; i < n16; i += stride) {
+      const uint32_t q = vmax4(p[i]);
+      acc = max(acc, max(q & 0xFFFFu, q >> 16));
+    }
+    m[t] = acc << 16;   // fp32 bit pattern of the bf16 maximum
   }
-  // workgroup maxima (as fp32 bit patterns) -> partials -> grid barrier
-  uint32_t m0 = tm[0] << 16, m1 = tm[1] << 16;
-  block_reduce_max2(m0, m1, s_red);
-  if (tid == 0) {
-    a.ws->partial[0][blockIdx.x] = m0;
-    a.ws->partial[1][blockIdx.x] = m1;
-    const uint32_t gen = __hip_atomic_load(&a.ws->gen, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    const uint32_t arrived = __hip_atomic_fetch_add(&a.ws->count, 1u, __ATOMIC_ACQ_REL,
-                                                    __HIP_MEMORY_SCOPE_AGENT);
-    if (arrived == gridDim.x - 1) {
-      __hip_atomic_store(&a.ws->count, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      __hip_atomic_store(&a.ws->gen, gen + 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
-    } else {
-      // all workgroups are co-resident (cooperative launch); the bound only keeps a
-      // corrupted workspace from hanging the device
-      uint32_t spins = 0;
-      while (__hip_atomic_load(&a.ws->gen, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT) == gen) {
-        __builtin_amdgcn_s_sleep(1);
-        if (++spins > (1u << 26)) {
-          __hip_atomic_store(&a.ws->timeout, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-          break;
-        }
-      }
-    }
+  m[0] = wave_max_u32(m[0]);
+  m[1] = wave_max_u32(m[1]);
+  const int w = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) == 0) {
+    s_red[0][w] = m[0];
+    s_red[1][w] = m[1];
   }
   __syncthreads();
-  read_tensor_scales(a, gridDim.x, s_red, s_st);
-  if (blockIdx.x == 0 && tid < a.n_tensors) *a.t[tid].tensor_scale = s_st[tid];
-
-#pragma unroll
-  for (int i = 0; i < ITEMS; ++i) {
-    const int tile = blockIdx.x + i * gridDim.x;
-    if (tile >= a.total_tiles) break;   // uniform across the workgroup
-    const TileInfo t = decode_tile(a, tile);
-    const bool tr = a.t[t.tensor].transposed != 0;
-    if (act) encode_store_item(a, t, tp, b, x[i], bmax[i], s_st[t.tensor], s_tr, TP);
-    if (tr) {
-      __syncthreads();
-      store_transposed_tile(a, t, s_tr, TP);
-      __syncthreads();
-    }
+  if (threadIdx.x < 2) {
+    uint32_t r = 0;
+    for (int i = 0; i < kAmaxThreads / 64; ++i) r = max(r, s_red[threadIdx.x][i]);
+    a.ws->partial[threadIdx.x][blockIdx.x] = r;
   }
 }
 
-// Two-pass fallback, pass 1: per-workgroup maxima over a grid-stride set of tiles.
-__global__ __launch_bounds__(kQuantThreads) void quantize_amax_kernel(QuantArgs a) {
-  __shared__ uint32_t s_red[16];
-  const int tid = threadIdx.x;
-  const int nb = a.D >> 4;
-  const int TP = kQuantThreads / nb;
-  const bool act = tid < TP * nb;
-  const int b = tid % nb, tp = tid / nb;
-  uint32_t tm[2] = {0u, 0u};
-  for (int tile = blockIdx.x; tile < a.total_tiles; tile += gridDim.x) {
-    if (!act) continue;
-    const TileInfo t = decode_tile(a, tile);
-    uint32_t x[16];
-    const uint32_t bm = load_item(a, t, tp, b, x);
-    const uint32_t m = max(bm & 0xFFFFu, bm >> 16);
-    if (t.tensor == 0) tm[0] = max(tm[0], m);
-    else tm[1] = max(tm[1], m);
-  }
-  uint32_t m0 = tm[0] << 16, m1 = tm[1] << 16;
-  block_reduce_max2(m0, m1, s_red);
-  if (tid == 0) {
-    a.ws->partial[0][blockIdx.x] = m0;
-    a.ws->partial[1][blockIdx.x] = m1;
-  }
-}
-
-// Two-pass fallback, pass 2: re-reads the input and encodes.
+// Pass 2: tensor scales from the partials, then every tile is re-read and encoded.
 __global__ __launch_bounds__(kQuantThreads) void quantize_encode_kernel(QuantArgs a, int g_amax) {
   __shared__ uint32_t s_red[16];
   __shared__ float s_st[2];
@@ -313,13 +348,15 @@ __global__ __launch_bounds__(kQuantThreads) void quantize_encode_kernel(QuantArg
   const int b = tid % nb, tp = tid / nb;
   read_tensor_scales(a, g_amax, s_red, s_st);
   if (blockIdx.x == 0 && tid < a.n_tensors) *a.t[tid].tensor_scale = s_st[tid];
+  const TensorConsts tc0 = tensor_consts(s_st[0]);
+  const TensorConsts tc1 = tensor_consts(s_st[1]);
   for (int tile = blockIdx.x; tile < a.total_tiles; tile += gridDim.x) {
     const TileInfo t = decode_tile(a, tile);
     const bool tr = a.t[t.tensor].transposed != 0;
     if (act) {
       uint32_t x[16];
       const uint32_t bm = load_item(a, t, tp, b, x);
-      encode_store_item(a, t, tp, b, x, bm, s_st[t.tensor], s_tr, TP);
+      encode_store_item(a, t, tp, b, x, bm, t.tensor ? tc1 : tc0, s_tr, TP);
     }
     if (tr) {
       __syncthreads();
@@ -330,45 +367,21 @@ __global__ __launch_bounds__(kQuantThreads) void quantize_encode_kernel(QuantArg
 }
 
 namespace {
-
 constexpr int kMaxDevices = 64;
-int g_max_grid[kMaxDevices][4];   // per device, per ITEMS in {1,2,4,8}; 0 = unknown
 int g_cu_count[kMaxDevices];
 
-int coop_max_grid(int dev, int idx, const void *fn) {
-  if (dev < 0 || dev >= kMaxDevices) return 0;
-  if (g_max_grid[dev][idx] == 0) {
-    int per_cu = 0, cus = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, kQuantThreads, 0) != hipSuccess)
-      return 0;
-    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
-      return 0;
+int cu_count(int dev) {
+  if (dev < 0 || dev >= kMaxDevices) return 256;
+  if (g_cu_count[dev] == 0) {
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        cus <= 0)
+      return 256;
     g_cu_count[dev] = cus;
-    int g = per_cu * cus;
-    if (g > kMaxQuantGrid) g = kMaxQuantGrid;
-    g_max_grid[dev][idx] = g;
   }
-  return g_max_grid[dev][idx];
+  return g_cu_count[dev];
 }
-
-const void *coop_fn(int idx) {
-  switch (idx) {
-    case 0: return reinterpret_cast<const void *>(&quantize_coop_kernel<1>);
-    case 1: return reinterpret_cast<const void *>(&quantize_coop_kernel<2>);
-    case 2: return reinterpret_cast<const void *>(&quantize_coop_kernel<4>);
-    default: return reinterpret_cast<const void *>(&quantize_coop_kernel<8>);
-  }
-}
-
 }  // namespace
-
-int quantize_max_grid(int items, int *grid) {
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess) return NVFP4KV_EHIP;
-  const int idx = items <= 1 ? 0 : items <= 2 ? 1 : items <= 4 ? 2 : 3;
-  *grid = coop_max_grid(dev, idx, coop_fn(idx));
-  return *grid > 0 ? NVFP4KV_OK : NVFP4KV_EHIP;
-}
 
 int launch_quantize(const QuantArgs &in, void *stream) {
   QuantArgs a = in;
@@ -382,28 +395,19 @@ int launch_quantize(const QuantArgs &in, void *stream) {
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return NVFP4KV_EHIP;
-
-  // smallest register depth whose co-resident grid covers every tile
-  for (int idx = 0; idx < 4; ++idx) {
-    const int items = 1 << idx;
-    const int gmax = coop_max_grid(dev, idx, coop_fn(idx));
-    if (gmax <= 0) return NVFP4KV_EHIP;
-    const int64_t g = (total + items - 1) / items;
-    if (g <= gmax) {
-      a.items = items;
-      void *args[] = {&a};
-      const hipError_t e = hipLaunchCooperativeKernel(coop_fn(idx), dim3(unsigned(g)),
-                                                      dim3(kQuantThreads), args, 0, s);
-      return e == hipSuccess ? NVFP4KV_OK : NVFP4KV_EHIP;
-    }
-  }
-  // too large for one register-resident pass: amax pass + encode pass
-  int cus = g_cu_count[dev] > 0 ? g_cu_count[dev] : 256;
-  int g = cus * 4;
-  if (g > kMaxQuantGrid) g = kMaxQuantGrid;
-  hipLaunchKernelGGL(quantize_amax_kernel, dim3(g), dim3(kQuantThreads), 0, s, a);
+  const int cus = cu_count(dev);
+  // pass 1: one 1024-thread workgroup per CU (fewer for small inputs)
+  const int64_t vecs = int64_t(a.H) * a.T * a.D / 8;
+  int64_t g1 = (vecs + kAmaxThreads * 4 - 1) / (kAmaxThreads * 4);
+  if (g1 > cus) g1 = cus;
+  if (g1 < 1) g1 = 1;
+  hipLaunchKernelGGL(quantize_amax_kernel, dim3(unsigned(g1)), dim3(kAmaxThreads), 0, s, a);
   if (hipGetLastError() != hipSuccess) return NVFP4KV_EHIP;
-  hipLaunchKernelGGL(quantize_encode_kernel, dim3(g), dim3(kQuantThreads), 0, s, a, g);
+  // pass 2: enough 256-thread workgroups to cover every tile or fill the GPU 8 deep
+  int64_t g2 = total;
+  if (g2 > int64_t(cus) * 8) g2 = int64_t(cus) * 8;
+  hipLaunchKernelGGL(quantize_encode_kernel, dim3(unsigned(g2)), dim3(kQuantThreads), 0, s, a,
+                     int(g1));
   return NVFP4KV_HIP_OK(hipGetLastError());
 }
 
