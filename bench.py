@@ -48,17 +48,25 @@ def parse():
     p.add_argument("--warmup", type=int, default=4)
     p.add_argument("--reps", type=int, default=30, help="launches per kernel microbenchmark")
     p.add_argument("--no-cpu-baseline", action="store_true")
-    p.add_argument("--cpu-rows", type=int, default=768, help="query rows per head in the CPU sample")
+    p.add_argument("--cpu-calls", type=int, default=2,
+                   help="full 1.3B-shaped attention calls the CPU oracle runs as its baseline sample")
     p.add_argument("--skip-configs", action="store_true", help="rollout + roofline legs only")
+    p.add_argument("--only", choices=["attention", "quantize", "copy"],
+                   help="run one kernel leg only (for profiler runs): the attention kernel on the "
+                        "1.3B-shaped cache, the append of the quantize-only workload, or a plain "
+                        "256 MiB device copy (reference for the HBM byte counters)")
     return p.parse_args()
 
 
-def timed(fn, reps, torch):
+def timed(fn, reps, torch, host_us_per_call=60.0):
     """Mean ms per call of fn() over `reps` back-to-back calls, HIP events on
-    the current stream."""
+    the current stream.  A device-side sleep is queued first so that the host
+    has enqueued every call before the first one starts: the events then time
+    back-to-back GPU execution, not the Python call rate."""
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     fn()
     torch.cuda.synchronize()
+    torch.cuda._sleep(int(2.0e3 * host_us_per_call * reps) + 1_000_000)   # ~cycles at >= 2 GHz
     e0.record()
     for _ in range(reps):
         fn()
@@ -176,10 +184,10 @@ def attention_config(name, args, torch, ops, W, device):
 
 
 def cpu_baseline(args, W):
-    """The oracle, untuned, on a bounded sample: chunk attention of the
-    1.3B-shaped workload (same shape as the steady-state rollout step) for
-    `cpu_rows` query rows of every head over all 23400 keys; plus the oracle
-    codec on one K tensor [12, 4680, 128]."""
+    """The oracle, untuned, on a bounded sample: `cpu_calls` full chunk-attention
+    calls of the 1.3B-shaped workload (same shape as the steady-state rollout
+    step: 12 heads x 4680 queries x 23400 keys), on consecutive query chunks over
+    the same cache; plus the oracle codec on one K tensor [12, 4680, 128]."""
     import numpy as np
     from oracle import CacheModel, chunk_attention_ref, quantize_ref
     wl = W.WORKLOADS["wan13b"]
@@ -187,13 +195,13 @@ def cpu_baseline(args, W):
     for c in range(wl.n_cache_chunks):
         model.append(*W.clean_chunk(wl, c))
     ck, cv = model.dequantized_kv()
-    q, ko, vo = W.noisy_chunk(wl, wl.n_cache_chunks)
-    rows = np.arange(min(args.cpu_rows, wl.n_q))
+    calls = [W.noisy_chunk(wl, wl.n_cache_chunks, step=s) for s in range(max(1, args.cpu_calls))]
     t0 = time.perf_counter()
-    chunk_attention_ref(q, ko, vo, ck, cv, wl.softmax_scale, rows=rows)
+    for q, ko, vo in calls:
+        chunk_attention_ref(q, ko, vo, ck, cv, wl.softmax_scale)
     dt = time.perf_counter() - t0
     n_k = ck.shape[1] + wl.n_q
-    flops = W.attention_flops(wl.n_heads, len(rows), n_k, wl.head_dim)
+    flops = len(calls) * W.attention_flops(wl.n_heads, wl.n_q, n_k, wl.head_dim)
     k, _ = W.clean_chunk(W.WORKLOADS["quantize"], 0)
     t1 = time.perf_counter()
     quantize_ref(k)
@@ -212,8 +220,9 @@ def cpu_baseline(args, W):
     except OSError:
         pass
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
-            "sample": f"float64 chunk attention, 1.3B-shaped cache (12 heads x {len(rows)} query rows x "
-                      f"{n_k} keys x D128), {dt:.1f} s; numpy BLAS threads={cores}; {cpu_model}",
+            "sample": f"{len(calls)} float64 chunk-attention calls of the 1.3B-shaped workload (12 heads x "
+                      f"{wl.n_q} queries x {n_k} keys x D128), {dt:.1f} s; numpy BLAS threads={cores}; "
+                      f"{cpu_model}",
             "seconds": dt, "host_cpus": os.cpu_count(),
             "quantize_GB_per_s": W.quantize_bytes(k.size) / dq / 1e9, "quantize_seconds": dq}
 
@@ -232,6 +241,21 @@ def main():
     device = torch.device("cuda:0")
     ops.lib()
     log(f"device: {torch.cuda.get_device_name(0)}")
+    if args.only == "attention":
+        r = attention_config("wan13b", args, torch, ops, W, device)
+        print(json.dumps({"leg": "attention", "workload": "wan13b", **r}), flush=True)
+        return
+    if args.only == "copy":
+        src = torch.ones(64 << 20, dtype=torch.float32, device=device)   # 256 MiB
+        dst = torch.empty_like(src)
+        ms = timed(lambda: dst.copy_(src), 5, torch)
+        print(json.dumps({"leg": "copy", "bytes_read": src.numel() * 4, "bytes_written": dst.numel() * 4,
+                          "ms": ms, "GB_per_s": 2 * src.numel() * 4 / (ms * 1e-3) / 1e9}), flush=True)
+        return
+    if args.only == "quantize":
+        qz = quantize_leg(args, torch, ops, W, device)
+        print(json.dumps({"leg": "quantize", "workload": "quantize", **qz}), flush=True)
+        return
 
     r = rollout(args, torch, ops, W, device)
     log(f"rollout: {r['ms_per_step']:.3f} ms/step, {r['tflops']:.1f} TFLOP/s, "

@@ -17,25 +17,30 @@
 //      chunk, 28.8 MB for the 1.3B shape, is still in the 256 MB Infinity Cache)
 //      and writes codes and scales.
 //
-// Exact encoding without a division per element.  The gfx950 converts
+// Exact encoding without an IEEE division per element.  The gfx950 converts
 // v_cvt_scalef32_pk_fp4_f32 / _fp8_f32 (scale 1.0) round to nearest-even and
 // saturate exactly like the recipe for every finite fp32 input (fp8 needs a clamp
-// at 448, above which it returns NaN).  So the code of the correctly rounded
-// quotient q = RN(|x| / eff) is hw_fp4(q).  With r ~ 1/eff (v_rcp_f32, <= 1 ulp),
-// q_hi = x * r * (1 + 2^-20) and q_lo = x * r * (1 - 2^-20) bracket q (their error
-// is below 2^-22 relative); the E2M1 code is monotone in q, so when
-// hw_fp4(q_lo) == hw_fp4(q_hi) that is hw_fp4(q).  Otherwise -- q within ~2^-20 of a
-// rounding threshold, rare except for data built on the grid -- the element is
-// divided exactly.  The block scale uses the same bracket on (amax/6)/s_t with
-// hw_fp8, falling back to the two divisions.
+// at 448, above which it returns NaN), so the code is hw_fp4(RN(x / eff)).  The
+// quotient RN(x / b) is obtained from r = RN(1 / b) (one IEEE division per block)
+// by Markstein's method: q0 = RN(x r) is within 1.5 ulp of x / b; one correction
+// q1 = RN(q0 + (x - q0 b) r) makes it faithful; a second one, with the now exact
+// remainder, q2 = RN(q1 + (x - q1 b) r), is the correctly rounded quotient
+// (Markstein's theorem: y = RN(1/b) and a faithful q give RN(a/b) in one step).
+// Five fp32 operations and no branches per element; the block scale's two
+// divisions use the same scheme.  Quotients below 2^-126 fall out of the theorem's
+// range but are far below the first E2M1 threshold (0.25), so their code is exact
+// regardless; blocks whose eff leaves [2^-120, 2^110] divide each element with
+// IEEE division instead.
 //
-// Work unit: a tile of (256 / (D/16)) token pairs x all D/16 blocks of one head of
-// one frame; thread (pair p, block b) owns 2 tokens x 16 elements.  Tiles never
+// Work unit: a tile of 2 x (256 / (D/16)) token pairs x all D/16 blocks of one head
+// of one frame; thread (pair p, block b) owns token pairs p and p + 256/(D/16), i.e.
+// 4 tokens x 16 elements.  Tiles never
 // straddle a frame, so each tile lands in one cache slot.  K (and the standalone
 // codec) are written in the codec layout [h][token][D/2]; V in the cache is written
 // transposed, [h][d][token/2], through LDS, so that the attention kernel can read 8
-// consecutive keys of one d with one load.  For the transposed layout a byte holds
-// tokens (2p, 2p+1) of one d, and the fp4 convert is fed exactly that pair.
+// consecutive keys of one d with one load; a tile then writes 64 contiguous bytes
+// per d row.  For the transposed layout a byte holds tokens (2p, 2p+1) of one d,
+// and the fp4 convert is fed exactly that pair.
 
 #include "device_common.h"
 
@@ -74,11 +79,10 @@ __device__ __forceinline__ uint32_t vmax4(uint4 u) {
   return pmax(pmax(a, b), pmax(c, d));
 }
 
-// Loads the 2 x 16 bf16 of (pair tp, block b) of a tile; returns block maxima of
-// |x| as bf16 bit patterns packed (token 2tp in the low half).
-__device__ __forceinline__ uint32_t load_item(const QuantArgs &a, const TileInfo &t, int tp,
+// Loads the 2 x 16 bf16 of tokens (tin, tin+1) of a tile's frame, block b; returns
+// block maxima of |x| as bf16 bit patterns packed (token tin in the low half).
+__device__ __forceinline__ uint32_t load_item(const QuantArgs &a, const TileInfo &t, int tin,
                                               int b, uint32_t (&x)[16]) {
-  const int tin = t.ti * a.tile_tokens + 2 * tp;
   const int tok = t.f * a.tokens_per_frame + tin;
   const uint16_t *src = a.t[t.tensor].src + (int64_t(t.h) * a.T + tok) * a.D + b * 16;
 #pragma unroll
@@ -106,27 +110,36 @@ __device__ __forceinline__ uint32_t load_item(const QuantArgs &a, const TileInfo
   return max(mA, mB) | (max(mC, mD) << 16);
 }
 
+// RN(x / b) from r = RN(1 / b): q0 = RN(x r), then two Markstein corrections.
+__device__ __forceinline__ float div_rn(float x, float b, float r) {
+  float q = x * r;
+  float e = __builtin_fmaf(-q, b, x);
+  q = __builtin_fmaf(e, r, q);
+  e = __builtin_fmaf(-q, b, x);
+  return __builtin_fmaf(e, r, q);
+}
+
 // Per-tensor constants of the encoder.
 struct TensorConsts {
   float st;       // s_t
-  float k;        // ~ 1 / (6 s_t), for the block-scale bracket
-  bool fast;      // s_t is a normal number well inside range: use the brackets
+  float rst;      // RN(1 / s_t)
+  bool fast;      // s_t well inside the normal range: Markstein quotients apply
 };
 
 __device__ __forceinline__ TensorConsts tensor_consts(float st) {
   TensorConsts c;
   c.st = st;
   c.fast = st >= 0x1p-120f && st <= 0x1p100f;
-  c.k = c.fast ? __builtin_amdgcn_rcpf(st) * (1.0f / 6.0f) : 0.0f;
+  c.rst = c.fast ? 1.0f / st : 0.0f;
   return c;
 }
 
-// Block scale byte and the per-element multipliers of one 16-element block.
+// Block scale byte and the per-element divisor of one 16-element block.
 struct BlockConsts {
   uint32_t sc;    // E4M3 byte
   float eff;      // E4M3(bs) * s_t
-  float rhi, rlo; // bracket multipliers for x / eff; 0 when eff == 0
-  bool exact;     // eff too small for the reciprocal bracket: divide every element
+  float r;        // RN(1 / eff); 0 when eff == 0 (codes keep only the signs)
+  bool exact;     // eff outside [2^-120, 2^110]: IEEE-divide every element
 };
 
 __device__ __forceinline__ BlockConsts block_consts(uint32_t bmax_bits, const TensorConsts &tc) {
@@ -134,27 +147,17 @@ __device__ __forceinline__ BlockConsts block_consts(uint32_t bmax_bits, const Te
   const float amax = bf16_bits_to_float(bmax_bits);
   uint32_t sc = 0;
   if (tc.st > 0.0f) {
-    bool done = false;
-    if (tc.fast) {
-      const float bs = amax * tc.k;
-      const float lo = fminf(bs * (1.0f - 0x1p-19f), 448.0f);
-      const float hi = fminf(bs * (1.0f + 0x1p-19f), 448.0f);
-      short2_ p = {0, 0};
-      p = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(p, lo, hi, 1.0f, false);
-      const uint32_t w = uint32_t(uint16_t(p[0]));
-      if ((w & 0xFFu) == (w >> 8)) {
-        sc = w & 0xFFu;
-        done = true;
-      }
-    }
-    if (!done) sc = e4m3_rne_sat((amax / 6.0f) / tc.st);
+    float bs;
+    if (tc.fast) bs = div_rn(div_rn(amax, 6.0f, 1.0f / 6.0f), tc.st, tc.rst);
+    else bs = (amax / 6.0f) / tc.st;
+    short2_ p = {0, 0};
+    p = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(p, fminf(bs, 448.0f), 0.0f, 1.0f, false);
+    sc = uint32_t(uint16_t(p[0])) & 0xFFu;
   }
   bc.sc = sc;
   bc.eff = __builtin_amdgcn_cvt_f32_fp8(sc, 0) * tc.st;
   bc.exact = bc.eff > 0.0f && (bc.eff < 0x1p-120f || bc.eff > 0x1p110f);
-  const float r = (bc.eff > 0.0f && !bc.exact) ? __builtin_amdgcn_rcpf(bc.eff) : 0.0f;
-  bc.rhi = r * (1.0f + 0x1p-20f);
-  bc.rlo = r * (1.0f - 0x1p-20f);
+  bc.r = (bc.eff > 0.0f && !bc.exact) ? 1.0f / bc.eff : 0.0f;
   return bc;
 }
 
@@ -163,44 +166,38 @@ __device__ __forceinline__ uint32_t cvt_fp4(uint32_t old, float a, float b) {
   return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(old, a, b, 1.0f, SEL);
 }
 
+// Correctly rounded signed quotient x / eff (0 with x's sign when eff == 0).  The
+// corrections of div_rn can turn a zero result into +0 (+0 + -0 = +0), so the sign
+// is re-applied from x: a nonzero quotient already carries it.
+__device__ __forceinline__ float quot(float x, const BlockConsts &bc) {
+  if (!bc.exact) return __builtin_copysignf(div_rn(x, bc.eff, bc.r), x);
+  return fminf(fmaxf(x / bc.eff, -1e30f), 1e30f);
+}
+
 // Codes of 4 element pairs (xa[i], xb[i]) -> 4 bytes, pair i in byte i (a in the
-// low nibble).  ra/rb: the pair members' block multipliers.
+// low nibble).
 __device__ __forceinline__ uint32_t encode4(const float (&xa)[4], const float (&xb)[4],
                                             const BlockConsts &ba, const BlockConsts &bb) {
-  uint32_t hi = 0, lo = 0;
-  hi = cvt_fp4<0>(hi, xa[0] * ba.rhi, xb[0] * bb.rhi);
-  lo = cvt_fp4<0>(lo, xa[0] * ba.rlo, xb[0] * bb.rlo);
-  hi = cvt_fp4<1>(hi, xa[1] * ba.rhi, xb[1] * bb.rhi);
-  lo = cvt_fp4<1>(lo, xa[1] * ba.rlo, xb[1] * bb.rlo);
-  hi = cvt_fp4<2>(hi, xa[2] * ba.rhi, xb[2] * bb.rhi);
-  lo = cvt_fp4<2>(lo, xa[2] * ba.rlo, xb[2] * bb.rlo);
-  hi = cvt_fp4<3>(hi, xa[3] * ba.rhi, xb[3] * bb.rhi);
-  lo = cvt_fp4<3>(lo, xa[3] * ba.rlo, xb[3] * bb.rlo);
-  if (hi != lo || ba.exact || bb.exact) {
-    // exact path: correctly rounded quotient, then the (exact) hardware rounding
-    // (an all-zero block, eff == 0, keeps only the signs; quotients are clamped far
-    // above 6 so that the convert never sees an infinity)
-    const float ea = ba.eff > 0.0f ? ba.eff : 1.0f, eb = bb.eff > 0.0f ? bb.eff : 1.0f;
-    const float za = ba.eff > 0.0f ? 1.0f : 0.0f, zb = bb.eff > 0.0f ? 1.0f : 0.0f;
-    auto q = [](float x, float e, float z) { return fminf(fmaxf(x / e, -1e30f), 1e30f) * z; };
-    hi = 0;
-    hi = cvt_fp4<0>(hi, q(xa[0], ea, za), q(xb[0], eb, zb));
-    hi = cvt_fp4<1>(hi, q(xa[1], ea, za), q(xb[1], eb, zb));
-    hi = cvt_fp4<2>(hi, q(xa[2], ea, za), q(xb[2], eb, zb));
-    hi = cvt_fp4<3>(hi, q(xa[3], ea, za), q(xb[3], eb, zb));
-  }
-  return hi;
+  uint32_t c = 0;
+  c = cvt_fp4<0>(c, quot(xa[0], ba), quot(xb[0], bb));
+  c = cvt_fp4<1>(c, quot(xa[1], ba), quot(xb[1], bb));
+  c = cvt_fp4<2>(c, quot(xa[2], ba), quot(xb[2], bb));
+  c = cvt_fp4<3>(c, quot(xa[3], ba), quot(xb[3], bb));
+  return c;
 }
 
 __device__ __forceinline__ float lo_f(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float hi_f(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
 
-__device__ __forceinline__ void encode_store_item(const QuantArgs &a, const TileInfo &t, int tp,
-                                                  int b, const uint32_t (&x)[16], uint32_t bmax,
-                                                  const TensorConsts &tc, uint8_t *s_tr, int TP) {
+// Encodes and stores one item: token pair p (tokens tin, tin+1 of frame t.f) x block b.
+// For the transposed layout the bytes go to s_tr[d][pair column `col`] (row stride
+// `pairs` bytes) and are written out per tile by store_transposed_tile.
+__device__ __forceinline__ void encode_store_item(const QuantArgs &a, const TileInfo &t, int tin,
+                                                  int col, int pairs, int b,
+                                                  const uint32_t (&x)[16], uint32_t bmax,
+                                                  const TensorConsts &tc, uint8_t *s_tr) {
   const QuantTensor &qt = a.t[t.tensor];
   const int nb = a.D >> 4;
-  const int tin = t.ti * a.tile_tokens + 2 * tp;
   const bool v0 = tin < a.tokens_per_frame, v1 = tin + 1 < a.tokens_per_frame;
   const int64_t dtok = int64_t(a.frame_slot[t.f]) * a.tokens_per_frame + tin;
   const BlockConsts b0 = block_consts(bmax & 0xFFFFu, tc);
@@ -227,7 +224,7 @@ __device__ __forceinline__ void encode_store_item(const QuantArgs &a, const Tile
       qt.scales[(int64_t(t.h) * a.rows + dtok + 1) * nb + b] = uint8_t(b1.sc);
     }
   } else {
-    // transposed: one byte per d holds (token 2tp, token 2tp+1)
+    // transposed: one byte per d holds (token tin, token tin+1)
 #pragma unroll
     for (int g = 0; g < 4; ++g) {   // d = 4g .. 4g+3 within the block
       const uint32_t w0 = x[2 * g], w1 = x[2 * g + 1], u0 = x[8 + 2 * g], u1 = x[8 + 2 * g + 1];
@@ -235,7 +232,7 @@ __device__ __forceinline__ void encode_store_item(const QuantArgs &a, const Tile
       const float xb[4] = {lo_f(u0), hi_f(u0), lo_f(u1), hi_f(u1)};
       const uint32_t c = encode4(xa, xb, b0, b1);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) s_tr[(b * 16 + 4 * g + i) * TP + tp] = uint8_t(c >> (8 * i));
+      for (int i = 0; i < 4; ++i) s_tr[(b * 16 + 4 * g + i) * pairs + col] = uint8_t(c >> (8 * i));
     }
     if (v0) {
       *reinterpret_cast<uint16_t *>(qt.scales + (int64_t(t.h) * nb + b) * a.rows + dtok) =
@@ -244,26 +241,27 @@ __device__ __forceinline__ void encode_store_item(const QuantArgs &a, const Tile
   }
 }
 
-// Writes one LDS-staged transposed tile ([D][TP] bytes) to V's [h][d][rows/2] plane.
+// Writes one LDS-staged transposed tile ([D][pairs] bytes, pairs = tile_tokens / 2)
+// to V's [h][d][rows/2] plane, 16 bytes per thread-step.
 __device__ __forceinline__ void store_transposed_tile(const QuantArgs &a, const TileInfo &t,
-                                                      const uint8_t *s_tr, int TP) {
+                                                      const uint8_t *s_tr, int pairs) {
   const QuantTensor &qt = a.t[t.tensor];
-  const int tid = threadIdx.x;
-  const int per_row = TP / 16;              // 16-byte pieces per d row
-  const int r = tid / per_row;
-  const int col = (tid - r * per_row) * 16;
-  if (r >= a.D) return;
   const int tok0 = t.ti * a.tile_tokens;
   int nvalid = a.tokens_per_frame - tok0;
   if (nvalid > a.tile_tokens) nvalid = a.tile_tokens;
   const int nbytes = nvalid / 2;            // multiple of 4 (T_f % 8 == 0)
   const int64_t dst0 = (int64_t(a.frame_slot[t.f]) * a.tokens_per_frame + tok0) / 2;
-  uint32_t *dst = reinterpret_cast<uint32_t *>(qt.codes + (int64_t(t.h) * a.D + r) * (a.rows / 2) +
-                                               dst0 + col);
-  const uint32_t *src = reinterpret_cast<const uint32_t *>(s_tr + r * TP + col);
+  const int per_row = pairs / 16;           // 16-byte pieces per d row
+  for (int k = threadIdx.x; k < a.D * per_row; k += kQuantThreads) {
+    const int r = k / per_row;
+    const int col = (k - r * per_row) * 16;
+    uint32_t *dst = reinterpret_cast<uint32_t *>(qt.codes + (int64_t(t.h) * a.D + r) * (a.rows / 2) +
+                                                 dst0 + col);
+    const uint32_t *src = reinterpret_cast<const uint32_t *>(s_tr + r * pairs + col);
 #pragma unroll
-  for (int j = 0; j < 4; ++j)
-    if (col + 4 * j < nbytes) dst[j] = src[j];
+    for (int j = 0; j < 4; ++j)
+      if (col + 4 * j < nbytes) dst[j] = src[j];
+  }
 }
 
 // Reduces the partial maxima of an amax pass of `g` workgroups; s_st[t] = amax_t / 2688.
@@ -297,32 +295,37 @@ __device__ __forceinline__ void read_tensor_scales(const QuantArgs &a, int g, ui
 }  // namespace
 
 // Pass 1: per-workgroup maxima of |x| over the flat K and V tensors (no atomics:
-// each workgroup owns one slot of the partials array).
+// each workgroup owns one slot of the partials array).  Each thread keeps up to
+// 4 vectors of K and 4 of V in flight.
 __global__ __launch_bounds__(kAmaxThreads) void quantize_amax_kernel(QuantArgs a) {
   __shared__ uint32_t s_red[2][kAmaxThreads / 64];
   const int64_t n16 = int64_t(a.H) * a.T * a.D / 8;   // uint4 vectors per tensor
   const int64_t stride = int64_t(gridDim.x) * kAmaxThreads;
-  uint32_t m[2] = {0u, 0u};
+  const uint4 *pk = reinterpret_cast<const uint4 *>(a.t[0].src);
+  const uint4 *pv = reinterpret_cast<const uint4 *>(a.n_tensors > 1 ? a.t[1].src : a.t[0].src);
+  const bool two = a.n_tensors > 1;
+  uint32_t mk = 0, mv = 0;
+  for (int64_t base = int64_t(blockIdx.x) * kAmaxThreads + threadIdx.x; base < n16;
+       base += 4 * stride) {
+    uint4 uk[4], uv[4];
 #pragma unroll
-  for (int t = 0; t < 2; ++t) {
-    if (t >= a.n_tensors) break;
-    const uint4 *p = reinterpret_cast<const uint4 *>(a.t[t].src);
-    uint32_t acc = 0;
-    int64_t i = int64_t(blockIdx.x) * kAmaxThreads + threadIdx.x;
-    for (; i + 3 * stride < n16; i += 4 * stride) {
-      const uint4 u0 = p[i], u1 = p[i + stride], u2 = p[i + 2 * stride], u3 = p[i + 3 * stride];
-      const uint32_t q0 = vmax4(u0), q1 = vmax4(u1), q2 = vmax4(u2), q3 = vmax4(u3);
-      acc = max(acc, max(max(q0 & 0xFFFFu, q0 >> 16), max(q1 & 0xFFFFu, q1 >> 16)));
-      acc = max(acc, max(max(q2 & 0xFFFFu, q2 >> 16), max(q3 & 0xFFFFu, q3 >> 16)));
+    for (int j = 0; j < 4; ++j) {
+      const int64_t i = base + j * stride;
+      uk[j] = make_uint4(0, 0, 0, 0);
+      uv[j] = make_uint4(0, 0, 0, 0);
+      if (i < n16) {
+        uk[j] = pk[i];
+        if (two) uv[j] = pv[i];
+      }
     }
-    for (; i < n16; i += stride) {
-      const uint32_t q = vmax4(p[i]);
-      acc = max(acc, max(q & 0xFFFFu, q >> 16));
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const uint32_t q = vmax4(uk[j]), w = vmax4(uv[j]);
+      mk = max(mk, max(q & 0xFFFFu, q >> 16));
+      mv = max(mv, max(w & 0xFFFFu, w >> 16));
     }
-    m[t] = acc << 16;   // fp32 bit pattern of the bf16 maximum
   }
-  m[0] = wave_max_u32(m[0]);
-  m[1] = wave_max_u32(m[1]);
+  uint32_t m[2] = {wave_max_u32(mk << 16), wave_max_u32(mv << 16)};   // fp32 bit patterns
   const int w = threadIdx.x >> 6;
   if ((threadIdx.x & 63) == 0) {
     s_red[0][w] = m[0];
@@ -336,31 +339,45 @@ __global__ __launch_bounds__(kAmaxThreads) void quantize_amax_kernel(QuantArgs a
   }
 }
 
-// Pass 2: tensor scales from the partials, then every tile is re-read and encoded.
+// Pass 2: each workgroup loads a tile (2 x 256 token-pair/block items), reduces the
+// pass-1 partials meanwhile, then encodes and stores.
 __global__ __launch_bounds__(kQuantThreads) void quantize_encode_kernel(QuantArgs a, int g_amax) {
   __shared__ uint32_t s_red[16];
   __shared__ float s_st[2];
-  __shared__ uint8_t s_tr[4096];
+  __shared__ uint8_t s_tr[8192];
   const int tid = threadIdx.x;
   const int nb = a.D >> 4;
-  const int TP = kQuantThreads / nb;
+  const int TP = kQuantThreads / nb;          // token pairs per item row
   const bool act = tid < TP * nb;
   const int b = tid % nb, tp = tid / nb;
-  read_tensor_scales(a, g_amax, s_red, s_st);
-  if (blockIdx.x == 0 && tid < a.n_tensors) *a.t[tid].tensor_scale = s_st[tid];
-  const TensorConsts tc0 = tensor_consts(s_st[0]);
-  const TensorConsts tc1 = tensor_consts(s_st[1]);
+  bool first = true;
+  TensorConsts tc0, tc1;
   for (int tile = blockIdx.x; tile < a.total_tiles; tile += gridDim.x) {
     const TileInfo t = decode_tile(a, tile);
     const bool tr = a.t[t.tensor].transposed != 0;
+    uint32_t x[2][16];
+    uint32_t bm[2] = {0u, 0u};
+    const int tin0 = t.ti * a.tile_tokens + 2 * tp;
     if (act) {
-      uint32_t x[16];
-      const uint32_t bm = load_item(a, t, tp, b, x);
-      encode_store_item(a, t, tp, b, x, bm, t.tensor ? tc1 : tc0, s_tr, TP);
+      bm[0] = load_item(a, t, tin0, b, x[0]);
+      bm[1] = load_item(a, t, tin0 + 2 * TP, b, x[1]);
+    }
+    if (first) {     // overlaps with the tile loads above
+      read_tensor_scales(a, g_amax, s_red, s_st);
+      if (blockIdx.x == 0 && tid < a.n_tensors) *a.t[tid].tensor_scale = s_st[tid];
+      tc0 = tensor_consts(s_st[0]);
+      tc1 = tensor_consts(s_st[1]);
+      first = false;
+    }
+    if (act) {
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+        encode_store_item(a, t, tin0 + 2 * TP * i, tp + TP * i, 2 * TP, b, x[i], bm[i],
+                          t.tensor ? tc1 : tc0, s_tr);
     }
     if (tr) {
       __syncthreads();
-      store_transposed_tile(a, t, s_tr, TP);
+      store_transposed_tile(a, t, s_tr, 2 * TP);
       __syncthreads();
     }
   }
@@ -387,7 +404,7 @@ int launch_quantize(const QuantArgs &in, void *stream) {
   QuantArgs a = in;
   const int nb = a.D / 16;
   const int TP = kQuantThreads / nb;
-  a.tile_tokens = 2 * TP;
+  a.tile_tokens = 4 * TP;
   a.tiles_per_frame = (a.tokens_per_frame + a.tile_tokens - 1) / a.tile_tokens;
   const int64_t total = int64_t(a.n_tensors) * a.H * a.n_frames * a.tiles_per_frame;
   if (total >= (int64_t(1) << 31)) return NVFP4KV_EINVAL;
@@ -398,14 +415,14 @@ int launch_quantize(const QuantArgs &in, void *stream) {
   const int cus = cu_count(dev);
   // pass 1: one 1024-thread workgroup per CU (fewer for small inputs)
   const int64_t vecs = int64_t(a.H) * a.T * a.D / 8;
-  int64_t g1 = (vecs + kAmaxThreads * 4 - 1) / (kAmaxThreads * 4);
+  int64_t g1 = (vecs + kAmaxThreads * 2 - 1) / (kAmaxThreads * 2);
   if (g1 > cus) g1 = cus;
   if (g1 < 1) g1 = 1;
   hipLaunchKernelGGL(quantize_amax_kernel, dim3(unsigned(g1)), dim3(kAmaxThreads), 0, s, a);
   if (hipGetLastError() != hipSuccess) return NVFP4KV_EHIP;
-  // pass 2: enough 256-thread workgroups to cover every tile or fill the GPU 8 deep
+  // pass 2: one workgroup per tile up to 4 per CU, then a grid-stride loop
   int64_t g2 = total;
-  if (g2 > int64_t(cus) * 8) g2 = int64_t(cus) * 8;
+  if (g2 > int64_t(cus) * 4) g2 = int64_t(cus) * 4;
   hipLaunchKernelGGL(quantize_encode_kernel, dim3(unsigned(g2)), dim3(kQuantThreads), 0, s, a,
                      int(g1));
   return NVFP4KV_HIP_OK(hipGetLastError());
