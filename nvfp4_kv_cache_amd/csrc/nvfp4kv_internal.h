@@ -40,10 +40,10 @@ struct QuantArgs {
   int32_t tokens_per_frame;   // T_f; source token t is frame t / T_f
   int32_t n_frames;
   int64_t rows;               // destination tokens per head
-  int32_t tile_tokens;        // tokens per workgroup tile
-  int32_t tiles_per_frame;
-  int32_t total_tiles;
-  int32_t items;              // tiles per workgroup (>= ceil(total_tiles / grid))
+  int32_t tile_tokens;        // tokens per workgroup tile (set by the launcher)
+  int32_t tiles_per_head;     // set by the launcher
+  int32_t total_tiles;        // set by the launcher
+  int32_t pad;
   QuantWorkspace *ws;
   int32_t frame_slot[kMaxFrames];   // destination slot of each source frame
 };
@@ -85,7 +85,5 @@ int launch_attention(const AttnArgs &a, void *stream);
 int launch_export(const ExportArgs &a, void *stream);
 int zero_device_bytes_blocking(void *ptr, size_t bytes);
 int zero_device_bytes_async(void *ptr, size_t bytes, void *stream);
-// Largest co-resident grid of the quantize kernel for `items` tiles per workgroup.
-int quantize_max_grid(int items, int *grid);
 
 }  // namespace nvfp4kv

@@ -32,42 +32,31 @@
 // regardless; blocks whose eff leaves [2^-120, 2^110] divide each element with
 // IEEE division instead.
 //
-// Work unit: a tile of 2 x (256 / (D/16)) token pairs x all D/16 blocks of one head
-// of one frame; thread (pair p, block b) owns token pairs p and p + 256/(D/16), i.e.
-// 4 tokens x 16 elements.  Tiles never
-// straddle a frame, so each tile lands in one cache slot.  K (and the standalone
-// codec) are written in the codec layout [h][token][D/2]; V in the cache is written
-// transposed, [h][d][token/2], through LDS, so that the attention kernel can read 8
-// consecutive keys of one d with one load; a tile then writes 64 contiguous bytes
-// per d row.  For the transposed layout a byte holds tokens (2p, 2p+1) of one d,
-// and the fp4 convert is fed exactly that pair.
+// Work unit: an item is one octet of consecutive tokens x one 16-element block
+// (8 x 32 bytes of bf16), one item per thread; a workgroup tile is 256 / (D/16)
+// octets x all D/16 blocks of one head.  Lanes run over blocks fastest, so a
+// token's D values are read by neighbouring lanes.  Tiles run over the chunk's
+// tokens regardless of frames: the destination row of each octet comes from its
+// own frame's cache slot (cache frames hold a multiple of 8 tokens, so an octet
+// never straddles two frames).  K (and the standalone codec) are written in the
+// codec layout [h][token][D/2]; V in the cache is written transposed,
+// [h][d][token/2], so that the attention kernel reads 8 consecutive keys of one d
+// with one load: an item then owns one 4-byte word (its 8 tokens) of 16 d rows,
+// and each byte holds tokens (2i, 2i+1) of one d, which is exactly the pair the
+// fp4 convert is fed.  Tokens are processed pair by pair in load order, so a wave
+// starts encoding as soon as its first loads arrive.
 
 #include "device_common.h"
 
 namespace nvfp4kv {
 
 constexpr int kAmaxThreads = 1024;
+constexpr int kOctet = 8;           // tokens per item
+constexpr int kScaleCodes = 128;    // E4M3 bytes 0x00..0x7F (0x7E is the largest produced)
 
 typedef short short2_ __attribute__((ext_vector_type(2)));
 
 namespace {
-
-struct TileInfo {
-  int tensor, h, f, ti;
-};
-
-__device__ __forceinline__ TileInfo decode_tile(const QuantArgs &a, int tile) {
-  const int per_tensor = a.H * a.n_frames * a.tiles_per_frame;
-  TileInfo t;
-  t.tensor = tile / per_tensor;
-  int r = tile - t.tensor * per_tensor;
-  const int per_head = a.n_frames * a.tiles_per_frame;
-  t.h = r / per_head;
-  r -= t.h * per_head;
-  t.f = r / a.tiles_per_frame;
-  t.ti = r - t.f * a.tiles_per_frame;
-  return t;
-}
 
 // max of the 8 |bf16| in a uint4, as two packed 16-bit halves
 __device__ __forceinline__ uint32_t vmax4(uint4 u) {
@@ -79,86 +68,86 @@ __device__ __forceinline__ uint32_t vmax4(uint4 u) {
   return pmax(pmax(a, b), pmax(c, d));
 }
 
-// Loads the 2 x 16 bf16 of tokens (tin, tin+1) of a tile's frame, block b; returns
-// block maxima of |x| as bf16 bit patterns packed (token tin in the low half).
-__device__ __forceinline__ uint32_t load_item(const QuantArgs &a, const TileInfo &t, int tin,
-                                              int b, uint32_t (&x)[16]) {
-  const int tok = t.f * a.tokens_per_frame + tin;
-  const uint16_t *src = a.t[t.tensor].src + (int64_t(t.h) * a.T + tok) * a.D + b * 16;
-#pragma unroll
-  for (int j = 0; j < 16; ++j) x[j] = 0;
-  uint4 u0 = make_uint4(0, 0, 0, 0), u1 = u0, u2 = u0, u3 = u0;
-  if (tin < a.tokens_per_frame) {
-    const uint4 *p = reinterpret_cast<const uint4 *>(src);
-    u0 = p[0];
-    u1 = p[1];
-  }
-  if (tin + 1 < a.tokens_per_frame) {
-    const uint4 *p = reinterpret_cast<const uint4 *>(src + a.D);
-    u2 = p[0];
-    u3 = p[1];
-  }
-  x[0] = u0.x; x[1] = u0.y; x[2] = u0.z; x[3] = u0.w;
-  x[4] = u1.x; x[5] = u1.y; x[6] = u1.z; x[7] = u1.w;
-  x[8] = u2.x; x[9] = u2.y; x[10] = u2.z; x[11] = u2.w;
-  x[12] = u3.x; x[13] = u3.y; x[14] = u3.z; x[15] = u3.w;
-  const uint32_t m01 = vmax4(u0), m23 = vmax4(u2);
-  const uint32_t mA = max(vmax4(u1) & 0xFFFFu, m01 & 0xFFFFu);
-  const uint32_t mB = max(vmax4(u1) >> 16, m01 >> 16);
-  const uint32_t mC = max(vmax4(u3) & 0xFFFFu, m23 & 0xFFFFu);
-  const uint32_t mD = max(vmax4(u3) >> 16, m23 >> 16);
-  return max(mA, mB) | (max(mC, mD) << 16);
-}
-
-// RN(x / b) from r = RN(1 / b): q0 = RN(x r), then two Markstein corrections.
+// RN(x / b) from r = RN(1 / b): q0 = RN(x r), then two Markstein corrections.  The
+// remainder is formed negated (q b - x) and subtracted, which leaves every nonzero
+// result unchanged and keeps the sign of a zero quotient equal to x's (an added
+// remainder would turn -0 into +0).
 __device__ __forceinline__ float div_rn(float x, float b, float r) {
   float q = x * r;
-  float e = __builtin_fmaf(-q, b, x);
-  q = __builtin_fmaf(e, r, q);
-  e = __builtin_fmaf(-q, b, x);
-  return __builtin_fmaf(e, r, q);
+  float e = __builtin_fmaf(q, b, -x);
+  q = __builtin_fmaf(-e, r, q);
+  e = __builtin_fmaf(q, b, -x);
+  return __builtin_fmaf(-e, r, q);
 }
 
 // Per-tensor constants of the encoder.
 struct TensorConsts {
   float st;       // s_t
-  float rst;      // RN(1 / s_t)
-  bool fast;      // s_t well inside the normal range: Markstein quotients apply
+  float rst;      // RN(1 / s_t), 0 when s_t == 0
+  float amin;     // block maxima below this take IEEE divisions for the scale byte
+  float xs;       // 2^K applied to x and eff alike when s_t is extreme, else 1
 };
 
+// Power of two that brings s_t near 2^-10 when s_t leaves [2^-100, 2^100]: x / eff
+// is unchanged when both are scaled by it, and all the scaled operands stay normal.
+__device__ __forceinline__ float extreme_rescale(float st) {
+  if (!(st > 0.0f) || (st >= 0x1p-100f && st <= 0x1p100f)) return 1.0f;
+  const int e = st < 0x1p-126f ? -127 : int((__float_as_uint(st) >> 23) & 0xFF) - 127;
+  return __builtin_ldexpf(1.0f, -10 - e);
+}
+
+// Markstein quotients for the scale byte need s_t well inside the normal range and
+// amax / 6 far enough above it for the remainders to stay normal.  An all-zero
+// tensor (s_t == 0) takes them too: every block maximum is 0 and gives bs = 0.
 __device__ __forceinline__ TensorConsts tensor_consts(float st) {
   TensorConsts c;
   c.st = st;
-  c.fast = st >= 0x1p-120f && st <= 0x1p100f;
-  c.rst = c.fast ? 1.0f / st : 0.0f;
+  const bool fast = st >= 0x1p-120f && st <= 0x1p100f;
+  c.rst = fast ? 1.0f / st : 0.0f;
+  c.amin = fast ? 0x1p-90f : (st == 0.0f ? 0.0f : __builtin_inff());
+  c.xs = extreme_rescale(st);
   return c;
 }
 
-// Block scale byte and the per-element divisor of one 16-element block.
-struct BlockConsts {
-  uint32_t sc;    // E4M3 byte
-  float eff;      // E4M3(bs) * s_t
-  float r;        // RN(1 / eff); 0 when eff == 0 (codes keep only the signs)
-  bool exact;     // eff outside [2^-120, 2^110]: IEEE-divide every element
-};
+// E4M3 scale byte of one block: bs = (amax / 6) / s_t, nearest-even, saturating.
+// Markstein quotients when both are comfortably normal; IEEE division otherwise.
+__device__ __forceinline__ uint32_t scale_code(float amax, const TensorConsts &tc) {
+  float bs;
+  if (amax >= tc.amin) bs = div_rn(div_rn(amax, 6.0f, 1.0f / 6.0f), tc.st, tc.rst);
+  else bs = (amax / 6.0f) / tc.st;
+  short2_ p = {0, 0};
+  p = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(p, fminf(bs, 448.0f), 0.0f, 1.0f, false);
+  return uint32_t(uint16_t(p[0])) & 0xFFu;
+}
 
-__device__ __forceinline__ BlockConsts block_consts(uint32_t bmax_bits, const TensorConsts &tc) {
-  BlockConsts bc;
-  const float amax = bf16_bits_to_float(bmax_bits);
-  uint32_t sc = 0;
-  if (tc.st > 0.0f) {
-    float bs;
-    if (tc.fast) bs = div_rn(div_rn(amax, 6.0f, 1.0f / 6.0f), tc.st, tc.rst);
-    else bs = (amax / 6.0f) / tc.st;
-    short2_ p = {0, 0};
-    p = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(p, fminf(bs, 448.0f), 0.0f, 1.0f, false);
-    sc = uint32_t(uint16_t(p[0])) & 0xFFu;
+// Divisor entry of one scale byte: eff = E4M3(sc) * s_t (rounded as fp32, subnormals
+// included), then scaled by xs, and r = RN(1 / eff); r = 0 when eff == 0 (codes keep
+// only the signs).
+__device__ __forceinline__ float2 divisor_entry(uint32_t sc, float st, float xs) {
+  const float eff = (__builtin_amdgcn_cvt_f32_fp8(sc, 0) * st) * xs;
+  return make_float2(eff, eff > 0.0f ? 1.0f / eff : 0.0f);
+}
+
+template <bool SCALED>
+__device__ __forceinline__ float quot(float x, float eff, float r, float xs) {
+  return div_rn(SCALED ? x * xs : x, eff, r);
+}
+
+// One token's 16 bf16 of a block as fp32 (exact), element order.
+__device__ __forceinline__ void unpack16(const uint4 (&u)[2], float (&x)[16]) {
+  const uint32_t w[8] = {u[0].x, u[0].y, u[0].z, u[0].w, u[1].x, u[1].y, u[1].z, u[1].w};
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    x[2 * k] = __uint_as_float(w[k] << 16);
+    x[2 * k + 1] = __uint_as_float(w[k] & 0xFFFF0000u);
   }
-  bc.sc = sc;
-  bc.eff = __builtin_amdgcn_cvt_f32_fp8(sc, 0) * tc.st;
-  bc.exact = bc.eff > 0.0f && (bc.eff < 0x1p-120f || bc.eff > 0x1p110f);
-  bc.r = (bc.eff > 0.0f && !bc.exact) ? 1.0f / bc.eff : 0.0f;
-  return bc;
+}
+
+__device__ __forceinline__ float absmax16(const float (&x)[16]) {
+  float m = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 16; i += 2) m = fmaxf(m, fmaxf(fabsf(x[i]), fabsf(x[i + 1])));
+  return m;
 }
 
 template <int SEL>
@@ -166,130 +155,123 @@ __device__ __forceinline__ uint32_t cvt_fp4(uint32_t old, float a, float b) {
   return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(old, a, b, 1.0f, SEL);
 }
 
-// Correctly rounded signed quotient x / eff (0 with x's sign when eff == 0).  The
-// corrections of div_rn can turn a zero result into +0 (+0 + -0 = +0), so the sign
-// is re-applied from x: a nonzero quotient already carries it.
-__device__ __forceinline__ float quot(float x, const BlockConsts &bc) {
-  if (!bc.exact) return __builtin_copysignf(div_rn(x, bc.eff, bc.r), x);
-  return fminf(fmaxf(x / bc.eff, -1e30f), 1e30f);
+// Codec layout: one token's 16 values -> 8 bytes (element 2k in the low nibble).
+template <bool SCALED>
+__device__ __forceinline__ uint2 encode_token(const float (&x)[16], float eff, float r, float xs) {
+  uint32_t c[2] = {0u, 0u};
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const float *y = x + 8 * h;
+    c[h] = cvt_fp4<0>(c[h], quot<SCALED>(y[0], eff, r, xs), quot<SCALED>(y[1], eff, r, xs));
+    c[h] = cvt_fp4<1>(c[h], quot<SCALED>(y[2], eff, r, xs), quot<SCALED>(y[3], eff, r, xs));
+    c[h] = cvt_fp4<2>(c[h], quot<SCALED>(y[4], eff, r, xs), quot<SCALED>(y[5], eff, r, xs));
+    c[h] = cvt_fp4<3>(c[h], quot<SCALED>(y[6], eff, r, xs), quot<SCALED>(y[7], eff, r, xs));
+  }
+  return make_uint2(c[0], c[1]);
 }
 
-// Codes of 4 element pairs (xa[i], xb[i]) -> 4 bytes, pair i in byte i (a in the
-// low nibble).
-__device__ __forceinline__ uint32_t encode4(const float (&xa)[4], const float (&xb)[4],
-                                            const BlockConsts &ba, const BlockConsts &bb) {
-  uint32_t c = 0;
-  c = cvt_fp4<0>(c, quot(xa[0], ba), quot(xb[0], bb));
-  c = cvt_fp4<1>(c, quot(xa[1], ba), quot(xb[1], bb));
-  c = cvt_fp4<2>(c, quot(xa[2], ba), quot(xb[2], bb));
-  c = cvt_fp4<3>(c, quot(xa[3], ba), quot(xb[3], bb));
-  return c;
+// Transposed layout: tokens (2*SEL, 2*SEL+1) of the octet fill byte SEL of each of
+// the 16 per-d words.
+template <int SEL, bool SCALED>
+__device__ __forceinline__ void encode_pair_transposed(const float (&xa)[16], const float (&xb)[16],
+                                                       float effa, float ra, float effb, float rb,
+                                                       float xs, uint32_t (&out)[16]) {
+#pragma unroll
+  for (int d = 0; d < 16; ++d)
+    out[d] = cvt_fp4<SEL>(out[d], quot<SCALED>(xa[d], effa, ra, xs), quot<SCALED>(xb[d], effb, rb, xs));
 }
 
-__device__ __forceinline__ float lo_f(uint32_t w) { return __uint_as_float(w << 16); }
-__device__ __forceinline__ float hi_f(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+struct Octet {
+  int tensor, h, tok;       // source token of the octet's first token
+  int64_t row;              // destination row of that token
+  int nvalid;               // tokens of the octet inside the chunk (0..8)
+};
 
-// Encodes and stores one item: token pair p (tokens tin, tin+1 of frame t.f) x block b.
-// For the transposed layout the bytes go to s_tr[d][pair column `col`] (row stride
-// `pairs` bytes) and are written out per tile by store_transposed_tile.
-__device__ __forceinline__ void encode_store_item(const QuantArgs &a, const TileInfo &t, int tin,
-                                                  int col, int pairs, int b,
-                                                  const uint32_t (&x)[16], uint32_t bmax,
-                                                  const TensorConsts &tc, uint8_t *s_tr) {
-  const QuantTensor &qt = a.t[t.tensor];
+// Canonical item: per token, block max -> scale byte -> divisor -> 8 code bytes.
+template <bool SCALED>
+__device__ __forceinline__ void item_canonical(const QuantArgs &a, const Octet &o, int b,
+                                               const uint4 (&u)[kOctet][2],
+                                               const TensorConsts &tc, const float2 *tab) {
+  const QuantTensor &qt = a.t[o.tensor];
   const int nb = a.D >> 4;
-  const bool v0 = tin < a.tokens_per_frame, v1 = tin + 1 < a.tokens_per_frame;
-  const int64_t dtok = int64_t(a.frame_slot[t.f]) * a.tokens_per_frame + tin;
-  const BlockConsts b0 = block_consts(bmax & 0xFFFFu, tc);
-  const BlockConsts b1 = block_consts(bmax >> 16, tc);
-  if (!qt.transposed) {
-    // token rows: pairs of consecutive elements of the same token
-    uint32_t c[4];
 #pragma unroll
-    for (int g = 0; g < 4; ++g) {   // g: token (g >> 1), 8-element half (g & 1)
-      const uint32_t *w = x + 4 * g;
-      const float xa[4] = {lo_f(w[0]), lo_f(w[1]), lo_f(w[2]), lo_f(w[3])};
-      const float xb[4] = {hi_f(w[0]), hi_f(w[1]), hi_f(w[2]), hi_f(w[3])};
-      const BlockConsts &bc = (g < 2) ? b0 : b1;
-      c[g] = encode4(xa, xb, bc, bc);
-    }
-    if (v0) {
-      *reinterpret_cast<uint2 *>(qt.codes + (int64_t(t.h) * a.rows + dtok) * (a.D / 2) + b * 8) =
-          make_uint2(c[0], c[1]);
-      qt.scales[(int64_t(t.h) * a.rows + dtok) * nb + b] = uint8_t(b0.sc);
-    }
-    if (v1) {
-      *reinterpret_cast<uint2 *>(qt.codes + (int64_t(t.h) * a.rows + dtok + 1) * (a.D / 2) +
-                                 b * 8) = make_uint2(c[2], c[3]);
-      qt.scales[(int64_t(t.h) * a.rows + dtok + 1) * nb + b] = uint8_t(b1.sc);
-    }
-  } else {
-    // transposed: one byte per d holds (token tin, token tin+1)
-#pragma unroll
-    for (int g = 0; g < 4; ++g) {   // d = 4g .. 4g+3 within the block
-      const uint32_t w0 = x[2 * g], w1 = x[2 * g + 1], u0 = x[8 + 2 * g], u1 = x[8 + 2 * g + 1];
-      const float xa[4] = {lo_f(w0), hi_f(w0), lo_f(w1), hi_f(w1)};
-      const float xb[4] = {lo_f(u0), hi_f(u0), lo_f(u1), hi_f(u1)};
-      const uint32_t c = encode4(xa, xb, b0, b1);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) s_tr[(b * 16 + 4 * g + i) * pairs + col] = uint8_t(c >> (8 * i));
-    }
-    if (v0) {
-      *reinterpret_cast<uint16_t *>(qt.scales + (int64_t(t.h) * nb + b) * a.rows + dtok) =
-          uint16_t(b0.sc | (b1.sc << 8));
+  for (int j = 0; j < kOctet; ++j) {
+    float x[16];
+    unpack16(u[j], x);
+    const uint32_t sc = scale_code(absmax16(x), tc);
+    const float2 dv = tab[sc];
+    const uint2 c = encode_token<SCALED>(x, dv.x, dv.y, tc.xs);
+    if (j < o.nvalid) {
+      const int64_t row = int64_t(o.h) * a.rows + o.row + j;
+      *reinterpret_cast<uint2 *>(qt.codes + row * (a.D / 2) + b * 8) = c;
+      qt.scales[row * nb + b] = uint8_t(sc);
     }
   }
 }
 
-// Writes one LDS-staged transposed tile ([D][pairs] bytes, pairs = tile_tokens / 2)
-// to V's [h][d][rows/2] plane, 16 bytes per thread-step.
-__device__ __forceinline__ void store_transposed_tile(const QuantArgs &a, const TileInfo &t,
-                                                      const uint8_t *s_tr, int pairs) {
-  const QuantTensor &qt = a.t[t.tensor];
-  const int tok0 = t.ti * a.tile_tokens;
-  int nvalid = a.tokens_per_frame - tok0;
-  if (nvalid > a.tile_tokens) nvalid = a.tile_tokens;
-  const int nbytes = nvalid / 2;            // multiple of 4 (T_f % 8 == 0)
-  const int64_t dst0 = (int64_t(a.frame_slot[t.f]) * a.tokens_per_frame + tok0) / 2;
-  const int per_row = pairs / 16;           // 16-byte pieces per d row
-  for (int k = threadIdx.x; k < a.D * per_row; k += kQuantThreads) {
-    const int r = k / per_row;
-    const int col = (k - r * per_row) * 16;
-    uint32_t *dst = reinterpret_cast<uint32_t *>(qt.codes + (int64_t(t.h) * a.D + r) * (a.rows / 2) +
-                                                 dst0 + col);
-    const uint32_t *src = reinterpret_cast<const uint32_t *>(s_tr + r * pairs + col);
+// Transposed item (V in the cache; full octets only): 16 words of 8 tokens, one per
+// d of the block, and the octet's 8 scale bytes of this block.  Token pairs are
+// taken in load order: scale bytes and divisors of a pair right before its codes.
+template <bool SCALED>
+__device__ __forceinline__ void item_transposed(const QuantArgs &a, const Octet &o, int b,
+                                                const uint4 (&u)[kOctet][2],
+                                                const TensorConsts &tc, const float2 *tab) {
+  const QuantTensor &qt = a.t[o.tensor];
+  const int nb = a.D >> 4;
+  uint32_t sc[kOctet];
+  uint32_t out[16];
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
-      if (col + 4 * j < nbytes) dst[j] = src[j];
+  for (int d = 0; d < 16; ++d) out[d] = 0u;
+#define NVFP4KV_PAIR(SEL)                                                            \
+  {                                                                                  \
+    float xa[16], xb[16];                                                            \
+    unpack16(u[2 * SEL], xa);                                                        \
+    unpack16(u[2 * SEL + 1], xb);                                                    \
+    sc[2 * SEL] = scale_code(absmax16(xa), tc);                                      \
+    sc[2 * SEL + 1] = scale_code(absmax16(xb), tc);                                  \
+    const float2 da = tab[sc[2 * SEL]], db = tab[sc[2 * SEL + 1]];                   \
+    encode_pair_transposed<SEL, SCALED>(xa, xb, da.x, da.y, db.x, db.y, tc.xs, out); \
+  }
+  NVFP4KV_PAIR(0)
+  NVFP4KV_PAIR(1)
+  NVFP4KV_PAIR(2)
+  NVFP4KV_PAIR(3)
+#undef NVFP4KV_PAIR
+  if (o.nvalid == kOctet) {
+    uint8_t *dst = qt.codes + (int64_t(o.h) * a.D + 16 * b) * (a.rows / 2) + o.row / 2;
+#pragma unroll
+    for (int d = 0; d < 16; ++d) *reinterpret_cast<uint32_t *>(dst + d * (a.rows / 2)) = out[d];
+    *reinterpret_cast<uint2 *>(qt.scales + (int64_t(o.h) * nb + b) * a.rows + o.row) =
+        make_uint2(sc[0] | (sc[1] << 8) | (sc[2] << 16) | (sc[3] << 24),
+                   sc[4] | (sc[5] << 8) | (sc[6] << 16) | (sc[7] << 24));
   }
 }
 
-// Reduces the partial maxima of an amax pass of `g` workgroups; s_st[t] = amax_t / 2688.
-__device__ __forceinline__ void read_tensor_scales(const QuantArgs &a, int g, uint32_t *s_red,
-                                                   float *s_st) {
-  uint32_t m0 = 0, m1 = 0;
-  for (int j = threadIdx.x; j < g; j += kQuantThreads) {
-    m0 = max(m0, a.ws->partial[0][j]);
-    m1 = max(m1, a.ws->partial[1][j]);
+__device__ __forceinline__ Octet locate_octet(const QuantArgs &a, int tile, int o) {
+  Octet r;
+  r.tensor = tile / (a.H * a.tiles_per_head);
+  const int rem = tile - r.tensor * a.H * a.tiles_per_head;
+  r.h = rem / a.tiles_per_head;
+  r.tok = (rem - r.h * a.tiles_per_head) * a.tile_tokens + kOctet * o;
+  r.nvalid = min(max(a.T - r.tok, 0), kOctet);
+  const int f = min(r.tok / a.tokens_per_frame, a.n_frames - 1);
+  r.row = int64_t(a.frame_slot[f]) * a.tokens_per_frame + (r.tok - f * a.tokens_per_frame);
+  return r;
+}
+
+// Loads the octet's 8 x 16 values; tokens past the chunk end re-read its last
+// token (their results are not stored), so every load is unconditional.
+__device__ __forceinline__ void load_octet(const QuantArgs &a, const Octet &o, int b,
+                                           uint4 (&u)[kOctet][2]) {
+  const uint4 *src = reinterpret_cast<const uint4 *>(a.t[o.tensor].src + int64_t(o.h) * a.T * a.D +
+                                                     16 * b);
+  const int stride = a.D / 8;    // uint4 per token
+#pragma unroll
+  for (int j = 0; j < kOctet; ++j) {
+    const int64_t tok = min(o.tok + j, a.T - 1);
+    u[j][0] = src[tok * stride];
+    u[j][1] = src[tok * stride + 1];
   }
-  m0 = wave_max_u32(m0);
-  m1 = wave_max_u32(m1);
-  const int w = threadIdx.x >> 6;
-  if ((threadIdx.x & 63) == 0) {
-    s_red[w] = m0;
-    s_red[8 + w] = m1;
-  }
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    uint32_t r0 = 0, r1 = 0;
-    for (int i = 0; i < kQuantThreads / 64; ++i) {
-      r0 = max(r0, s_red[i]);
-      r1 = max(r1, s_red[8 + i]);
-    }
-    s_st[0] = __uint_as_float(r0) / 2688.0f;
-    s_st[1] = __uint_as_float(r1) / 2688.0f;
-  }
-  __syncthreads();
 }
 
 }  // namespace
@@ -339,46 +321,66 @@ __global__ __launch_bounds__(kAmaxThreads) void quantize_amax_kernel(QuantArgs a
   }
 }
 
-// Pass 2: each workgroup loads a tile (2 x 256 token-pair/block items), reduces the
-// pass-1 partials meanwhile, then encodes and stores.
+// Pass 2: every workgroup loads the pass-1 partials first, then its first tile; it
+// reduces the partials to s_t and fills a per-tensor table of divisors (eff, 1/eff
+// for each of the 128 scale bytes) while the tile is in flight, then encodes.
 __global__ __launch_bounds__(kQuantThreads) void quantize_encode_kernel(QuantArgs a, int g_amax) {
-  __shared__ uint32_t s_red[16];
+  __shared__ uint32_t s_red[2][kQuantThreads / 64];
   __shared__ float s_st[2];
-  __shared__ uint8_t s_tr[8192];
+  __shared__ float2 s_tab[2][kScaleCodes];
   const int tid = threadIdx.x;
   const int nb = a.D >> 4;
-  const int TP = kQuantThreads / nb;          // token pairs per item row
-  const bool act = tid < TP * nb;
-  const int b = tid % nb, tp = tid / nb;
-  bool first = true;
-  TensorConsts tc0, tc1;
-  for (int tile = blockIdx.x; tile < a.total_tiles; tile += gridDim.x) {
-    const TileInfo t = decode_tile(a, tile);
-    const bool tr = a.t[t.tensor].transposed != 0;
-    uint32_t x[2][16];
-    uint32_t bm[2] = {0u, 0u};
-    const int tin0 = t.ti * a.tile_tokens + 2 * tp;
+  const int opt = kQuantThreads / nb;         // octets per tile
+  const bool act = tid < opt * nb;
+  const int b = tid % nb, o = tid / nb;
+
+  // g_amax <= kQuantThreads: one partial per thread, duplicates are harmless
+  const int pj = min(tid, g_amax - 1);
+  uint32_t m0 = a.ws->partial[0][pj];
+  uint32_t m1 = a.ws->partial[1][pj];
+  int tile = blockIdx.x;
+  uint4 u[kOctet][2];
+  Octet oc = locate_octet(a, min(tile, a.total_tiles - 1), min(o, opt - 1));
+  load_octet(a, oc, b, u);
+
+  m0 = wave_max_u32(m0);
+  m1 = wave_max_u32(m1);
+  if ((tid & 63) == 0) {
+    s_red[0][tid >> 6] = m0;
+    s_red[1][tid >> 6] = m1;
+  }
+  __syncthreads();
+  if (tid < 2) {
+    uint32_t r = 0;
+    for (int i = 0; i < kQuantThreads / 64; ++i) r = max(r, s_red[tid][i]);
+    s_st[tid] = __uint_as_float(r) / 2688.0f;
+  }
+  __syncthreads();
+  if (blockIdx.x == 0 && tid < a.n_tensors) *a.t[tid].tensor_scale = s_st[tid];
+  const TensorConsts tc0 = tensor_consts(s_st[0]), tc1 = tensor_consts(s_st[1]);
+  for (int e = tid; e < 2 * kScaleCodes; e += kQuantThreads) {
+    const int t = e / kScaleCodes;
+    s_tab[t][e % kScaleCodes] = divisor_entry(e % kScaleCodes, s_st[t], t ? tc1.xs : tc0.xs);
+  }
+  __syncthreads();
+
+  while (tile < a.total_tiles) {
     if (act) {
-      bm[0] = load_item(a, t, tin0, b, x[0]);
-      bm[1] = load_item(a, t, tin0 + 2 * TP, b, x[1]);
+      const TensorConsts &tc = oc.tensor ? tc1 : tc0;
+      const float2 *tab = s_tab[oc.tensor];
+      const bool tr = a.t[oc.tensor].transposed != 0;
+      if (tc.xs == 1.0f) {
+        if (tr) item_transposed<false>(a, oc, b, u, tc, tab);
+        else item_canonical<false>(a, oc, b, u, tc, tab);
+      } else {
+        if (tr) item_transposed<true>(a, oc, b, u, tc, tab);
+        else item_canonical<true>(a, oc, b, u, tc, tab);
+      }
     }
-    if (first) {     // overlaps with the tile loads above
-      read_tensor_scales(a, g_amax, s_red, s_st);
-      if (blockIdx.x == 0 && tid < a.n_tensors) *a.t[tid].tensor_scale = s_st[tid];
-      tc0 = tensor_consts(s_st[0]);
-      tc1 = tensor_consts(s_st[1]);
-      first = false;
-    }
-    if (act) {
-#pragma unroll
-      for (int i = 0; i < 2; ++i)
-        encode_store_item(a, t, tin0 + 2 * TP * i, tp + TP * i, 2 * TP, b, x[i], bm[i],
-                          t.tensor ? tc1 : tc0, s_tr);
-    }
-    if (tr) {
-      __syncthreads();
-      store_transposed_tile(a, t, s_tr, 2 * TP);
-      __syncthreads();
+    tile += gridDim.x;
+    if (tile < a.total_tiles) {
+      oc = locate_octet(a, tile, min(o, opt - 1));
+      load_octet(a, oc, b, u);
     }
   }
 }
@@ -403,10 +405,10 @@ int cu_count(int dev) {
 int launch_quantize(const QuantArgs &in, void *stream) {
   QuantArgs a = in;
   const int nb = a.D / 16;
-  const int TP = kQuantThreads / nb;
-  a.tile_tokens = 4 * TP;
-  a.tiles_per_frame = (a.tokens_per_frame + a.tile_tokens - 1) / a.tile_tokens;
-  const int64_t total = int64_t(a.n_tensors) * a.H * a.n_frames * a.tiles_per_frame;
+  if (nb < 1 || nb > kQuantThreads || a.tokens_per_frame < 1 || a.n_frames < 1) return NVFP4KV_EINVAL;
+  a.tile_tokens = kOctet * (kQuantThreads / nb);
+  a.tiles_per_head = int32_t((int64_t(a.T) + a.tile_tokens - 1) / a.tile_tokens);
+  const int64_t total = int64_t(a.n_tensors) * a.H * a.tiles_per_head;
   if (total >= (int64_t(1) << 31)) return NVFP4KV_EINVAL;
   a.total_tiles = int32_t(total);
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
@@ -417,12 +419,13 @@ int launch_quantize(const QuantArgs &in, void *stream) {
   const int64_t vecs = int64_t(a.H) * a.T * a.D / 8;
   int64_t g1 = (vecs + kAmaxThreads * 2 - 1) / (kAmaxThreads * 2);
   if (g1 > cus) g1 = cus;
+  if (g1 > kMaxQuantGrid) g1 = kMaxQuantGrid;
   if (g1 < 1) g1 = 1;
   hipLaunchKernelGGL(quantize_amax_kernel, dim3(unsigned(g1)), dim3(kAmaxThreads), 0, s, a);
   if (hipGetLastError() != hipSuccess) return NVFP4KV_EHIP;
-  // pass 2: one workgroup per tile up to 4 per CU, then a grid-stride loop
+  // pass 2: one workgroup per tile, up to 16 per CU, then a grid-stride loop
   int64_t g2 = total;
-  if (g2 > int64_t(cus) * 4) g2 = int64_t(cus) * 4;
+  if (g2 > int64_t(cus) * 16) g2 = int64_t(cus) * 16;
   hipLaunchKernelGGL(quantize_encode_kernel, dim3(unsigned(g2)), dim3(kQuantThreads), 0, s, a,
                      int(g1));
   return NVFP4KV_HIP_OK(hipGetLastError());

@@ -40,10 +40,6 @@ int launch_export(const ExportArgs &a, void *) {
 }
 int zero_device_bytes_blocking(void *, size_t) { return 0; }
 int zero_device_bytes_async(void *, size_t, void *) { return 0; }
-int quantize_max_grid(int, int *grid) {
-  *grid = 2048;
-  return 0;
-}
 }  // namespace nvfp4kv
 
 using namespace nvfp4kv;
