@@ -33,6 +33,17 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 MFMA_BF16_PEAK_TFLOPS = 2516.6     # MI355X dense bf16 (fp16 is the same)
+CSRC = os.path.join(ROOT, "nvfp4_kv_cache_amd", "csrc")
+# kernel sources whose digest a PMC summary in profiles/ records; a summary taken
+# on other sources no longer describes the kernel, and its traffic is not reported
+TRAFFIC_SOURCES = {
+    "attention": ("attention.hip", "device_common.h", "nvfp4kv_internal.h"),
+    "quantize": ("quantize.hip", "device_common.h", "nvfp4kv_internal.h"),
+}
+TRAFFIC_PROFILES = {
+    "attention": "chunk_attention_kernel_rollout_steady_pmc.md",
+    "quantize": "quantize_append_quantize_workload_pmc.md",
+}
 HBM_PEAK_GBPS = 8000.0             # MI355X HBM3E
 METRIC = "NVFP4-KV chunk attention TFLOP/s + latent frames/s; KV-quantize GB/s"
 
@@ -47,26 +58,62 @@ def parse():
     p.add_argument("--steps", type=int, default=36)
     p.add_argument("--warmup", type=int, default=4)
     p.add_argument("--reps", type=int, default=30, help="launches per kernel microbenchmark")
+    p.add_argument("--warm-launches", type=int, default=30,
+                   help="untimed attention launches enqueued right before the timed ones")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-calls", type=int, default=2,
                    help="full 1.3B-shaped attention calls the CPU oracle runs as its baseline sample")
     p.add_argument("--skip-configs", action="store_true", help="rollout + roofline legs only")
     p.add_argument("--only", choices=["attention", "quantize", "copy"],
                    help="run one kernel leg only (for profiler runs): the attention kernel on the "
-                        "1.3B-shaped cache, the append of the quantize-only workload, or a plain "
-                        "256 MiB device copy (reference for the HBM byte counters)")
+                        "steady-state rollout cache (the roofline leg), the append of the "
+                        "quantize-only workload, or a plain 256 MiB device copy (reference for "
+                        "the HBM byte counters)")
     return p.parse_args()
 
 
-def timed(fn, reps, torch, host_us_per_call=60.0):
+def source_digest(leg):
+    import hashlib
+    h = hashlib.sha256()
+    for name in TRAFFIC_SOURCES[leg]:
+        with open(os.path.join(CSRC, name), "rb") as f:
+            h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()
+
+
+def measured_traffic(leg):
+    """HBM bytes per launch from the committed PMC summary of this leg
+    (FETCH_SIZE and WRITE_SIZE, each scaled by what it reads for a plain copy),
+    or None when the summary is missing or was taken on other kernel sources."""
+    path = os.path.join(ROOT, "profiles", TRAFFIC_PROFILES[leg])
+    fields = {}
+    try:
+        for ln in open(path):
+            cells = [c.strip() for c in ln.strip().strip("|").split("|")]
+            if len(cells) == 2:
+                fields[cells[0]] = cells[1]
+        if fields.get("sources_sha256") != source_digest(leg):
+            return None
+        return float(fields["traffic_bytes_per_launch"])
+    except (OSError, KeyError, ValueError):
+        return None
+
+
+def timed(fn, reps, torch, warm=3, host_us_per_call=None):
     """Mean ms per call of fn() over `reps` back-to-back calls, HIP events on
-    the current stream.  A device-side sleep is queued first so that the host
-    has enqueued every call before the first one starts: the events then time
+    the current stream (the stream the library launches on).  `warm` untimed
+    calls are enqueued right before the timed ones, so the GPU is at its working
+    clock when timing starts.  For calls shorter than the host's enqueue time,
+    `host_us_per_call` queues a device-side sleep first, long enough for the host
+    to enqueue every timed call before the first one starts: the events then time
     back-to-back GPU execution, not the Python call rate."""
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     fn()
     torch.cuda.synchronize()
-    torch.cuda._sleep(int(2.0e3 * host_us_per_call * reps) + 1_000_000)   # ~cycles at >= 2 GHz
+    for _ in range(warm):
+        fn()
+    if host_us_per_call:
+        torch.cuda._sleep(int(2.0e3 * host_us_per_call * reps) + 1_000_000)   # ~cycles at >= 2 GHz
     e0.record()
     for _ in range(reps):
         fn()
@@ -125,15 +172,40 @@ def rollout(args, torch, ops, W, device):
         "cache_tokens": n_k - wl.n_q,
         "steady_state": steady,
     }
-    # attention kernel alone, on the steady-state cache
     q, k, v = inputs[-1][0][0]
-    ams = timed(lambda: cache.attention(q, k, v, scale, out=out), args.reps, torch)
+    res.update(attention_roofline(args, torch, ops, W, cache, (q, k, v), out))
+    return res
+
+
+def attention_roofline(args, torch, ops, W, cache, qkv, out):
+    """The attention kernel alone on the steady-state rollout cache: mean launch
+    time over `reps` back-to-back launches (HIP events on the launch stream)."""
+    wl = W.WORKLOADS["rollout"]
+    q, k, v = qkv
+    ams = timed(lambda: cache.attention(q, k, v, wl.softmax_scale, out=out), args.reps, torch,
+                warm=args.warm_launches)
     flops = W.attention_flops(wl.n_heads, wl.n_q, cache.tokens()[0] + cache.tokens()[1] + wl.n_q,
                               wl.head_dim)
-    res["attn_ms"] = ams
-    res["attn_flops"] = flops
-    res["attn_tflops"] = flops / (ams * 1e-3) / 1e12
-    return res
+    return {"attn_ms": ams, "attn_flops": flops, "attn_tflops": flops / (ams * 1e-3) / 1e12}
+
+
+def roofline_only(args, torch, ops, W, device):
+    """--only attention: the same measurement as the roofline leg of a full run,
+    with the steady-state cache filled by appends alone, so that a profiler run
+    of this command sees only the timed attention launches."""
+    wl = W.WORKLOADS["rollout"]
+    cache = ops.KVCache(wl.n_heads, wl.head_dim, wl.tokens_per_frame, wl.sink_frames,
+                        wl.window_frames, device=device)
+    n_fill = (wl.sink_frames + wl.window_frames + wl.chunk_frames - 1) // wl.chunk_frames
+    for c in range(n_fill):
+        kc, vc = (W.draw_device_normal(wl, c, W.APPEND_STEP, t, device) for t in (W.K_ID, W.V_ID))
+        cache.append(kc, vc, wl.chunk_frames)
+    qkv = tuple(W.draw_device_normal(wl, n_fill, 0, t, device) for t in (W.Q_ID, W.K_ID, W.V_ID))
+    out = torch.empty((wl.n_heads, wl.n_q, wl.head_dim), dtype=torch.float32, device=device)
+    r = attention_roofline(args, torch, ops, W, cache, qkv, out)
+    return {"launch_us": r["attn_ms"] * 1e3, "flops_per_launch": r["attn_flops"],
+            "tflops": r["attn_tflops"], "frac_mfma_peak": r["attn_tflops"] / MFMA_BF16_PEAK_TFLOPS,
+            "cache_tokens": sum(cache.tokens())}
 
 
 def quantize_leg(args, torch, ops, W, device):
@@ -155,13 +227,13 @@ def quantize_leg(args, torch, ops, W, device):
         cache.append(k, v, wl.chunk_frames)
 
     reps = max(args.reps, 50)
-    ms = timed(app, reps, torch)
+    ms = timed(app, reps, torch, warm=10, host_us_per_call=60.0)
     elems = wl.n_heads * wl.chunk_tokens * wl.head_dim
     nbytes = 2 * W.quantize_bytes(elems)
     gbps = nbytes / (ms * 1e-3) / 1e9
     return {"us_per_append": ms * 1e3, "bytes_per_append": nbytes, "GB_per_s": gbps,
             "roofline": {"bound": "hbm", "achieved": gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                         "frac": gbps / HBM_PEAK_GBPS, "traffic": None}}
+                         "frac": gbps / HBM_PEAK_GBPS, "traffic": measured_traffic("quantize")}}
 
 
 def attention_config(name, args, torch, ops, W, device):
@@ -175,7 +247,9 @@ def attention_config(name, args, torch, ops, W, device):
     q, ko, vo = (dev_bits(torch, b, device) for b in W.noisy_chunk(wl, wl.n_cache_chunks))
     out = torch.empty((wl.n_heads, wl.n_q, wl.head_dim), dtype=torch.float32, device=device)
     reps = args.reps if name != "tiny" else 200
-    ms = timed(lambda: cache.attention(q, ko, vo, wl.softmax_scale, out=out), reps, torch)
+    ms = timed(lambda: cache.attention(q, ko, vo, wl.softmax_scale, out=out), reps, torch,
+               warm=args.warm_launches if name != "tiny" else 20,
+               host_us_per_call=60.0 if name == "tiny" else None)
     s, w = cache.tokens()
     flops = W.attention_flops(wl.n_heads, wl.n_q, s + w + wl.n_q, wl.head_dim)
     tf = flops / (ms * 1e-3) / 1e12
@@ -242,13 +316,13 @@ def main():
     ops.lib()
     log(f"device: {torch.cuda.get_device_name(0)}")
     if args.only == "attention":
-        r = attention_config("wan13b", args, torch, ops, W, device)
-        print(json.dumps({"leg": "attention", "workload": "wan13b", **r}), flush=True)
+        r = roofline_only(args, torch, ops, W, device)
+        print(json.dumps({"leg": "attention", "workload": "rollout steady state", **r}), flush=True)
         return
     if args.only == "copy":
         src = torch.ones(64 << 20, dtype=torch.float32, device=device)   # 256 MiB
         dst = torch.empty_like(src)
-        ms = timed(lambda: dst.copy_(src), 5, torch)
+        ms = timed(lambda: dst.copy_(src), 5, torch, warm=2)
         print(json.dumps({"leg": "copy", "bytes_read": src.numel() * 4, "bytes_written": dst.numel() * 4,
                           "ms": ms, "GB_per_s": 2 * src.numel() * 4 / (ms * 1e-3) / 1e9}), flush=True)
         return
@@ -298,7 +372,8 @@ def main():
         "wall_ms_per_step": r["wall_ms_per_step"],
         "roofline": {"bound": "mfma", "kernel": "chunk_attention_kernel<128>",
                      "achieved": r["attn_tflops"], "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                     "frac": r["attn_tflops"] / MFMA_BF16_PEAK_TFLOPS, "traffic": None,
+                     "frac": r["attn_tflops"] / MFMA_BF16_PEAK_TFLOPS,
+                     "traffic": measured_traffic("attention"),
                      "launch_us": r["attn_ms"] * 1e3, "flops_per_launch": r["attn_flops"]},
         "quantize": qz,
         "configs": configs,
