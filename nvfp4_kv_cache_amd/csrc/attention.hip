@@ -8,13 +8,15 @@
 // inside the attention kernel).
 //
 // Design for CDNA4:
-//  * A workgroup owns 128 queries of one head (4 waves x 32); two workgroups share
-//    a CU, so each SIMD interleaves two waves: one wave's softmax and dequant VALU
-//    work runs while the other's MFMAs do (measured here: LDS delivers ~210 B/clk
-//    per CU with two waves per SIMD, enough for 32-query waves re-reading K/V from
-//    LDS).  Keys stream in tiles of 64.  Each tile is dequantized ONCE per
-//    workgroup into LDS, double-buffered, while the packed bytes of the next tile
-//    are already in flight to registers.
+//  * A workgroup owns kWaves x 32 queries of one head (8 waves = 256 queries for
+//    D = 128: one workgroup per CU, two waves per SIMD; 4 waves for D = 64).  Keys
+//    stream in tiles of 64.  Each tile is dequantized ONCE per workgroup into LDS,
+//    double-buffered, so a wave's share of the dequantization work shrinks as the
+//    workgroup grows.
+//  * Software pipeline with one barrier per tile: a wave issues the QK^T MFMAs of
+//    tile t, then dequantizes its share of tile t+1 into the other LDS buffer (VALU
+//    work that runs while the matrix cores execute), issues the global loads of the
+//    packed bytes of tile t+2, and only then takes the softmax and PV of tile t.
 //  * Dequantization uses the CDNA4 converts v_cvt_scalef32_pk_f16_fp4 and
 //    _pk_f16_fp8 with scale 1.0 (exact: E2M1 and E4M3 values are fp16 numbers) and
 //    one v_pk_mul_f16 per two elements.  E2M1 x E4M3 has at most 6 significant bits
@@ -31,7 +33,8 @@
 //    V^T with the keys of each 16-key group permuted to match.
 //  * The own segment runs after the cache with Q reloaded as bf16 and K_own in
 //    bf16 (v_mfma_f32_32x32x16_bf16); V_own is converted to fp16 for the PV product
-//    (|v| < 65504 required).
+//    (|v| < 65504 required).  Its raw bf16 tiles are prefetched into registers one
+//    tile ahead, like the packed cache bytes.
 //  * Online softmax in fp32 with exp2 (log2 e folded into the multiplier).  The
 //    running maximum is raised only when a tile's maximum exceeds it by more than
 //    8 (in log2 units), so the accumulator rescale is rare; probabilities are then
@@ -53,11 +56,17 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 namespace {
 
 constexpr int kBN = 64;        // keys per tile
-constexpr int kWaves = 4;
-constexpr int kThreads = kWaves * 64;
 constexpr int kQW = 32;        // queries per wave
-constexpr int kBM = kWaves * kQW;
 constexpr float kLazy = 8.0f;  // log2 headroom before the running max is raised
+
+// Workgroup shape per head_dim.
+template <int D>
+struct Cfg {
+  static constexpr int kWaves = D >= 128 ? 8 : 4;
+  static constexpr int kThreads = kWaves * 64;
+  static constexpr int kBM = kWaves * kQW;             // queries per workgroup
+  static constexpr int kWgPerCu = kWaves == 8 ? 1 : 2;
+};
 
 // ---------------------------------------------------------------- LDS layouts
 // Rows are padded by 16 bytes: for Ks (row stride 2D+16 B = 68 dwords at D=128) and
@@ -101,16 +110,12 @@ __device__ __forceinline__ f16x2 fp8x2(uint32_t w) {
 // group) V tasks.
 template <int D>
 struct Packed {
-  static constexpr int kTasks = kBN * (D / 16) / kThreads;
+  static constexpr int kTasks = kBN * (D / 16) / Cfg<D>::kThreads;
+  static_assert(kTasks >= 1 && kTasks * Cfg<D>::kThreads == kBN * (D / 16), "task split");
   uint32_t kc[kTasks][2];    // 16 K codes
   uint32_t ks[kTasks];       // K scale byte
   uint32_t vc[kTasks][2];    // 16 V codes (keys 0-7, 8-15)
   uint32_t vs[kTasks][4];    // 16 V scale bytes
-};
-
-struct TileRef {
-  int seg;           // segment index
-  int k0;            // first key of the tile within the segment
 };
 
 // One head's cache planes (uniform pointers: the loads below use a scalar base and
@@ -132,45 +137,41 @@ __device__ __forceinline__ HeadPlanes head_planes(const AttnArgs &a, int h) {
   return p;
 }
 
+// Loads are unconditional: keys past `nval` (a multiple of 8, >= 8) re-read the
+// tile's last valid key or 8-key group, so every loaded byte is a valid code or
+// scale; those keys are masked out of the softmax.
 template <int D>
 __device__ __forceinline__ void load_packed(const HeadPlanes &hp, uint32_t tok, int nval,
                                             Packed<D> &p) {
   constexpr int nb = D / 16;
 #pragma unroll
   for (int i = 0; i < Packed<D>::kTasks; ++i) {
-    const int t = threadIdx.x + i * kThreads;
+    const int t = threadIdx.x + i * Cfg<D>::kThreads;
     // K task: (key, block) = (t / nb, t % nb)
     {
-      const int key = t / nb, b = t % nb;
-      p.kc[i][0] = p.kc[i][1] = 0;
-      p.ks[i] = 0;
-      if (key < nval) {
-        const uint32_t row = tok + uint32_t(key);
-        const uint2 c = *reinterpret_cast<const uint2 *>(hp.kc + (row * (D / 2) + uint32_t(b) * 8));
-        p.kc[i][0] = c.x;
-        p.kc[i][1] = c.y;
-        p.ks[i] = hp.ks[row * nb + uint32_t(b)];
-      }
+      const int key = min(t / nb, nval - 1), b = t % nb;
+      const uint32_t row = tok + uint32_t(key);
+      const uint2 c = *reinterpret_cast<const uint2 *>(hp.kc + (row * (D / 2) + uint32_t(b) * 8));
+      p.kc[i][0] = c.x;
+      p.kc[i][1] = c.y;
+      p.ks[i] = hp.ks[row * nb + uint32_t(b)];
     }
-    // V task: (d, 16-key group) = (t / 4, t % 4)
+    // V task: (d, 16-key group) = (t / 4, t % 4); two 8-key halves
     {
       const int d = t >> 2, g = t & 3;
-      p.vc[i][0] = p.vc[i][1] = 0;
-      for (int j = 0; j < 4; ++j) p.vs[i][j] = 0;
-      const uint32_t c0 = uint32_t(d) * (hp.rows / 2) + (tok >> 1) + uint32_t(g) * 8;
-      const uint32_t s0 = uint32_t(d >> 4) * hp.rows + tok + uint32_t(g) * 16;
-      const uint32_t *cp = reinterpret_cast<const uint32_t *>(hp.vc + c0);
-      const uint32_t *sp = reinterpret_cast<const uint32_t *>(hp.vs + s0);
-      if (g * 16 < nval) {          // nval is a multiple of 8
-        p.vc[i][0] = cp[0];
-        p.vs[i][0] = sp[0];
-        p.vs[i][1] = sp[1];
-      }
-      if (g * 16 + 8 < nval) {
-        p.vc[i][1] = cp[1];
-        p.vs[i][2] = sp[2];
-        p.vs[i][3] = sp[3];
-      }
+      const int last8 = (nval >> 3) - 1;                 // last valid 8-key group
+      const uint32_t h0 = uint32_t(min(2 * g, last8)), h1 = uint32_t(min(2 * g + 1, last8));
+      const uint32_t cbase = uint32_t(d) * (hp.rows / 2) + (tok >> 1);
+      const uint32_t sbase = uint32_t(d >> 4) * hp.rows + tok;
+      const uint32_t *cp = reinterpret_cast<const uint32_t *>(hp.vc + cbase);
+      const uint2 *sp = reinterpret_cast<const uint2 *>(hp.vs + sbase);
+      p.vc[i][0] = cp[h0];
+      p.vc[i][1] = cp[h1];
+      const uint2 s0 = sp[h0], s1 = sp[h1];
+      p.vs[i][0] = s0.x;
+      p.vs[i][1] = s0.y;
+      p.vs[i][2] = s1.x;
+      p.vs[i][3] = s1.y;
     }
   }
 }
@@ -194,7 +195,7 @@ __device__ __forceinline__ void dequant_store(const Packed<D> &p, uint16_t *Ks, 
   constexpr int nb = D / 16;
 #pragma unroll
   for (int i = 0; i < Packed<D>::kTasks; ++i) {
-    const int t = threadIdx.x + i * kThreads;
+    const int t = threadIdx.x + i * Cfg<D>::kThreads;
     {
       const int key = t / nb, b = t % nb;
       const f16x2 s0 = fp8x2<false>(p.ks[i] | (p.ks[i] << 8));   // (s, s)
@@ -218,50 +219,66 @@ __device__ __forceinline__ void dequant_store(const Packed<D> &p, uint16_t *Ks, 
   }
 }
 
-// Own bf16 K/V tile -> LDS (K as bf16, V^T as fp16).
+// Raw bf16 bytes of one own-segment tile held by one thread between its load and
+// its store to LDS: 2 x 16 bytes of K (key = t / (D/16), 16-byte chunks 2c, 2c+1) and
+// the (d, d+1) dwords of 8 consecutive keys of V.
+struct OwnRaw {
+  uint4 k[2];
+  uint32_t v[8];
+};
+
 template <int D>
-__device__ __forceinline__ void stage_own(const AttnArgs &a, int h, int tok, int nval,
-                                          uint16_t *Ks, uint16_t *Vs) {
+__device__ __forceinline__ void load_own(const AttnArgs &a, int h, int tok, int nval, OwnRaw &r) {
+  constexpr int cpk = D / 16;                   // thread pairs of 16-byte chunks per key
+  static_assert(kBN * cpk == Cfg<D>::kThreads, "own K split");
+  static_assert((D / 2) * (kBN / 8) == Cfg<D>::kThreads, "own V split");
   const int t = threadIdx.x;
-  constexpr int qpr = D / 32;                    // 32-element quarters per key row
-  for (int task = t; task < kBN * qpr; task += kThreads) {
-    const int key = task / qpr, qd = task % qpr;
-    uint4 v[4] = {make_uint4(0, 0, 0, 0), make_uint4(0, 0, 0, 0), make_uint4(0, 0, 0, 0),
-                  make_uint4(0, 0, 0, 0)};
-    if (key < nval) {
-      const uint4 *src = reinterpret_cast<const uint4 *>(
-          a.k_own + size_t(h) * a.n_q * D + (uint32_t(tok + key) * D + uint32_t(qd) * 32));
-#pragma unroll
-      for (int i = 0; i < 4; ++i) v[i] = src[i];
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i) *reinterpret_cast<uint4 *>(Ks + ks_off<D>(key, 4 * qd + i)) = v[i];
+  const uint16_t *kbase = a.k_own + size_t(h) * a.n_q * D;
+  const uint16_t *vbase = a.v_own + size_t(h) * a.n_q * D;
+  {
+    const int key = min(t / cpk, nval - 1), c = t % cpk;   // past the end: re-read a valid key
+    const uint4 *src = reinterpret_cast<const uint4 *>(kbase + (uint32_t(tok + key) * D + uint32_t(c) * 16));
+    r.k[0] = src[0];
+    r.k[1] = src[1];
   }
-  // V^T: thread = (d pair, 16-key group); one dword (d, d+1) per key
-  for (int task = t; task < (D / 2) * (kBN / 16); task += kThreads) {
-    const int dp = task % (D / 2), g = task / (D / 2);   // 2 groups of 16 keys
+  {
+    const int dp = t % (D / 2), g = t / (D / 2);            // d pair, 8-key group
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const int key = min(g * 8 + k, nval - 1);
+      r.v[k] = *reinterpret_cast<const uint32_t *>(vbase + (uint32_t(tok + key) * D + uint32_t(2 * dp)));
+    }
+  }
+}
+
+// Own tile -> LDS: K as bf16 rows, V^T as fp16 in the permuted key order.
+template <int D>
+__device__ __forceinline__ void store_own(const OwnRaw &r, uint16_t *Ks, uint16_t *Vs) {
+  constexpr int cpk = D / 16;
+  const int t = threadIdx.x;
+  {
+    const int key = t / cpk, c = t % cpk;
+    *reinterpret_cast<uint4 *>(Ks + ks_off<D>(key, 2 * c)) = r.k[0];
+    *reinterpret_cast<uint4 *>(Ks + ks_off<D>(key, 2 * c + 1)) = r.k[1];
+  }
+  {
+    const int dp = t % (D / 2), g = t / (D / 2);
     const int d = 2 * dp;
-    uint32_t w[16];
+    uint32_t lo[4], hi[4];   // fp16 pairs (key 2i, key 2i+1) of row d and of row d+1
 #pragma unroll
-    for (int k = 0; k < 16; ++k) {
-      const int key = g * 16 + k;
-      w[k] = 0;
-      if (key < nval)
-        w[k] = *reinterpret_cast<const uint32_t *>(a.v_own + size_t(h) * a.n_q * D +
-                                                   (uint32_t(tok + key) * D + uint32_t(d)));
+    for (int i = 0; i < 4; ++i) {
+      lo[i] = as_u32(pkrtz(__uint_as_float(r.v[2 * i] << 16), __uint_as_float(r.v[2 * i + 1] << 16)));
+      hi[i] = as_u32(pkrtz(__uint_as_float(r.v[2 * i] & 0xFFFF0000u),
+                           __uint_as_float(r.v[2 * i + 1] & 0xFFFF0000u)));
     }
-    uint32_t lo[8], hi[8];   // fp16 pairs (key 2i, key 2i+1) of row d and of row d+1
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      lo[i] = as_u32(pkrtz(__uint_as_float(w[2 * i] << 16),
-                                                __uint_as_float(w[2 * i + 1] << 16)));
-      hi[i] = as_u32(pkrtz(__uint_as_float(w[2 * i] & 0xFFFF0000u),
-                                                __uint_as_float(w[2 * i + 1] & 0xFFFF0000u)));
-    }
-    *reinterpret_cast<uint4 *>(Vs + vs_off(d, 2 * g)) = make_uint4(lo[0], lo[1], lo[4], lo[5]);
-    *reinterpret_cast<uint4 *>(Vs + vs_off(d, 2 * g + 1)) = make_uint4(lo[2], lo[3], lo[6], lo[7]);
-    *reinterpret_cast<uint4 *>(Vs + vs_off(d + 1, 2 * g)) = make_uint4(hi[0], hi[1], hi[4], hi[5]);
-    *reinterpret_cast<uint4 *>(Vs + vs_off(d + 1, 2 * g + 1)) = make_uint4(hi[2], hi[3], hi[6], hi[7]);
+    // 8-key group g is half (g & 1) of 16-key group g >> 1: its pairs (0,1),(2,3) go
+    // to chunk 2(g>>1) and its pairs (4,5),(6,7) to chunk 2(g>>1)+1, at 8-byte offset
+    // 8 (g & 1) within each chunk
+    const int g16 = g >> 1, off = 4 * (g & 1);
+    *reinterpret_cast<uint2 *>(Vs + vs_off(d, 2 * g16) + off) = make_uint2(lo[0], lo[1]);
+    *reinterpret_cast<uint2 *>(Vs + vs_off(d, 2 * g16 + 1) + off) = make_uint2(lo[2], lo[3]);
+    *reinterpret_cast<uint2 *>(Vs + vs_off(d + 1, 2 * g16) + off) = make_uint2(hi[0], hi[1]);
+    *reinterpret_cast<uint2 *>(Vs + vs_off(d + 1, 2 * g16 + 1) + off) = make_uint2(hi[2], hi[3]);
   }
 }
 
@@ -270,29 +287,38 @@ struct Softmax {
   float l;      // partial row sum over this lane's keys
 };
 
-// One tile: S^T = K Q^T, online softmax, O^T += V^T P^T, for the wave's 32 queries.
-template <int D, bool BF16, bool MASK>
-__device__ __forceinline__ void compute_tile(const uint16_t *Ks, const uint16_t *Vs,
-                                             const u32x4 (&qr)[D / 16], float cmul, int nval,
-                                             Softmax &sm, f32x16 (&acc)[D / 32]) {
+// S^T = K Q^T for the wave's 32 queries (all K fragments read before the MFMAs).
+template <int D, bool BF16>
+__device__ __forceinline__ void qk_tile(const uint16_t *Ks, const u32x4 (&qr)[D / 16], f32x16 (&s)[2]) {
   const int lane = threadIdx.x & 63, half = lane >> 5, l32 = lane & 31;
-  f32x16 s[2];   // [32-key block]
+  u32x4 kf[2][D / 16];
 #pragma unroll
-  for (int kb = 0; kb < 2; ++kb) {
+  for (int st = 0; st < D / 16; ++st)
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+      kf[kb][st] = *reinterpret_cast<const u32x4 *>(Ks + ks_off<D>(kb * 32 + l32, 2 * st + half));
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
     for (int r = 0; r < 16; ++r) s[kb][r] = 0.0f;
-    const int row = kb * 32 + l32;
 #pragma unroll
-    for (int st = 0; st < D / 16; ++st) {
-      const u32x4 kw = *reinterpret_cast<const u32x4 *>(Ks + ks_off<D>(row, 2 * st + half));
+  for (int st = 0; st < D / 16; ++st)
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
       if constexpr (BF16)
         s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-            __builtin_bit_cast(bf16x8, kw), __builtin_bit_cast(bf16x8, qr[st]), s[kb], 0, 0, 0);
+            __builtin_bit_cast(bf16x8, kf[kb][st]), __builtin_bit_cast(bf16x8, qr[st]), s[kb], 0, 0, 0);
       else
         s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
-            __builtin_bit_cast(f16x8, kw), __builtin_bit_cast(f16x8, qr[st]), s[kb], 0, 0, 0);
+            __builtin_bit_cast(f16x8, kf[kb][st]), __builtin_bit_cast(f16x8, qr[st]), s[kb], 0, 0, 0);
     }
-  }
+}
+
+// Online softmax of S^T, then O^T += V^T P^T.
+template <int D, bool MASK>
+__device__ __forceinline__ void softmax_pv(const uint16_t *Vs, f32x16 (&s)[2], float cmul, int nval,
+                                           Softmax &sm, f32x16 (&acc)[D / 32]) {
+  const int lane = threadIdx.x & 63, half = lane >> 5, l32 = lane & 31;
   // keys past the end of the segment (only in a segment's last tile): excluded
   // from the maximum here and given probability 0 below
   if constexpr (MASK) {
@@ -318,6 +344,12 @@ __device__ __forceinline__ void compute_tile(const uint16_t *Ks, const uint16_t 
 #pragma unroll
     for (int db = 0; db < D / 32; ++db) acc[db] *= alpha;
   }
+  f16x8 vf[D / 32][4];
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+      vf[db][ks] = *reinterpret_cast<const f16x8 *>(Vs + vs_off(db * 32 + l32, 2 * ks + half));
   const float mneg = -sm.m;
   float lsum = 0.0f;
   f16x8 p[4];    // [16-key step]
@@ -344,16 +376,11 @@ __device__ __forceinline__ void compute_tile(const uint16_t *Ks, const uint16_t 
       p[2 * kb + hh] = v;
     }
   sm.l += lsum;
-  // O^T += V^T P^T
 #pragma unroll
-  for (int db = 0; db < D / 32; ++db) {
-    const int row = db * 32 + l32;
+  for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      const f16x8 vf = *reinterpret_cast<const f16x8 *>(Vs + vs_off(row, 2 * ks + half));
-      acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vf, p[ks], acc[db], 0, 0, 0);
-    }
-  }
+    for (int db = 0; db < D / 32; ++db)
+      acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vf[db][ks], p[ks], acc[db], 0, 0, 0);
 }
 
 // Loads the wave's 32 query rows as MFMA B operands (bf16 bits).
@@ -368,14 +395,50 @@ __device__ __forceinline__ void load_q(const AttnArgs &a, int h, int q0, u32x4 (
     qr[st] = ok ? *reinterpret_cast<const u32x4 *>(qp + 16 * st) : u32x4{0, 0, 0, 0};
 }
 
+// Order of the cache tiles: the full 64-key tiles of every segment, then each
+// segment's ragged tail (fewer than 64 keys), so that the main loop never masks.
+// Cursors are (segment, first key) pairs of plain integers (uniform values).
+__device__ __forceinline__ bool first_full(const AttnArgs &a, int from, int &seg, int &k0) {
+  for (int sg = from; sg < a.n_seg; ++sg)
+    if (a.seg[sg].ntok >= kBN) {
+      seg = sg;
+      k0 = 0;
+      return true;
+    }
+  return false;
+}
+
+__device__ __forceinline__ bool next_full(const AttnArgs &a, int &seg, int &k0) {
+  if (k0 + 2 * kBN <= a.seg[seg].ntok) {
+    k0 += kBN;
+    return true;
+  }
+  return first_full(a, seg + 1, seg, k0);
+}
+
+// next segment at or after `from` with a ragged tail; k0 = first key of the tail
+__device__ __forceinline__ bool first_tail(const AttnArgs &a, int from, int &seg, int &k0, int &nval) {
+  for (int sg = from; sg < a.n_seg; ++sg) {
+    const int r = a.seg[sg].ntok % kBN;
+    if (r) {
+      seg = sg;
+      k0 = a.seg[sg].ntok - r;
+      nval = r;
+      return true;
+    }
+  }
+  return false;
+}
+
 }  // namespace
 
 template <int D>
-__global__ __launch_bounds__(kThreads, 2) void chunk_attention_kernel(AttnArgs a) {
+__global__ __launch_bounds__(Cfg<D>::kThreads, Cfg<D>::kWgPerCu) void chunk_attention_kernel(AttnArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t Ks[2][kKsElems<D>];
   __shared__ __attribute__((aligned(16))) uint16_t Vs[2][kVsElems<D>];
+  constexpr int kBM = Cfg<D>::kBM;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int half = lane >> 5, l32 = lane & 31;
+  const int l32 = lane & 31;
 
   // XCD-aware numbering: hardware places workgroup `bid` on XCD bid % 8; give each
   // XCD a contiguous range of logical (head, query-tile) ids.
@@ -424,72 +487,117 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_attention_kernel(AttnArgs a
   sm.m = -INFINITY;
   sm.l = 0.0f;
   float vunit = 1.0f;
+  f32x16 s[2];
 
-  // ---- cache segments (NVFP4), software-pipelined over tiles
+  // ---- cache segments (NVFP4)
   if (a.n_seg > 0) {
-    int cs = 0, ck = 0;   // current tile: segment, first key
     const HeadPlanes hp = head_planes<D>(a, h);
-    Packed<D> pk;
-    load_packed<D>(hp, uint32_t(a.seg[0].tok0), min(kBN, a.seg[0].ntok), pk);
-    int buf = 0;
     int cur_seg = -1;
     float cmul = 0.0f;
-    while (cs < a.n_seg) {
-      const Segment sg = a.seg[cs];
-      const int nval = min(kBN, sg.ntok - ck);
-      int ns = cs, nk = ck + kBN;
-      if (nk >= sg.ntok) {
-        ns += 1;
-        nk = 0;
-      }
-      dequant_store<D>(pk, Ks[buf], Vs[buf]);
-      if (ns < a.n_seg) {
-        const Segment sn = a.seg[ns];
-        load_packed<D>(hp, uint32_t(sn.tok0 + nk), min(kBN, sn.ntok - nk), pk);
-      }
-      if (cs != cur_seg) {
-        cur_seg = cs;
-        const float sk = a.scale_table[2 * sg.scale_slot];
-        const float sv = a.scale_table[2 * sg.scale_slot + 1];
-        cmul = a.sm_scale_log2 * sk * cq;
-        // accumulator in units of this segment's s_V (an all-zero V chunk has
-        // s_V = 0 and contributes nothing: keep the current units)
-        if (sv > 0.0f) {
-          const float r = vunit / sv;
+    // per segment: s_K folds into the logit multiplier; the accumulator moves to
+    // units of the segment's s_V (an all-zero V chunk has s_V = 0 and contributes
+    // nothing: keep the current units)
+    auto enter_segment = [&](int sg) {
+      if (sg == cur_seg) return;
+      cur_seg = sg;
+      const int slot = a.seg[sg].scale_slot;
+      const float sk = a.scale_table[2 * slot];
+      const float sv = a.scale_table[2 * slot + 1];
+      cmul = a.sm_scale_log2 * sk * cq;
+      if (sv > 0.0f) {
+        const float r = vunit / sv;
 #pragma unroll
-          for (int db = 0; db < D / 32; ++db) acc[db] *= r;
-          vunit = sv;
-        }
+        for (int db = 0; db < D / 32; ++db) acc[db] *= r;
+        vunit = sv;
       }
+    };
+
+    // full tiles, software-pipelined: tile t in LDS buffer t % 2, the packed bytes
+    // of tile t+1 in registers.  Past the last tile the pipeline re-stages the last
+    // one into the free buffer (never read).
+    int cs, ck;
+    if (first_full(a, 0, cs, ck)) {
+      Packed<D> pk;
+      load_packed<D>(hp, uint32_t(a.seg[cs].tok0 + ck), kBN, pk);
+      dequant_store<D>(pk, Ks[0], Vs[0]);
+      int ns = cs, nk = ck;
+      bool have_next = next_full(a, ns, nk);
+      int ltok = have_next ? a.seg[ns].tok0 + nk : a.seg[cs].tok0 + ck;
+      load_packed<D>(hp, uint32_t(ltok), kBN, pk);
       __syncthreads();
-      if (nval < kBN) compute_tile<D, false, true>(Ks[buf], Vs[buf], qr, cmul, nval, sm, acc);
-      else compute_tile<D, false, false>(Ks[buf], Vs[buf], qr, cmul, nval, sm, acc);
-      buf ^= 1;
-      cs = ns;
-      ck = nk;
+      int buf = 0;
+      while (true) {
+        enter_segment(cs);
+        qk_tile<D, false>(Ks[buf], qr, s);
+        // stage tile t+1 while the MFMAs run, then fetch the bytes of tile t+2
+        dequant_store<D>(pk, Ks[buf ^ 1], Vs[buf ^ 1]);
+        int s2 = ns, k2 = nk;
+        const bool have_n2 = have_next && next_full(a, s2, k2);
+        if (have_n2) ltok = a.seg[s2].tok0 + k2;
+        load_packed<D>(hp, uint32_t(ltok), kBN, pk);
+        softmax_pv<D, false>(Vs[buf], s, cmul, kBN, sm, acc);
+        __syncthreads();
+        if (!have_next) break;
+        buf ^= 1;
+        cs = ns;
+        ck = nk;
+        ns = s2;
+        nk = k2;
+        have_next = have_n2;
+      }
     }
-    __syncthreads();
+    // ragged tails, one at a time
+    int tn = 0;
+    for (bool more = first_tail(a, 0, cs, ck, tn); more; more = first_tail(a, cs + 1, cs, ck, tn)) {
+      Packed<D> pk;
+      load_packed<D>(hp, uint32_t(a.seg[cs].tok0 + ck), tn, pk);
+      dequant_store<D>(pk, Ks[0], Vs[0]);
+      enter_segment(cs);
+      __syncthreads();
+      qk_tile<D, false>(Ks[0], qr, s);
+      softmax_pv<D, true>(Vs[0], s, cmul, tn, sm, acc);
+      __syncthreads();
+    }
   }
 
-  // ---- own segment (bf16 K/V of the chunk itself)
+  // ---- own segment (bf16 K/V of the chunk itself): full tiles pipelined like the
+  // cache, then the ragged tail
   {
     load_q<D>(a, h, q0, qr);   // plain bf16 Q
     const float cmul = a.sm_scale_log2;
 #pragma unroll
     for (int db = 0; db < D / 32; ++db) acc[db] *= vunit;   // to s_V = 1 units
     vunit = 1.0f;
-    int buf = 0;
-    for (int k0 = 0; k0 < a.n_q; k0 += kBN) {
-      const int nval = min(kBN, a.n_q - k0);
-      stage_own<D>(a, h, k0, nval, Ks[buf], Vs[buf]);
+    const int nfull = a.n_q / kBN;
+    if (nfull > 0) {
+      OwnRaw raw;
+      load_own<D>(a, h, 0, kBN, raw);
+      store_own<D>(raw, Ks[0], Vs[0]);
+      load_own<D>(a, h, min(1, nfull - 1) * kBN, kBN, raw);
       __syncthreads();
-      if (nval < kBN) compute_tile<D, true, true>(Ks[buf], Vs[buf], qr, cmul, nval, sm, acc);
-      else compute_tile<D, true, false>(Ks[buf], Vs[buf], qr, cmul, nval, sm, acc);
-      buf ^= 1;
+      int buf = 0;
+      for (int t = 0; t < nfull; ++t) {
+        qk_tile<D, true>(Ks[buf], qr, s);
+        store_own<D>(raw, Ks[buf ^ 1], Vs[buf ^ 1]);
+        load_own<D>(a, h, min(t + 2, nfull - 1) * kBN, kBN, raw);
+        softmax_pv<D, false>(Vs[buf], s, cmul, kBN, sm, acc);
+        __syncthreads();
+        buf ^= 1;
+      }
+    }
+    if (nfull * kBN < a.n_q) {
+      const int nval = a.n_q - nfull * kBN;
+      OwnRaw raw;
+      load_own<D>(a, h, nfull * kBN, nval, raw);
+      store_own<D>(raw, Ks[0], Vs[0]);
+      __syncthreads();
+      qk_tile<D, true>(Ks[0], qr, s);
+      softmax_pv<D, true>(Vs[0], s, cmul, nval, sm, acc);
     }
   }
 
   // ---- epilogue: O = acc * s_V / l
+  const int half = lane >> 5;
   const float ltot = sm.l + __shfl_xor(sm.l, 32, 64);
   const float fin = vunit / ltot;
   if (qi < a.n_q) {
@@ -508,15 +616,17 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_attention_kernel(AttnArgs a
 
 int launch_attention(const AttnArgs &a, void *stream) {
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  const int qtiles = (a.n_q + kBM - 1) / kBM;
-  const int64_t nblk = int64_t(qtiles) * a.H;
-  if (nblk >= (int64_t(1) << 31)) return NVFP4KV_EINVAL;
-  if (a.D == 128)
-    hipLaunchKernelGGL(chunk_attention_kernel<128>, dim3(unsigned(nblk)), dim3(kThreads), 0, s, a);
-  else if (a.D == 64)
-    hipLaunchKernelGGL(chunk_attention_kernel<64>, dim3(unsigned(nblk)), dim3(kThreads), 0, s, a);
-  else
+  if (a.D == 128) {
+    const int64_t nblk = int64_t((a.n_q + Cfg<128>::kBM - 1) / Cfg<128>::kBM) * a.H;
+    if (nblk >= (int64_t(1) << 31)) return NVFP4KV_EINVAL;
+    hipLaunchKernelGGL(chunk_attention_kernel<128>, dim3(unsigned(nblk)), dim3(Cfg<128>::kThreads), 0, s, a);
+  } else if (a.D == 64) {
+    const int64_t nblk = int64_t((a.n_q + Cfg<64>::kBM - 1) / Cfg<64>::kBM) * a.H;
+    if (nblk >= (int64_t(1) << 31)) return NVFP4KV_EINVAL;
+    hipLaunchKernelGGL(chunk_attention_kernel<64>, dim3(unsigned(nblk)), dim3(Cfg<64>::kThreads), 0, s, a);
+  } else {
     return NVFP4KV_EINVAL;
+  }
   return NVFP4KV_HIP_OK(hipGetLastError());
 }
 
