@@ -33,8 +33,8 @@
 //    V^T with the keys of each 16-key group permuted to match.
 //  * The own segment runs after the cache with Q reloaded as bf16 and K_own in
 //    bf16 (v_mfma_f32_32x32x16_bf16); V_own is converted to fp16 for the PV product
-//    (|v| < 65504 required).  Its raw bf16 tiles are prefetched into registers one
-//    tile ahead, like the packed cache bytes.
+//    (|v| < 65504 required).  V_own is prefetched into registers one tile ahead;
+//    K_own is fetched at the top of the iteration that stores it.
 //  * Online softmax in fp32 with exp2 (log2 e folded into the multiplier).  The
 //    running maximum is raised only when a tile's maximum exceeds it by more than
 //    8 (in log2 units), so the accumulator rescale is rare; probabilities are then
@@ -219,67 +219,62 @@ __device__ __forceinline__ void dequant_store(const Packed<D> &p, uint16_t *Ks, 
   }
 }
 
-// Raw bf16 bytes of one own-segment tile held by one thread between its load and
-// its store to LDS: 2 x 16 bytes of K (key = t / (D/16), 16-byte chunks 2c, 2c+1) and
-// the (d, d+1) dwords of 8 consecutive keys of V.
-struct OwnRaw {
-  uint4 k[2];
-  uint32_t v[8];
-};
-
+// Own-segment tiles: K_own rows (bf16) are copied to LDS as they are; V_own is
+// transposed into fp16 V^T rows with the same permuted key order as the cache.
 template <int D>
-__device__ __forceinline__ void load_own(const AttnArgs &a, int h, int tok, int nval, OwnRaw &r) {
+__device__ __forceinline__ void load_own_k(const AttnArgs &a, int h, int tok, int nval, uint4 (&k)[2]) {
   constexpr int cpk = D / 16;                   // thread pairs of 16-byte chunks per key
   static_assert(kBN * cpk == Cfg<D>::kThreads, "own K split");
-  static_assert((D / 2) * (kBN / 8) == Cfg<D>::kThreads, "own V split");
   const int t = threadIdx.x;
   const uint16_t *kbase = a.k_own + size_t(h) * a.n_q * D;
+  const int key = min(t / cpk, nval - 1), c = t % cpk;   // past the end: re-read a valid key
+  const uint4 *src = reinterpret_cast<const uint4 *>(kbase + (uint32_t(tok + key) * D + uint32_t(c) * 16));
+  k[0] = src[0];
+  k[1] = src[1];
+}
+
+template <int D>
+__device__ __forceinline__ void load_own_v(const AttnArgs &a, int h, int tok, int nval, uint32_t (&v)[8]) {
+  static_assert((D / 2) * (kBN / 8) == Cfg<D>::kThreads, "own V split");
+  const int t = threadIdx.x;
   const uint16_t *vbase = a.v_own + size_t(h) * a.n_q * D;
-  {
-    const int key = min(t / cpk, nval - 1), c = t % cpk;   // past the end: re-read a valid key
-    const uint4 *src = reinterpret_cast<const uint4 *>(kbase + (uint32_t(tok + key) * D + uint32_t(c) * 16));
-    r.k[0] = src[0];
-    r.k[1] = src[1];
-  }
-  {
-    const int dp = t % (D / 2), g = t / (D / 2);            // d pair, 8-key group
+  const int dp = t % (D / 2), g = t / (D / 2);            // d pair, 8-key group
 #pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      const int key = min(g * 8 + k, nval - 1);
-      r.v[k] = *reinterpret_cast<const uint32_t *>(vbase + (uint32_t(tok + key) * D + uint32_t(2 * dp)));
-    }
+  for (int k = 0; k < 8; ++k) {
+    const int key = min(g * 8 + k, nval - 1);
+    v[k] = *reinterpret_cast<const uint32_t *>(vbase + (uint32_t(tok + key) * D + uint32_t(2 * dp)));
   }
 }
 
-// Own tile -> LDS: K as bf16 rows, V^T as fp16 in the permuted key order.
 template <int D>
-__device__ __forceinline__ void store_own(const OwnRaw &r, uint16_t *Ks, uint16_t *Vs) {
+__device__ __forceinline__ void store_own_k(const uint4 (&k)[2], uint16_t *Ks) {
   constexpr int cpk = D / 16;
   const int t = threadIdx.x;
-  {
-    const int key = t / cpk, c = t % cpk;
-    *reinterpret_cast<uint4 *>(Ks + ks_off<D>(key, 2 * c)) = r.k[0];
-    *reinterpret_cast<uint4 *>(Ks + ks_off<D>(key, 2 * c + 1)) = r.k[1];
-  }
-  {
-    const int dp = t % (D / 2), g = t / (D / 2);
-    const int d = 2 * dp;
-    uint32_t lo[4], hi[4];   // fp16 pairs (key 2i, key 2i+1) of row d and of row d+1
+  const int key = t / cpk, c = t % cpk;
+  *reinterpret_cast<uint4 *>(Ks + ks_off<D>(key, 2 * c)) = k[0];
+  *reinterpret_cast<uint4 *>(Ks + ks_off<D>(key, 2 * c + 1)) = k[1];
+}
+
+// V^T as fp16 in the permuted key order
+template <int D>
+__device__ __forceinline__ void store_own_v(const uint32_t (&v)[8], uint16_t *Vs) {
+  const int t = threadIdx.x;
+  const int dp = t % (D / 2), g = t / (D / 2);
+  const int d = 2 * dp;
+  uint32_t lo[4], hi[4];   // fp16 pairs (key 2i, key 2i+1) of row d and of row d+1
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      lo[i] = as_u32(pkrtz(__uint_as_float(r.v[2 * i] << 16), __uint_as_float(r.v[2 * i + 1] << 16)));
-      hi[i] = as_u32(pkrtz(__uint_as_float(r.v[2 * i] & 0xFFFF0000u),
-                           __uint_as_float(r.v[2 * i + 1] & 0xFFFF0000u)));
-    }
-    // 8-key group g is half (g & 1) of 16-key group g >> 1: its pairs (0,1),(2,3) go
-    // to chunk 2(g>>1) and its pairs (4,5),(6,7) to chunk 2(g>>1)+1, at 8-byte offset
-    // 8 (g & 1) within each chunk
-    const int g16 = g >> 1, off = 4 * (g & 1);
-    *reinterpret_cast<uint2 *>(Vs + vs_off(d, 2 * g16) + off) = make_uint2(lo[0], lo[1]);
-    *reinterpret_cast<uint2 *>(Vs + vs_off(d, 2 * g16 + 1) + off) = make_uint2(lo[2], lo[3]);
-    *reinterpret_cast<uint2 *>(Vs + vs_off(d + 1, 2 * g16) + off) = make_uint2(hi[0], hi[1]);
-    *reinterpret_cast<uint2 *>(Vs + vs_off(d + 1, 2 * g16 + 1) + off) = make_uint2(hi[2], hi[3]);
+  for (int i = 0; i < 4; ++i) {
+    lo[i] = as_u32(pkrtz(__uint_as_float(v[2 * i] << 16), __uint_as_float(v[2 * i + 1] << 16)));
+    hi[i] = as_u32(pkrtz(__uint_as_float(v[2 * i] & 0xFFFF0000u), __uint_as_float(v[2 * i + 1] & 0xFFFF0000u)));
   }
+  // 8-key group g is half (g & 1) of 16-key group g >> 1: its pairs (0,1),(2,3) go
+  // to chunk 2(g>>1) and its pairs (4,5),(6,7) to chunk 2(g>>1)+1, at 8-byte offset
+  // 8 (g & 1) within each chunk
+  const int g16 = g >> 1, off = 4 * (g & 1);
+  *reinterpret_cast<uint2 *>(Vs + vs_off(d, 2 * g16) + off) = make_uint2(lo[0], lo[1]);
+  *reinterpret_cast<uint2 *>(Vs + vs_off(d, 2 * g16 + 1) + off) = make_uint2(lo[2], lo[3]);
+  *reinterpret_cast<uint2 *>(Vs + vs_off(d + 1, 2 * g16) + off) = make_uint2(hi[0], hi[1]);
+  *reinterpret_cast<uint2 *>(Vs + vs_off(d + 1, 2 * g16 + 1) + off) = make_uint2(hi[2], hi[3]);
 }
 
 struct Softmax {
@@ -570,16 +565,24 @@ __global__ __launch_bounds__(Cfg<D>::kThreads, Cfg<D>::kWgPerCu) void chunk_atte
     vunit = 1.0f;
     const int nfull = a.n_q / kBN;
     if (nfull > 0) {
-      OwnRaw raw;
-      load_own<D>(a, h, 0, kBN, raw);
-      store_own<D>(raw, Ks[0], Vs[0]);
-      load_own<D>(a, h, min(1, nfull - 1) * kBN, kBN, raw);
+      uint4 rk[2];
+      uint32_t rv[8];
+      load_own_k<D>(a, h, 0, kBN, rk);
+      load_own_v<D>(a, h, 0, kBN, rv);
+      store_own_k<D>(rk, Ks[0]);
+      store_own_v<D>(rv, Vs[0]);
+      load_own_v<D>(a, h, min(1, nfull - 1) * kBN, kBN, rv);
       __syncthreads();
       int buf = 0;
       for (int t = 0; t < nfull; ++t) {
+        // K of tile t+1 is fetched at the top of the iteration (its latency runs under
+        // the QK^T MFMAs); V of tile t+1 was fetched one iteration ahead
+        const int tn = min(t + 1, nfull - 1) * kBN;
+        load_own_k<D>(a, h, tn, kBN, rk);
         qk_tile<D, true>(Ks[buf], qr, s);
-        store_own<D>(raw, Ks[buf ^ 1], Vs[buf ^ 1]);
-        load_own<D>(a, h, min(t + 2, nfull - 1) * kBN, kBN, raw);
+        store_own_v<D>(rv, Vs[buf ^ 1]);
+        store_own_k<D>(rk, Ks[buf ^ 1]);
+        load_own_v<D>(a, h, min(t + 2, nfull - 1) * kBN, kBN, rv);
         softmax_pv<D, false>(Vs[buf], s, cmul, kBN, sm, acc);
         __syncthreads();
         buf ^= 1;
@@ -587,9 +590,12 @@ __global__ __launch_bounds__(Cfg<D>::kThreads, Cfg<D>::kWgPerCu) void chunk_atte
     }
     if (nfull * kBN < a.n_q) {
       const int nval = a.n_q - nfull * kBN;
-      OwnRaw raw;
-      load_own<D>(a, h, nfull * kBN, nval, raw);
-      store_own<D>(raw, Ks[0], Vs[0]);
+      uint4 rk[2];
+      uint32_t rv[8];
+      load_own_k<D>(a, h, nfull * kBN, nval, rk);
+      load_own_v<D>(a, h, nfull * kBN, nval, rv);
+      store_own_k<D>(rk, Ks[0]);
+      store_own_v<D>(rv, Vs[0]);
       __syncthreads();
       qk_tile<D, true>(Ks[0], qr, s);
       softmax_pv<D, true>(Vs[0], s, cmul, nval, sm, acc);
