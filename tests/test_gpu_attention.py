@@ -139,3 +139,42 @@ def test_attention_deterministic(ops):
     a = host(cache.attention(q, ko, vo, 0.1))
     b = host(cache.attention(q, ko, vo, 0.1))
     assert np.array_equal(a, b)
+
+
+def test_streaming_rollout(ops):
+    """Streaming rollout workload: 40 chunks appended to a 3 sink + 9 window cache of
+    1560-token frames, with attention checked (sampled query rows of every head) at
+    an empty cache, sinks only, a full window, the first eviction, mid-run and the
+    end; the resident chunks' codes must then equal the oracle codec of the same
+    tensors byte for byte."""
+    from gpu_util import dev, host
+    from oracle import quantize_ref
+    wl = W.WORKLOADS["rollout"]
+    cache, model = build_both(ops, wl.n_heads, wl.head_dim, wl.tokens_per_frame, wl.sink_frames,
+                              wl.window_frames, [])
+    rng = np.random.default_rng(5)
+    n_q = wl.n_q
+    check_at = {0, 1, 4, 5, 17, wl.n_chunks - 1}
+    last = None
+    for c in range(wl.n_chunks):
+        if c in check_at:
+            step = int(rng.integers(wl.steps_per_chunk))
+            q, ko, vo = W.noisy_chunk(wl, c, step=step)
+            rows = np.unique(np.concatenate([rng.choice(n_q, 16, replace=False), [0, n_q - 1]]))
+            run_case(ops, cache, model, q, ko, vo, wl.softmax_scale, rows=rows,
+                     what=f"rollout chunk {c} step {step}")
+        k, v = W.clean_chunk(wl, c)
+        cache.append(dev(k), dev(v), wl.chunk_frames)
+        model.append(k, v)
+        if c == 0:
+            sink = (k, v)
+        last = (k, v)
+    assert cache.tokens() == (wl.sink_frames * wl.tokens_per_frame,
+                              wl.window_frames * wl.tokens_per_frame)
+    for c, (k, v) in ((0, sink), (wl.n_chunks - 1, last)):
+        kc, ks, vc, vs, sk, sv = cache.export_chunk(c)
+        for got, want, what in (((host(kc), host(ks), host(sk)[0]), quantize_ref(k), "K"),
+                                ((host(vc), host(vs), host(sv)[0]), quantize_ref(v), "V")):
+            assert np.array_equal(got[0], want[0]), f"chunk {c} {what} codes"
+            assert np.array_equal(got[1], want[1]), f"chunk {c} {what} scales"
+            assert np.float32(got[2]) == want[2], f"chunk {c} {what} tensor scale"
