@@ -57,6 +57,13 @@ const char *nvfp4kv_strerror(int status);
 /* Library version as "major.minor.patch" (host, static string). */
 const char *nvfp4kv_version(void);
 
+/* Testing hook for the single-pass quantizer that kvcache_append uses: its workgroups
+ * exchange their maxima through the cache's workspace and each waits for the others
+ * for at most `limit` polls (default 65536) before computing the tensor maxima itself
+ * by scanning the whole chunk; either way the result is the same.  A small limit
+ * exercises that scan.  Process-wide, read at each append.  Errors: EINVAL (limit < 0). */
+int nvfp4kv_set_quantize_spin_limit(int32_t limit);
+
 /* ------------------------------------------------------------------------------
  * Standalone NVFP4 codec of one tensor (paper section 2.2; reading note section II).
  *

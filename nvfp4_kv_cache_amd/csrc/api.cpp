@@ -9,6 +9,7 @@
 
 #include <string.h>
 
+#include <atomic>
 #include <map>
 #include <new>
 
@@ -20,6 +21,8 @@ using namespace nvfp4kv;
 namespace {
 
 constexpr size_t kAlign = 256;
+constexpr int32_t kDefaultSpinLimit = 1 << 16;
+std::atomic<int32_t> g_spin_limit{kDefaultSpinLimit};
 
 size_t round_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
@@ -91,6 +94,7 @@ struct kvcache {
   Layout L;
   uint8_t *base;
   State st;
+  uint64_t epoch = 0;   // last epoch given to the single-pass quantizer (workspace zeroed at create)
 
   uint8_t *kcodes() const { return base + L.kcodes; }
   uint8_t *kscales() const { return base + L.kscales; }
@@ -272,6 +276,8 @@ int kvcache_append(kvcache *c, const uint16_t *k, const uint16_t *v, int32_t n_f
   a.n_frames = n_frames;
   a.rows = c->L.rows;
   a.ws = c->ws();
+  a.epoch = ++c->epoch;   // never reused, even if the launch fails
+  a.spin_limit = g_spin_limit.load(std::memory_order_relaxed);
   const int rc = launch_quantize(a, stream);
   if (rc != NVFP4KV_OK) return rc;
   c->st = s;
@@ -380,6 +386,12 @@ int kvcache_export_chunk(const kvcache *c, int32_t chunk_index, uint8_t *k_codes
   a.v_scale_out = v_scale;
   for (int32_t f = 0; f < rec.n_frames; ++f) a.frame_slot[f] = rec.slot[f];
   return launch_export(a, stream);
+}
+
+int nvfp4kv_set_quantize_spin_limit(int32_t limit) {
+  if (limit < 0) return NVFP4KV_EINVAL;
+  g_spin_limit.store(limit, std::memory_order_relaxed);
+  return NVFP4KV_OK;
 }
 
 }  // extern "C"

@@ -15,10 +15,14 @@ constexpr int kMaxSegments = kMaxFrames;  // one per resident frame at worst
 constexpr int kMaxQuantGrid = 2048;       // workgroups of one quantize launch
 constexpr int kQuantThreads = 256;
 
-// Per-workgroup partial maxima of |x| (fp32 bit patterns) written by the amax
-// pass and read by the encode pass of the same call; no state survives a call.
+// Quantizer scratch.  partial: per-workgroup maxima of |x| (fp32 bit patterns)
+// written by the amax pass and read by the encode pass of the same call.  slot:
+// one word per workgroup of the single-pass kernel, (epoch << 30) | (K max << 15) |
+// V max with the maxima as |bf16| bit patterns; a slot is current only when it holds
+// the launch's epoch, so the words must start zeroed and epochs never repeat.
 struct QuantWorkspace {
   uint32_t partial[2][kMaxQuantGrid];
+  uint64_t slot[kMaxQuantGrid];
 };
 
 // One tensor of a quantize launch.  Source: bf16 [H][T][D].  Destination, canonical
@@ -43,7 +47,8 @@ struct QuantArgs {
   int32_t tile_tokens;        // tokens per workgroup tile (set by the launcher)
   int32_t tiles_per_head;     // set by the launcher
   int32_t total_tiles;        // set by the launcher
-  int32_t pad;
+  int32_t spin_limit;         // polls of the single-pass wait before its fallback scan
+  uint64_t epoch;             // > 0: the single-pass kernel may be used with this epoch
   QuantWorkspace *ws;
   int32_t frame_slot[kMaxFrames];   // destination slot of each source frame
 };

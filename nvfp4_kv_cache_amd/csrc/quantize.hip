@@ -385,9 +385,143 @@ __global__ __launch_bounds__(kQuantThreads) void quantize_encode_kernel(QuantArg
   }
 }
 
+// Single pass (cache appends): every workgroup loads its tile into registers,
+// publishes its maxima of |x| in its workspace slot tagged with the launch's epoch,
+// waits until every workgroup's slot carries that epoch, and encodes from the
+// registers, so the chunk is read once.  All workgroups of the grid must be
+// resident at the same time (the launcher checks the grid against the occupancy).
+// The wait is bounded (a.spin_limit polls): a workgroup that gives up scans the whole
+// tensors for their maxima itself, which gives the same result, so no workgroup can
+// wait forever.
+
+__device__ __forceinline__ void tensor_max_scan(const QuantArgs &a, uint32_t &mk, uint32_t &mv) {
+  const int64_t n16 = int64_t(a.H) * a.T * a.D / 8;
+  const uint4 *pk = reinterpret_cast<const uint4 *>(a.t[0].src);
+  const uint4 *pv = reinterpret_cast<const uint4 *>(a.n_tensors > 1 ? a.t[1].src : a.t[0].src);
+  for (int64_t i = threadIdx.x; i < n16; i += kQuantThreads) {
+    const uint32_t q = vmax4(pk[i]), w = vmax4(pv[i]);
+    mk = max(mk, max(q & 0xFFFFu, q >> 16));
+    mv = max(mv, max(w & 0xFFFFu, w >> 16));
+  }
+}
+
+__global__ __launch_bounds__(kQuantThreads) void quantize_fused_kernel(QuantArgs a) {
+  __shared__ uint32_t s_red[2][kQuantThreads / 64];
+  __shared__ int s_ok[kQuantThreads / 64];
+  __shared__ float s_st[2];
+  __shared__ float2 s_tab[2][kScaleCodes];
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int nb = a.D >> 4;
+  const int opt = kQuantThreads / nb;         // octets per tile
+  const bool act = tid < opt * nb;
+  const int b = tid % nb, o = tid / nb;
+
+  // the tile (tokens past the end re-read the last token: part of the tensor)
+  uint4 u[kOctet][2];
+  const Octet oc = locate_octet(a, blockIdx.x, min(o, opt - 1));
+  load_octet(a, oc, b, u);
+  uint32_t mx = 0;
+#pragma unroll
+  for (int j = 0; j < kOctet; ++j) {
+    const uint32_t q = vmax4(u[j][0]), r = vmax4(u[j][1]);
+    mx = max(mx, max(max(q & 0xFFFFu, q >> 16), max(r & 0xFFFFu, r >> 16)));
+  }
+  uint32_t mk = wave_max_u32(oc.tensor == 0 ? mx : 0u);
+  uint32_t mv = wave_max_u32(oc.tensor == 1 ? mx : 0u);
+  if (lane == 0) {
+    s_red[0][wv] = mk;
+    s_red[1][wv] = mv;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    uint32_t rk = 0, rv = 0;
+    for (int i = 0; i < kQuantThreads / 64; ++i) {
+      rk = max(rk, s_red[0][i]);
+      rv = max(rv, s_red[1][i]);
+    }
+    const uint64_t word = (a.epoch << 30) | (uint64_t(rk) << 15) | uint64_t(rv);
+    __hip_atomic_store(&a.ws->slot[blockIdx.x], word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  __syncthreads();
+
+  // wait for the slots of every workgroup of this launch
+  uint32_t gk = 0, gv = 0;
+  for (int spin = 0;; ++spin) {
+    bool ok = true;
+    uint32_t k = 0, v = 0;
+    for (int j = tid; j < int(gridDim.x); j += kQuantThreads) {
+      const uint64_t w = __hip_atomic_load(&a.ws->slot[j], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      ok = ok && (w >> 30) == a.epoch;
+      k = max(k, uint32_t(w >> 15) & 0x7FFFu);
+      v = max(v, uint32_t(w) & 0x7FFFu);
+    }
+    const int wave_ok = __all(ok);
+    k = wave_max_u32(k);
+    v = wave_max_u32(v);
+    if (lane == 0) {
+      s_ok[wv] = wave_ok;
+      s_red[0][wv] = k;
+      s_red[1][wv] = v;
+    }
+    __syncthreads();
+    bool all_ok = true;
+    gk = gv = 0;
+    for (int i = 0; i < kQuantThreads / 64; ++i) {
+      all_ok = all_ok && s_ok[i];
+      gk = max(gk, s_red[0][i]);
+      gv = max(gv, s_red[1][i]);
+    }
+    __syncthreads();
+    if (all_ok) break;
+    if (spin >= a.spin_limit) {   // give up waiting: scan the tensors
+      uint32_t fk = 0, fv = 0;
+      tensor_max_scan(a, fk, fv);
+      fk = wave_max_u32(fk);
+      fv = wave_max_u32(fv);
+      if (lane == 0) {
+        s_red[0][wv] = fk;
+        s_red[1][wv] = fv;
+      }
+      __syncthreads();
+      gk = gv = 0;
+      for (int i = 0; i < kQuantThreads / 64; ++i) {
+        gk = max(gk, s_red[0][i]);
+        gv = max(gv, s_red[1][i]);
+      }
+      break;
+    }
+    __builtin_amdgcn_s_sleep(2);
+  }
+
+  const float st0 = bf16_bits_to_float(gk) / 2688.0f, st1 = bf16_bits_to_float(gv) / 2688.0f;
+  if (blockIdx.x == 0 && tid == 0) {
+    *a.t[0].tensor_scale = st0;
+    if (a.n_tensors > 1) *a.t[1].tensor_scale = st1;
+  }
+  const TensorConsts tc0 = tensor_consts(st0), tc1 = tensor_consts(st1);
+  for (int e = tid; e < 2 * kScaleCodes; e += kQuantThreads) {
+    const int t = e / kScaleCodes;
+    s_tab[t][e % kScaleCodes] = divisor_entry(e % kScaleCodes, t ? st1 : st0, t ? tc1.xs : tc0.xs);
+  }
+  __syncthreads();
+  if (act) {
+    const TensorConsts &tc = oc.tensor ? tc1 : tc0;
+    const float2 *tab = s_tab[oc.tensor];
+    const bool tr = a.t[oc.tensor].transposed != 0;
+    if (tc.xs == 1.0f) {
+      if (tr) item_transposed<false>(a, oc, b, u, tc, tab);
+      else item_canonical<false>(a, oc, b, u, tc, tab);
+    } else {
+      if (tr) item_transposed<true>(a, oc, b, u, tc, tab);
+      else item_canonical<true>(a, oc, b, u, tc, tab);
+    }
+  }
+}
+
 namespace {
 constexpr int kMaxDevices = 64;
 int g_cu_count[kMaxDevices];
+int g_fused_per_cu[kMaxDevices];   // co-resident workgroups of the single-pass kernel per CU
 
 int cu_count(int dev) {
   if (dev < 0 || dev >= kMaxDevices) return 256;
@@ -415,6 +549,20 @@ int launch_quantize(const QuantArgs &in, void *stream) {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return NVFP4KV_EHIP;
   const int cus = cu_count(dev);
+  if (a.epoch > 0 && a.total_tiles <= kMaxQuantGrid && dev >= 0 && dev < kMaxDevices) {
+    if (g_fused_per_cu[dev] == 0) {
+      int per = 0;
+      if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, quantize_fused_kernel, kQuantThreads, 0) !=
+          hipSuccess)
+        return NVFP4KV_EHIP;
+      g_fused_per_cu[dev] = per > 0 ? per : -1;
+    }
+    if (g_fused_per_cu[dev] > 0 && a.total_tiles <= int64_t(cus) * g_fused_per_cu[dev]) {
+      hipLaunchKernelGGL(quantize_fused_kernel, dim3(unsigned(a.total_tiles)), dim3(kQuantThreads), 0, s,
+                         a);
+      return NVFP4KV_HIP_OK(hipGetLastError());
+    }
+  }
   // pass 1: one 1024-thread workgroup per CU (fewer for small inputs)
   const int64_t vecs = int64_t(a.H) * a.T * a.D / 8;
   int64_t g1 = (vecs + kAmaxThreads * 2 - 1) / (kAmaxThreads * 2);

@@ -40,6 +40,7 @@ def lib():
         sig = {
             "nvfp4kv_strerror": (ctypes.c_char_p, [I]),
             "nvfp4kv_version": (ctypes.c_char_p, []),
+            "nvfp4kv_set_quantize_spin_limit": (I, [ctypes.c_int32]),
             "nvfp4_quantize_workspace_bytes": (SZ, []),
             "nvfp4_quantize_kv": (I, [P, I64, I64, I64, P, P, P, P, SZ, P]),
             "kvcache_storage_bytes": (SZ, [ctypes.POINTER(KVCacheConfig)]),
@@ -68,6 +69,12 @@ def strerror(status):
 def _check(rc, where):
     if rc != 0:
         raise NVFP4KVError(rc, where)
+
+
+def set_quantize_spin_limit(limit):
+    """Testing hook: polls the single-pass append quantizer makes before it computes
+    the tensor maxima by a scan of its own (same result either way)."""
+    _check(lib().nvfp4kv_set_quantize_spin_limit(int(limit)), "nvfp4kv_set_quantize_spin_limit")
 
 
 def _stream():

@@ -119,3 +119,69 @@ def test_append_quantize_workload_steady_state(ops):
         assert_codec_equal((host(vc), host(vs), host(sv)[0]), quantize_ref(v), f"chunk {c} V")
     with pytest.raises(ops.NVFP4KVError):
         cache.export_chunk(1)          # evicted by chunk 4
+
+
+@pytest.mark.parametrize("D", [64, 128])
+def test_append_extreme_and_special_chunks(ops, D):
+    """Appends whose tensors have extreme, zero or special-valued contents, one after
+    another into one cache (each append computes its own s_t), with a frame length
+    that leaves a ragged quantizer tile; every resident chunk's codes, scale bytes
+    and tensor scales must equal the oracle's codec of the appended tensors."""
+    from gpu_util import dev, host
+    H, T_f, nf = 3, 40, 2
+    T = nf * T_f
+    rng = np.random.default_rng(7 + D)
+    cache = ops.KVCache(H, D, T_f, 2, 8)
+
+    def special():
+        x = rng.standard_normal((H, T, D)).astype(np.float32)
+        x[0, 0, :16] = 0.0
+        x[0, 1, :16] = -0.0
+        x[1, 2, :] *= 1e-6
+        x[1, 3, :] = np.float32(2.0 ** -130) * rng.integers(-50, 50, D)
+        x[2, 5, 0] = 4096.0
+        return W.f32_to_bf16_bits(x)
+
+    zero = np.zeros((H, T, D), dtype=np.uint16)
+    zero[:, ::3] = 0x8000
+    chunks = [
+        (t4_bits(rng, (H, T, D), 1e-30), t4_bits(rng, (H, T, D), 1e30)),
+        (special(), t4_bits(rng, (H, T, D), 1e-3)),
+        (zero, special()),
+        (np.full((H, T, D), 0x0001, dtype=np.uint16), t4_bits(rng, (H, T, D), 1e4)),
+        (t4_bits(rng, (H, T, D)), zero),
+    ]
+    for k, v in chunks:
+        cache.append(dev(k), dev(v), nf)
+    for c, (k, v) in enumerate(chunks):
+        kc, ks, vc, vs, sk, sv = cache.export_chunk(c)
+        assert_codec_equal((host(kc), host(ks), host(sk)[0]), quantize_ref(k), f"D{D} chunk {c} K")
+        assert_codec_equal((host(vc), host(vs), host(sv)[0]), quantize_ref(v), f"D{D} chunk {c} V")
+
+
+def test_append_wait_fallback_scan(ops):
+    """With a zero poll limit, workgroups of the single-pass append quantizer that do
+    not find every maximum published on their first look compute the tensor maxima by
+    scanning the chunk themselves; codes, scale bytes and tensor scales must not change."""
+    from gpu_util import dev, host
+    H, D, T_f = 4, 128, 256         # 16 workgroups per append
+    rng = np.random.default_rng(11)
+    chunks = [(t4_bits(rng, (H, 2 * T_f, D), s), t4_bits(rng, (H, 2 * T_f, D), 1.0 / s))
+              for s in (1.0, 1e-20, 3e5)]
+    results = []
+    for limit in (0, 1 << 16):
+        ops.set_quantize_spin_limit(limit)
+        try:
+            cache = ops.KVCache(H, D, T_f, 2, 4)
+            for k, v in chunks:
+                cache.append(dev(k), dev(v), 2)
+            results.append([tuple(host(t) for t in cache.export_chunk(c)) for c in range(3)])
+        finally:
+            ops.set_quantize_spin_limit(1 << 16)
+    for c, (k, v) in enumerate(chunks):
+        for r in results:
+            kc, ks, vc, vs, sk, sv = r[c]
+            assert_codec_equal((kc, ks, sk[0]), quantize_ref(k), f"chunk {c} K")
+            assert_codec_equal((vc, vs, sv[0]), quantize_ref(v), f"chunk {c} V")
+    with pytest.raises(ops.NVFP4KVError):
+        ops.set_quantize_spin_limit(-1)
