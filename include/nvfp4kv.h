@@ -57,12 +57,16 @@ const char *nvfp4kv_strerror(int status);
 /* Library version as "major.minor.patch" (host, static string). */
 const char *nvfp4kv_version(void);
 
-/* Testing hook for the single-pass quantizer that kvcache_append uses: its workgroups
- * exchange their maxima through the cache's workspace and each waits for the others
- * for at most `limit` polls (default 65536) before computing the tensor maxima itself
- * by scanning the whole chunk; either way the result is the same.  A small limit
- * exercises that scan.  Process-wide, read at each append.  Errors: EINVAL (limit < 0). */
-int nvfp4kv_set_quantize_spin_limit(int32_t limit);
+/* Testing hook for the two bounded waits between workgroups; either way the results
+ * are the same.  kvcache_append's single-pass quantizer: workgroups exchange their
+ * maxima through the cache's workspace and each waits for the others for at most
+ * `limit` polls before computing the tensor maxima itself by scanning the whole chunk.
+ * chunk_attention: a query block cut between workgroups is finished by the one that
+ * holds its first key tiles, which waits for the others' partial results for at most
+ * `limit` polls per partial before processing the block's remaining tiles itself.
+ * Default 65536; a small limit exercises the fallbacks.  Process-wide, read at each
+ * call.  Errors: EINVAL (limit < 0). */
+int nvfp4kv_set_wait_limit(int32_t limit);
 
 /* ------------------------------------------------------------------------------
  * Standalone NVFP4 codec of one tensor (paper section 2.2; reading note section II).
@@ -112,8 +116,11 @@ typedef struct {
 typedef struct kvcache kvcache; /* opaque host object */
 
 /* Device bytes the cache needs: 9/16 byte per cached K or V element (codes + block
- * scales, i.e. 9/8 T H d for K and V together), plus a per-chunk tensor-scale table
- * and the quantizer's workspace.  Returns 0 for an unsupported configuration. */
+ * scales, i.e. 9/8 T H d for K and V together), plus scratch of a fixed size that does
+ * not grow with the cache: a per-chunk tensor-scale table, the quantizer's workspace
+ * and chunk_attention's load-balancing slots (one partial query-block result per
+ * workgroup of a full-GPU launch: about 34.6 MB for head_dim 128, 17.8 MB for 64).
+ * Returns 0 for an unsupported configuration. */
 size_t kvcache_storage_bytes(const kvcache_config *cfg);
 
 /* Creates the host object over caller-owned device storage (>= kvcache_storage_bytes,
@@ -151,6 +158,9 @@ int kvcache_chunk_count(const kvcache *c, int32_t *n_chunks);
  * the chunk's own n_q bf16 tokens, with no mask (bidirectional inside the chunk).
  *   q, k_own, v_own  bf16 [H, n_q, D] (finite; |v_own| < 65504);
  *   out              fp32 [H, n_q, D];  n_q >= 1;  softmax_scale > 0 and finite.
+ * The work (query blocks x key tiles) is spread evenly over every CU; query blocks
+ * cut between workgroups are merged through the cache's scratch, so attention calls
+ * on one cache must not run concurrently (calls on different caches may).
  * Errors: EINVAL (null or misaligned pointer, bad size or scale), EHIP. */
 int chunk_attention(const kvcache *c, const uint16_t *q, const uint16_t *k_own,
                     const uint16_t *v_own, int64_t n_q, float softmax_scale, float *out,

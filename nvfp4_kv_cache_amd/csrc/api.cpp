@@ -30,7 +30,7 @@ bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p
 
 struct Layout {
   int64_t rows;   // token capacity per head
-  size_t kcodes, kscales, vcodes, vscales, table, ws, total;
+  size_t kcodes, kscales, vcodes, vscales, table, ws, attn_flags, attn_part, total;
 };
 
 bool config_ok(const kvcache_config *c) {
@@ -61,6 +61,8 @@ bool make_layout(const kvcache_config *c, Layout *L) {
   L->vscales = off; off = round_up(off + size_t(H * L->rows * D / 16));
   L->table = off;   off = round_up(off + sizeof(float) * 2 * kScaleSlots);
   L->ws = off;      off = round_up(off + sizeof(QuantWorkspace));
+  L->attn_flags = off; off = round_up(off + sizeof(uint64_t) * attn_max_grid(int(D)));
+  L->attn_part = off; off = round_up(off + attn_max_grid(int(D)) * attn_slot_bytes(int(D)));
   L->total = off;
   return true;
 }
@@ -95,6 +97,7 @@ struct kvcache {
   uint8_t *base;
   State st;
   uint64_t epoch = 0;   // last epoch given to the single-pass quantizer (workspace zeroed at create)
+  mutable uint64_t attn_epoch = 0;   // last epoch given to an attention launch (flags zeroed at create)
 
   uint8_t *kcodes() const { return base + L.kcodes; }
   uint8_t *kscales() const { return base + L.kscales; }
@@ -102,6 +105,8 @@ struct kvcache {
   uint8_t *vscales() const { return base + L.vscales; }
   float *table() const { return reinterpret_cast<float *>(base + L.table); }
   QuantWorkspace *ws() const { return reinterpret_cast<QuantWorkspace *>(base + L.ws); }
+  uint64_t *attn_flags() const { return reinterpret_cast<uint64_t *>(base + L.attn_flags); }
+  float *attn_partials() const { return reinterpret_cast<float *>(base + L.attn_part); }
   int32_t window_slot(const State &s, int32_t i) const {
     return cfg.sink_frames + (s.win_head + i) % cfg.window_frames;
   }
@@ -203,8 +208,9 @@ int kvcache_create(const kvcache_config *cfg, void *storage, size_t storage_byte
   c->cfg = *cfg;
   c->L = L;
   c->base = static_cast<uint8_t *>(storage);
-  // tensor-scale table and quantizer workspace start zeroed
-  int rc = zero_device_bytes_blocking(c->base + L.table, L.total - L.table);
+  // tensor-scale table, quantizer workspace and attention flags start zeroed (the
+  // attention partial slots need no initialization)
+  int rc = zero_device_bytes_blocking(c->base + L.table, L.attn_part - L.table);
   if (rc != NVFP4KV_OK) {
     delete c;
     return rc;
@@ -336,6 +342,10 @@ int chunk_attention(const kvcache *c, const uint16_t *q, const uint16_t *k_own,
   a.D = c->cfg.head_dim;
   a.n_q = int32_t(n_q);
   a.sm_scale_log2 = softmax_scale * 1.4426950408889634f;
+  a.partials = c->attn_partials();
+  a.flags = c->attn_flags();
+  a.epoch = ++c->attn_epoch;   // never reused, even if the launch fails
+  a.spin_limit = g_spin_limit.load(std::memory_order_relaxed);
   int32_t slots[kMaxFrames];
   const int nf = collect_frames(c, slots);
   const int32_t T_f = c->cfg.tokens_per_frame;
@@ -388,7 +398,7 @@ int kvcache_export_chunk(const kvcache *c, int32_t chunk_index, uint8_t *k_codes
   return launch_export(a, stream);
 }
 
-int nvfp4kv_set_quantize_spin_limit(int32_t limit) {
+int nvfp4kv_set_wait_limit(int32_t limit) {
   if (limit < 0) return NVFP4KV_EINVAL;
   g_spin_limit.store(limit, std::memory_order_relaxed);
   return NVFP4KV_OK;

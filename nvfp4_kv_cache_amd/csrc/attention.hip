@@ -40,8 +40,19 @@
 //    8 (in log2 units), so the accumulator rescale is rare; probabilities are then
 //    bounded by 2^8, well inside fp16.  Row sums are taken from the fp16-rounded
 //    probabilities that enter the PV product.
-//  * Workgroups are numbered so that each XCD (own L2) runs a contiguous range of
-//    (head, query-tile) pairs, i.e. mostly one head's keys.
+//  * Work distribution (stream-K style): the (query block, key tile) pairs of all
+//    heads form one list, weighted by the measured cost of each tile kind, that is
+//    cut into one equal share per resident workgroup (every CU busy, whatever the
+//    number of query blocks).  A share usually ends inside a query block; the
+//    workgroup holding the block's first tiles processes them last in its share and
+//    merges the partial results (unnormalized output, running max, row sum) that
+//    the workgroups holding the rest published as their first work, long before.
+//    Partials pass through memory with one L2 write-back per publishing workgroup
+//    and one invalidate per merging workgroup (each XCD has its own L2); the wait
+//    for a partial is bounded, after which the merging workgroup processes the
+//    block's remaining tiles itself.
+//  * Workgroups are numbered so that each XCD (own L2) runs a contiguous run of
+//    shares, i.e. mostly one head's keys.
 
 #include "device_common.h"
 
@@ -425,215 +436,430 @@ __device__ __forceinline__ bool first_tail(const AttnArgs &a, int from, int &seg
   return false;
 }
 
+// i-th full cache tile of a query block -> (segment, first key)
+__device__ __forceinline__ void nth_full(const AttnArgs &a, int i, int &seg, int &k0) {
+  int sg = 0;
+  for (; sg < a.n_seg; ++sg) {
+    const int nf = a.seg[sg].ntok / kBN;
+    if (i < nf) break;
+    i -= nf;
+  }
+  seg = sg;
+  k0 = i * kBN;
+}
+
+// i-th ragged cache tail of a query block -> segment
+__device__ __forceinline__ int nth_tail(const AttnArgs &a, int i) {
+  int sg = 0;
+  for (; sg < a.n_seg; ++sg) {
+    if (a.seg[sg].ntok % kBN == 0) continue;
+    if (i == 0) break;
+    --i;
+  }
+  return sg;
+}
+
+// Workgroup whose share [U g / G, U (g+1) / G) holds weighted position x.
+__device__ __forceinline__ int owner_of(int64_t x, int64_t U, int G) {
+  return int(((x + 1) * G + U - 1) / U) - 1;
+}
+
+// Number of a query block's tiles that start before weighted position x (0 <= x <=
+// the block's weight).  Tiles in order: cache full, cache tails, own full, own tail.
+__device__ __forceinline__ int tiles_before(const AttnArgs &a, int x) {
+  int n = 0;
+  auto part = [&](int count, int w) {
+    const int span = count * w;
+    n += x >= span ? count : (x + w - 1) / w;
+    x = max(x - span, 0);
+  };
+  part(a.n_cfull, a.w_cfull);
+  part(a.n_ctail, a.w_tail);
+  part(a.n_ofull, a.w_ofull);
+  part(a.n_otail, a.w_tail);
+  return n;
+}
+
+// Partial result of a range of a query block's tiles: the accumulator in absolute
+// units of V, then per lane the running max and the partial row sum.  Each thread
+// stores and later reads back only its own elements, 16 bytes at a time, so the
+// layout is private to the kernel and every access is coalesced.
+template <int D>
+__device__ __forceinline__ void store_partial(float *ps, const f32x16 (&acc)[D / 32], float vunit,
+                                              const Softmax &sm) {
+  constexpr int kT = Cfg<D>::kThreads;
+  const int tid = threadIdx.x;
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+    for (int g = 0; g < 4; ++g)
+      *reinterpret_cast<float4 *>(ps + ((db * 4 + g) * kT + tid) * 4) =
+          make_float4(acc[db][4 * g] * vunit, acc[db][4 * g + 1] * vunit, acc[db][4 * g + 2] * vunit,
+                      acc[db][4 * g + 3] * vunit);
+  *reinterpret_cast<float2 *>(ps + Cfg<D>::kBM * D + 2 * tid) = make_float2(sm.m, sm.l);
+}
+
+template <int D>
+__device__ __forceinline__ void write_out(const AttnArgs &a, int h, int qi, const f32x16 (&acc)[D / 32],
+                                          float fin) {
+  const int half = (threadIdx.x >> 5) & 1;
+  if (qi >= a.n_q) return;
+  float *op = a.out + (int64_t(h) * a.n_q + qi) * D;
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+    for (int gq = 0; gq < 4; ++gq) {
+      const int d = db * 32 + 8 * gq + 4 * half;
+      *reinterpret_cast<float4 *>(op + d) = make_float4(acc[db][4 * gq] * fin, acc[db][4 * gq + 1] * fin,
+                                                        acc[db][4 * gq + 2] * fin, acc[db][4 * gq + 3] * fin);
+    }
+}
+
 }  // namespace
 
 template <int D>
 __global__ __launch_bounds__(Cfg<D>::kThreads, Cfg<D>::kWgPerCu) void chunk_attention_kernel(AttnArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t Ks[2][kKsElems<D>];
   __shared__ __attribute__((aligned(16))) uint16_t Vs[2][kVsElems<D>];
+  __shared__ int s_ready;
   constexpr int kBM = Cfg<D>::kBM;
+  constexpr size_t kSlotFloats = attn_slot_bytes(D) / 4;
+  static_assert(kBM == attn_block_queries(D) && Cfg<D>::kThreads == attn_threads(D) &&
+                Cfg<D>::kWgPerCu == attn_wg_per_cu(D), "scratch sizing");
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int l32 = lane & 31;
+  const int l32 = lane & 31, half = lane >> 5;
 
   // XCD-aware numbering: hardware places workgroup `bid` on XCD bid % 8; give each
-  // XCD a contiguous range of logical (head, query-tile) ids.
-  const int n = gridDim.x, bid = blockIdx.x;
+  // XCD a contiguous run of work ranges, i.e. mostly one head's keys.
+  const int G = gridDim.x, bid = blockIdx.x;
   const int xcd = bid & 7;
-  const int logical = xcd * (n >> 3) + min(xcd, n & 7) + (bid >> 3);
-  const int qtiles = (a.n_q + kBM - 1) / kBM;
-  const int h = logical / qtiles;
-  const int q0 = (logical - h * qtiles) * kBM + w * kQW;
-  const int qi = q0 + l32;
+  const int g = xcd * (G >> 3) + min(xcd, G & 7) + (bid >> 3);
+  // this workgroup's share [u, uend) of the weighted list of all (query block, key
+  // tile) pairs; it processes the tiles that start inside its share (every share is
+  // at least one tile long, so every workgroup has tiles)
+  const int64_t U = a.work;
+  const int T = a.tiles, WB = a.w_block;
+  const int cache_tiles = a.n_cfull + a.n_ctail;
+  const int qblocks = (a.n_q + kBM - 1) / kBM;
+  const int last_w = a.n_otail ? a.w_tail : a.w_ofull;   // weight of a block's last tile
+  int64_t u = U * g / G;
+  const int64_t uend = U * (g + 1) / G;
 
-  // ---- Q as fp16 with a per-query power-of-two scale 2^sh (row max -> [2^14, 2^15))
-  u32x4 qr[D / 16];
-  load_q<D>(a, h, q0, qr);
-  float cq;
-  {
-    uint32_t mx = 0;
-#pragma unroll
-    for (int st = 0; st < D / 16; ++st)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const uint32_t v = qr[st][j] & 0x7FFF7FFFu;
-        mx = max(mx, max(v & 0xFFFFu, v >> 16));
-      }
-    mx = max(mx, uint32_t(__shfl_xor(int(mx), 32, 64)));
-    const int e = int(mx >> 7) - 127;   // floor(log2(row max)) (bf16 normals)
-    int sh = mx ? 14 - e : 0;
-    sh = max(-110, min(100, sh));
-    cq = __builtin_ldexpf(1.0f, -sh);
-#pragma unroll
-    for (int st = 0; st < D / 16; ++st)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const uint32_t v = qr[st][j];
-        qr[st][j] = as_u32(pkrtz(__builtin_ldexpf(__uint_as_float(v << 16), sh),
-                                 __builtin_ldexpf(__uint_as_float(v & 0xFFFF0000u), sh)));
-      }
-  }
+  while (u < uend) {
+    const int64_t b64 = u / WB;
+    const int b = int(b64);
+    const int p0 = int(u - b64 * WB);
+    const int p1 = int(min(int64_t(WB), int64_t(p0) + (uend - u)));
+    u = b64 * WB + p1;
+    const int t0 = tiles_before(a, p0), t1 = tiles_before(a, p1);
+    if (t0 == t1) continue;
+    const int h = b / qblocks;
+    const int q0 = (b - h * qblocks) * kBM + w * kQW;
+    const int qi = q0 + l32;
 
-  f32x16 acc[D / 32];
-#pragma unroll
-  for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) acc[db][r] = 0.0f;
-  Softmax sm;
-  sm.m = -INFINITY;
-  sm.l = 0.0f;
-  float vunit = 1.0f;
-  f32x16 s[2];
-
-  // ---- cache segments (NVFP4)
-  if (a.n_seg > 0) {
-    const HeadPlanes hp = head_planes<D>(a, h);
-    int cur_seg = -1;
-    float cmul = 0.0f;
-    // per segment: s_K folds into the logit multiplier; the accumulator moves to
-    // units of the segment's s_V (an all-zero V chunk has s_V = 0 and contributes
-    // nothing: keep the current units)
-    auto enter_segment = [&](int sg) {
-      if (sg == cur_seg) return;
-      cur_seg = sg;
-      const int slot = a.seg[sg].scale_slot;
-      const float sk = a.scale_table[2 * slot];
-      const float sv = a.scale_table[2 * slot + 1];
-      cmul = a.sm_scale_log2 * sk * cq;
-      if (sv > 0.0f) {
-        const float r = vunit / sv;
-#pragma unroll
-        for (int db = 0; db < D / 32; ++db) acc[db] *= r;
-        vunit = sv;
-      }
-    };
-
-    // full tiles, software-pipelined: tile t in LDS buffer t % 2, the packed bytes
-    // of tile t+1 in registers.  Past the last tile the pipeline re-stages the last
-    // one into the free buffer (never read).
-    int cs, ck;
-    if (first_full(a, 0, cs, ck)) {
-      Packed<D> pk;
-      load_packed<D>(hp, uint32_t(a.seg[cs].tok0 + ck), kBN, pk);
-      dequant_store<D>(pk, Ks[0], Vs[0]);
-      int ns = cs, nk = ck;
-      bool have_next = next_full(a, ns, nk);
-      int ltok = have_next ? a.seg[ns].tok0 + nk : a.seg[cs].tok0 + ck;
-      load_packed<D>(hp, uint32_t(ltok), kBN, pk);
-      __syncthreads();
-      int buf = 0;
-      while (true) {
-        enter_segment(cs);
-        qk_tile<D, false>(Ks[buf], qr, s);
-        // stage tile t+1 while the MFMAs run, then fetch the bytes of tile t+2
-        dequant_store<D>(pk, Ks[buf ^ 1], Vs[buf ^ 1]);
-        int s2 = ns, k2 = nk;
-        const bool have_n2 = have_next && next_full(a, s2, k2);
-        if (have_n2) ltok = a.seg[s2].tok0 + k2;
-        load_packed<D>(hp, uint32_t(ltok), kBN, pk);
-        softmax_pv<D, false>(Vs[buf], s, cmul, kBN, sm, acc);
-        __syncthreads();
-        if (!have_next) break;
-        buf ^= 1;
-        cs = ns;
-        ck = nk;
-        ns = s2;
-        nk = k2;
-        have_next = have_n2;
-      }
-    }
-    // ragged tails, one at a time
-    int tn = 0;
-    for (bool more = first_tail(a, 0, cs, ck, tn); more; more = first_tail(a, cs + 1, cs, ck, tn)) {
-      Packed<D> pk;
-      load_packed<D>(hp, uint32_t(a.seg[cs].tok0 + ck), tn, pk);
-      dequant_store<D>(pk, Ks[0], Vs[0]);
-      enter_segment(cs);
-      __syncthreads();
-      qk_tile<D, false>(Ks[0], qr, s);
-      softmax_pv<D, true>(Vs[0], s, cmul, tn, sm, acc);
-      __syncthreads();
-    }
-  }
-
-  // ---- own segment (bf16 K/V of the chunk itself): full tiles pipelined like the
-  // cache, then the ragged tail
-  {
-    load_q<D>(a, h, q0, qr);   // plain bf16 Q
-    const float cmul = a.sm_scale_log2;
-#pragma unroll
-    for (int db = 0; db < D / 32; ++db) acc[db] *= vunit;   // to s_V = 1 units
-    vunit = 1.0f;
-    const int nfull = a.n_q / kBN;
-    if (nfull > 0) {
-      uint4 rk[2];
-      uint32_t rv[8];
-      load_own_k<D>(a, h, 0, kBN, rk);
-      load_own_v<D>(a, h, 0, kBN, rv);
-      store_own_k<D>(rk, Ks[0]);
-      store_own_v<D>(rv, Vs[0]);
-      load_own_v<D>(a, h, min(1, nfull - 1) * kBN, kBN, rv);
-      __syncthreads();
-      int buf = 0;
-      for (int t = 0; t < nfull; ++t) {
-        // K of tile t+1 is fetched at the top of the iteration (its latency runs under
-        // the QK^T MFMAs); V of tile t+1 was fetched one iteration ahead
-        const int tn = min(t + 1, nfull - 1) * kBN;
-        load_own_k<D>(a, h, tn, kBN, rk);
-        qk_tile<D, true>(Ks[buf], qr, s);
-        store_own_v<D>(rv, Vs[buf ^ 1]);
-        store_own_k<D>(rk, Ks[buf ^ 1]);
-        load_own_v<D>(a, h, min(t + 2, nfull - 1) * kBN, kBN, rv);
-        softmax_pv<D, false>(Vs[buf], s, cmul, kBN, sm, acc);
-        __syncthreads();
-        buf ^= 1;
-      }
-    }
-    if (nfull * kBN < a.n_q) {
-      const int nval = a.n_q - nfull * kBN;
-      uint4 rk[2];
-      uint32_t rv[8];
-      load_own_k<D>(a, h, nfull * kBN, nval, rk);
-      load_own_v<D>(a, h, nfull * kBN, nval, rv);
-      store_own_k<D>(rk, Ks[0]);
-      store_own_v<D>(rv, Vs[0]);
-      __syncthreads();
-      qk_tile<D, true>(Ks[0], qr, s);
-      softmax_pv<D, true>(Vs[0], s, cmul, nval, sm, acc);
-    }
-  }
-
-  // ---- epilogue: O = acc * s_V / l
-  const int half = lane >> 5;
-  const float ltot = sm.l + __shfl_xor(sm.l, 32, 64);
-  const float fin = vunit / ltot;
-  if (qi < a.n_q) {
-    float *op = a.out + (int64_t(h) * a.n_q + qi) * D;
+    f32x16 acc[D / 32];
 #pragma unroll
     for (int db = 0; db < D / 32; ++db)
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int d = db * 32 + 8 * g + 4 * half;
-        *reinterpret_cast<float4 *>(op + d) =
-            make_float4(acc[db][4 * g] * fin, acc[db][4 * g + 1] * fin,
-                        acc[db][4 * g + 2] * fin, acc[db][4 * g + 3] * fin);
+      for (int r = 0; r < 16; ++r) acc[db][r] = 0.0f;
+    Softmax sm;
+    sm.m = -INFINITY;
+    sm.l = 0.0f;
+    float vunit = 1.0f;
+    f32x16 s[2];
+    u32x4 qr[D / 16];
+
+    // Tiles [r0, r1) of block b.  Normally r0 = t0, r1 = t1, once.  The workgroup
+    // that holds a cut block's first tiles waits (bounded) for the partials of the
+    // other workgroups; if one is still missing it processes the block's remaining
+    // tiles itself (a second pass of this loop) instead of merging.
+    int r0 = t0, r1 = t1;
+    while (true) {
+      // ---- cache tiles (NVFP4)
+      if (r0 < cache_tiles) {
+        // Q as fp16 with a per-query power-of-two scale 2^sh (row max -> [2^14, 2^15))
+        load_q<D>(a, h, q0, qr);
+        float cq;
+        {
+          uint32_t mx = 0;
+  #pragma unroll
+          for (int st = 0; st < D / 16; ++st)
+  #pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              const uint32_t v = qr[st][j] & 0x7FFF7FFFu;
+              mx = max(mx, max(v & 0xFFFFu, v >> 16));
+            }
+          mx = max(mx, uint32_t(__shfl_xor(int(mx), 32, 64)));
+          const int e = int(mx >> 7) - 127;   // floor(log2(row max)) (bf16 normals)
+          int sh = mx ? 14 - e : 0;
+          sh = max(-110, min(100, sh));
+          cq = __builtin_ldexpf(1.0f, -sh);
+  #pragma unroll
+          for (int st = 0; st < D / 16; ++st)
+  #pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              const uint32_t v = qr[st][j];
+              qr[st][j] = as_u32(pkrtz(__builtin_ldexpf(__uint_as_float(v << 16), sh),
+                                       __builtin_ldexpf(__uint_as_float(v & 0xFFFF0000u), sh)));
+            }
+        }
+        const HeadPlanes hp = head_planes<D>(a, h);
+        int cur_seg = -1;
+        float cmul = 0.0f;
+        // per segment: s_K folds into the logit multiplier; the accumulator moves to
+        // units of the segment's s_V (an all-zero V chunk has s_V = 0 and contributes
+        // nothing: keep the current units)
+        auto enter_segment = [&](int sg) {
+          if (sg == cur_seg) return;
+          cur_seg = sg;
+          const int slot = a.seg[sg].scale_slot;
+          const float sk = a.scale_table[2 * slot];
+          const float sv = a.scale_table[2 * slot + 1];
+          cmul = a.sm_scale_log2 * sk * cq;
+          if (sv > 0.0f) {
+            const float r = vunit / sv;
+  #pragma unroll
+            for (int db = 0; db < D / 32; ++db) acc[db] *= r;
+            vunit = sv;
+          }
+        };
+
+        // full tiles [r0, f1), software-pipelined: tile i in LDS buffer (i - r0) % 2,
+        // the packed bytes of tile i+1 in registers.  Past the range's last tile the
+        // pipeline re-stages the last one into the free buffer (never read).
+        const int f1 = min(r1, a.n_cfull);
+        if (r0 < f1) {
+          int cs, ck;
+          nth_full(a, r0, cs, ck);
+          Packed<D> pk;
+          load_packed<D>(hp, uint32_t(a.seg[cs].tok0 + ck), kBN, pk);
+          dequant_store<D>(pk, Ks[0], Vs[0]);
+          int ns = cs, nk = ck;
+          bool have_next = r0 + 1 < f1 && next_full(a, ns, nk);
+          int ltok = have_next ? a.seg[ns].tok0 + nk : a.seg[cs].tok0 + ck;
+          load_packed<D>(hp, uint32_t(ltok), kBN, pk);
+          __syncthreads();
+          int buf = 0;
+          for (int i = r0;; ++i) {
+            enter_segment(cs);
+            qk_tile<D, false>(Ks[buf], qr, s);
+            // stage tile i+1 while the MFMAs run, then fetch the bytes of tile i+2
+            dequant_store<D>(pk, Ks[buf ^ 1], Vs[buf ^ 1]);
+            int s2 = ns, k2 = nk;
+            const bool have_n2 = have_next && i + 2 < f1 && next_full(a, s2, k2);
+            if (have_n2) ltok = a.seg[s2].tok0 + k2;
+            load_packed<D>(hp, uint32_t(ltok), kBN, pk);
+            softmax_pv<D, false>(Vs[buf], s, cmul, kBN, sm, acc);
+            __syncthreads();
+            if (!have_next) break;
+            buf ^= 1;
+            cs = ns;
+            ck = nk;
+            ns = s2;
+            nk = k2;
+            have_next = have_n2;
+          }
+        }
+        // ragged tails, one at a time
+        const int c1 = min(r1, cache_tiles) - a.n_cfull;
+        for (int i = max(r0, a.n_cfull) - a.n_cfull; i < c1; ++i) {
+          const int cs = nth_tail(a, i);
+          const int tn = a.seg[cs].ntok % kBN;
+          const int ck = a.seg[cs].ntok - tn;
+          Packed<D> pk;
+          load_packed<D>(hp, uint32_t(a.seg[cs].tok0 + ck), tn, pk);
+          dequant_store<D>(pk, Ks[0], Vs[0]);
+          enter_segment(cs);
+          __syncthreads();
+          qk_tile<D, false>(Ks[0], qr, s);
+          softmax_pv<D, true>(Vs[0], s, cmul, tn, sm, acc);
+          __syncthreads();
+        }
       }
+
+      // ---- own segment (bf16 K/V of the chunk itself): full tiles pipelined like the
+      // cache, then the ragged tail
+      if (r1 > cache_tiles) {
+        load_q<D>(a, h, q0, qr);   // plain bf16 Q
+        const float cmul = a.sm_scale_log2;
+  #pragma unroll
+        for (int db = 0; db < D / 32; ++db) acc[db] *= vunit;   // to s_V = 1 units
+        vunit = 1.0f;
+        const int o0 = max(r0 - cache_tiles, 0), o1 = r1 - cache_tiles;
+        const int e = min(o1, a.n_ofull);
+        if (o0 < e) {
+          uint4 rk[2];
+          uint32_t rv[8];
+          load_own_k<D>(a, h, o0 * kBN, kBN, rk);
+          load_own_v<D>(a, h, o0 * kBN, kBN, rv);
+          store_own_k<D>(rk, Ks[0]);
+          store_own_v<D>(rv, Vs[0]);
+          load_own_v<D>(a, h, min(o0 + 1, e - 1) * kBN, kBN, rv);
+          __syncthreads();
+          int buf = 0;
+          for (int t = o0; t < e; ++t) {
+            // K of tile t+1 is fetched at the top of the iteration (its latency runs
+            // under the QK^T MFMAs); V of tile t+1 was fetched one iteration ahead
+            load_own_k<D>(a, h, min(t + 1, e - 1) * kBN, kBN, rk);
+            qk_tile<D, true>(Ks[buf], qr, s);
+            store_own_v<D>(rv, Vs[buf ^ 1]);
+            store_own_k<D>(rk, Ks[buf ^ 1]);
+            load_own_v<D>(a, h, min(t + 2, e - 1) * kBN, kBN, rv);
+            softmax_pv<D, false>(Vs[buf], s, cmul, kBN, sm, acc);
+            __syncthreads();
+            buf ^= 1;
+          }
+        }
+        if (o1 > a.n_ofull) {
+          const int nval = a.n_q - a.n_ofull * kBN;
+          uint4 rk[2];
+          uint32_t rv[8];
+          load_own_k<D>(a, h, a.n_ofull * kBN, nval, rk);
+          load_own_v<D>(a, h, a.n_ofull * kBN, nval, rv);
+          store_own_k<D>(rk, Ks[0]);
+          store_own_v<D>(rv, Vs[0]);
+          __syncthreads();
+          qk_tile<D, true>(Ks[0], qr, s);
+          softmax_pv<D, true>(Vs[0], s, cmul, nval, sm, acc);
+        }
+      }
+
+      if (r1 == T || t0 > 0) break;
+      if (tid == 0) {
+        const int gl = owner_of(b64 * WB + WB - last_w, U, G);
+        bool ready = true;
+        for (int gg = g + 1; gg <= gl && ready; ++gg) {
+          int spin = 0;
+          while (__hip_atomic_load(a.flags + gg, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != a.epoch) {
+            if (spin++ >= a.spin_limit) {
+              ready = false;
+              break;
+            }
+            __builtin_amdgcn_s_sleep(8);
+          }
+        }
+        // acquire: drops stale copies of the partials from this XCD's L2 and the L1
+        if (ready) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+        s_ready = ready;
+      }
+      __syncthreads();
+      if (s_ready) break;
+      r0 = r1;
+      r1 = T;
+    }
+
+    if (t0 > 0) {
+      // ---- not the block's first tiles: publish this range's partial result for the
+      // workgroup that owns the block's start (the partial lives in this workgroup's
+      // slot; its flag carries the launch's epoch once the slot is complete)
+      store_partial<D>(a.partials + size_t(g) * kSlotFloats, acc, vunit, sm);
+      __builtin_amdgcn_s_waitcnt(0);   // every wave's stores are in this XCD's L2
+      __syncthreads();
+      if (tid == 0) {
+        // one release for the workgroup: writes the L2's dirty lines back to memory,
+        // where the merging workgroup (possibly on another XCD) reads them
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+        __hip_atomic_store(a.flags + g, a.epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+    } else if (r1 < T) {
+      // ---- the block's first tiles, the rest done by workgroups g+1..gl (each of them
+      // as its first range, published long before this point): merge their partials
+      // with the registers, in workgroup order
+      const int gl = owner_of(b64 * WB + WB - last_w, U, G);   // holds the block's last tile
+      float mx = sm.m;
+      for (int gg = g + 1; gg <= gl; ++gg)
+        mx = fmaxf(mx, a.partials[size_t(gg) * kSlotFloats + kBM * D + 2 * tid]);
+      const float f0 = __builtin_amdgcn_exp2f(sm.m - mx);
+      float lsum = sm.l * f0;
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db) acc[db] *= vunit * f0;
+      for (int gg = g + 1; gg <= gl; ++gg) {
+        // issue every load of the partial before using any (one round trip, not 2 per 16 B)
+        const float *ps = a.partials + size_t(gg) * kSlotFloats;
+        float4 o[D / 32][4];
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+          for (int gq = 0; gq < 4; ++gq)
+            o[db][gq] = *reinterpret_cast<const float4 *>(ps + ((db * 4 + gq) * Cfg<D>::kThreads + tid) * 4);
+        const float2 ml = *reinterpret_cast<const float2 *>(ps + kBM * D + 2 * tid);
+        const float f = __builtin_amdgcn_exp2f(ml.x - mx);
+        lsum += ml.y * f;
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+          for (int gq = 0; gq < 4; ++gq) {
+            acc[db][4 * gq] += o[db][gq].x * f;
+            acc[db][4 * gq + 1] += o[db][gq].y * f;
+            acc[db][4 * gq + 2] += o[db][gq].z * f;
+            acc[db][4 * gq + 3] += o[db][gq].w * f;
+          }
+      }
+      write_out<D>(a, h, qi, acc, 1.0f / (lsum + __shfl_xor(lsum, 32, 64)));
+    } else {
+      // ---- the whole block here (or its rest, after giving up waiting)
+      write_out<D>(a, h, qi, acc, vunit / (sm.l + __shfl_xor(sm.l, 32, 64)));
+    }
+    __syncthreads();   // LDS buffers and s_ready are reused by the next range
   }
 }
 
+namespace {
+int g_attn_cus[64];
+
+int attn_cu_count() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return kAttnMaxCus;
+  if (g_attn_cus[dev] == 0) {
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+      return kAttnMaxCus;
+    g_attn_cus[dev] = cus;
+  }
+  return g_attn_cus[dev];
+}
+
+template <int D>
+int launch_attention_d(AttnArgs a, hipStream_t s) {
+  if (!a.partials || !a.flags) return NVFP4KV_EINVAL;
+  int nf = 0, nt = 0;
+  for (int i = 0; i < a.n_seg; ++i) {
+    nf += a.seg[i].ntok / kBN;
+    nt += a.seg[i].ntok % kBN ? 1 : 0;
+  }
+  a.n_cfull = nf;
+  a.n_ctail = nt;
+  a.n_ofull = a.n_q / kBN;
+  a.n_otail = a.n_q % kBN ? 1 : 0;
+  a.tiles = nf + nt + a.n_ofull + a.n_otail;
+  // measured relative costs: a pipelined NVFP4 tile 16, a pipelined bf16 own tile 20
+  // (its V is transposed in registers), a ragged tail 28 (not pipelined)
+  a.w_cfull = 16;
+  a.w_ofull = 20;
+  a.w_tail = 28;
+  const int64_t wb = int64_t(nf) * a.w_cfull + int64_t(nt + a.n_otail) * a.w_tail + int64_t(a.n_ofull) * a.w_ofull;
+  if (wb >= (int64_t(1) << 31)) return NVFP4KV_EINVAL;
+  a.w_block = int32_t(wb);
+  const int64_t blocks = int64_t((a.n_q + Cfg<D>::kBM - 1) / Cfg<D>::kBM) * a.H;
+  if (blocks >= (int64_t(1) << 31)) return NVFP4KV_EINVAL;
+  if (blocks * wb >= (int64_t(1) << 52)) return NVFP4KV_EINVAL;   // share bounds U g / G in int64
+  a.work = blocks * wb;
+  // one workgroup per resident slot (every CU busy), each with an equal share of the
+  // weighted work; every share must hold at least one tile start
+  int64_t grid = int64_t(min(attn_cu_count(), kAttnMaxCus)) * Cfg<D>::kWgPerCu;
+  const int64_t wmax = a.w_tail;   // the largest weight
+  if (grid > a.work / wmax) grid = a.work / wmax;
+  if (grid < 1) grid = 1;
+  hipLaunchKernelGGL(chunk_attention_kernel<D>, dim3(unsigned(grid)), dim3(Cfg<D>::kThreads), 0, s, a);
+  return NVFP4KV_HIP_OK(hipGetLastError());
+}
+}  // namespace
+
 int launch_attention(const AttnArgs &a, void *stream) {
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  if (a.D == 128) {
-    const int64_t nblk = int64_t((a.n_q + Cfg<128>::kBM - 1) / Cfg<128>::kBM) * a.H;
-    if (nblk >= (int64_t(1) << 31)) return NVFP4KV_EINVAL;
-    hipLaunchKernelGGL(chunk_attention_kernel<128>, dim3(unsigned(nblk)), dim3(Cfg<128>::kThreads), 0, s, a);
-  } else if (a.D == 64) {
-    const int64_t nblk = int64_t((a.n_q + Cfg<64>::kBM - 1) / Cfg<64>::kBM) * a.H;
-    if (nblk >= (int64_t(1) << 31)) return NVFP4KV_EINVAL;
-    hipLaunchKernelGGL(chunk_attention_kernel<64>, dim3(unsigned(nblk)), dim3(Cfg<64>::kThreads), 0, s, a);
-  } else {
-    return NVFP4KV_EINVAL;
-  }
-  return NVFP4KV_HIP_OK(hipGetLastError());
+  if (a.D == 128) return launch_attention_d<128>(a, s);
+  if (a.D == 64) return launch_attention_d<64>(a, s);
+  return NVFP4KV_EINVAL;
 }
 
 }  // namespace nvfp4kv

@@ -60,6 +60,23 @@ struct Segment {
   int32_t pad;
 };
 
+// Attention load balancing.  The key tiles of all (head, query block) pairs form one
+// list of work units that is cut into equal ranges, one per workgroup.  A query block
+// cut between workgroups g < g+1 < ... is finished by g, which holds its first tiles
+// and processes them last: every later workgroup holds a later part as its first
+// range, publishes the partial result in its slot and tags its flag with the
+// launch's epoch.  Scratch (in the cache's storage): one slot and one flag per
+// workgroup (flags start zeroed; epochs never repeat).
+constexpr int kAttnMaxCus = 256;
+constexpr int attn_wg_per_cu(int D) { return D >= 128 ? 1 : 2; }
+constexpr int attn_max_grid(int D) { return kAttnMaxCus * attn_wg_per_cu(D); }
+constexpr int attn_block_queries(int D) { return (D >= 128 ? 8 : 4) * 32; }
+constexpr int attn_threads(int D) { return (D >= 128 ? 8 : 4) * 64; }
+// one partial: the query block's unnormalized output (fp32) + per-lane max and sum
+constexpr size_t attn_slot_bytes(int D) {
+  return size_t(attn_block_queries(D)) * D * 4 + size_t(attn_threads(D)) * 8;
+}
+
 struct AttnArgs {
   const uint16_t *q, *k_own, *v_own;
   float *out;
@@ -69,7 +86,19 @@ struct AttnArgs {
   int32_t H, D, n_q;
   float sm_scale_log2;                                    // softmax_scale * log2(e)
   int32_t n_seg;
+  // set by the launcher: key tiles per query block, by kind (cache full tiles, cache
+  // ragged tails, own full tiles, own ragged tail), and the total work
+  int32_t n_cfull, n_ctail, n_ofull, n_otail, tiles;
+  // cost weights of a cache full tile, a ragged tail and an own full tile; a block's
+  // total weight; the work list is cut by weight
+  int32_t w_cfull, w_tail, w_ofull, w_block;
   int32_t pad;
+  int64_t work;               // query blocks x block weight
+  float *partials;            // [max grid][slot]
+  uint64_t *flags;            // [max grid]: epoch of the last partial published in the slot
+  uint64_t epoch;             // > 0, never repeated for one scratch area
+  int32_t spin_limit;         // polls before a workgroup stops waiting for a partial
+  int32_t pad2;
   Segment seg[kMaxSegments];
 };
 

@@ -40,7 +40,7 @@ def lib():
         sig = {
             "nvfp4kv_strerror": (ctypes.c_char_p, [I]),
             "nvfp4kv_version": (ctypes.c_char_p, []),
-            "nvfp4kv_set_quantize_spin_limit": (I, [ctypes.c_int32]),
+            "nvfp4kv_set_wait_limit": (I, [ctypes.c_int32]),
             "nvfp4_quantize_workspace_bytes": (SZ, []),
             "nvfp4_quantize_kv": (I, [P, I64, I64, I64, P, P, P, P, SZ, P]),
             "kvcache_storage_bytes": (SZ, [ctypes.POINTER(KVCacheConfig)]),
@@ -71,10 +71,11 @@ def _check(rc, where):
         raise NVFP4KVError(rc, where)
 
 
-def set_quantize_spin_limit(limit):
-    """Testing hook: polls the single-pass append quantizer makes before it computes
-    the tensor maxima by a scan of its own (same result either way)."""
-    _check(lib().nvfp4kv_set_quantize_spin_limit(int(limit)), "nvfp4kv_set_quantize_spin_limit")
+def set_wait_limit(limit):
+    """Testing hook: polls the bounded waits between workgroups make (the append
+    quantizer's maxima exchange, the attention's partial-result merge) before taking
+    their fallback paths (same results either way)."""
+    _check(lib().nvfp4kv_set_wait_limit(int(limit)), "nvfp4kv_set_wait_limit")
 
 
 def _stream():

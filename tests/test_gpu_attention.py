@@ -178,3 +178,22 @@ def test_streaming_rollout(ops):
             assert np.array_equal(got[0], want[0]), f"chunk {c} {what} codes"
             assert np.array_equal(got[1], want[1]), f"chunk {c} {what} scales"
             assert np.float32(got[2]) == want[2], f"chunk {c} {what} tensor scale"
+
+
+@pytest.mark.parametrize("D", [64, 128])
+def test_cut_blocks_wait_fallback(ops, D):
+    """Small problems spread one query block over many workgroups (one key tile
+    each).  With a zero wait limit the workgroup holding a block's first tiles
+    stops waiting for missing partial results at once and processes the block's
+    remaining tiles itself; both paths must match the oracle."""
+    rng = np.random.default_rng(40 + D)
+    H, T_f, sink, window, n_q = 2, 40, 2, 5, 300
+    chunks = [(rand_bits(rng, (H, nf * T_f, D)), rand_bits(rng, (H, nf * T_f, D))) for nf in (2, 3, 2, 1)]
+    cache, model = build_both(ops, H, D, T_f, sink, window, chunks)
+    q, ko, vo = (rand_bits(rng, (H, n_q, D)) for _ in range(3))
+    try:
+        for limit in (0, 1 << 16, 0):
+            ops.set_wait_limit(limit)
+            run_case(ops, cache, model, q, ko, vo, 1.0 / np.sqrt(D), what=f"D{D} wait limit {limit}")
+    finally:
+        ops.set_wait_limit(1 << 16)

@@ -170,18 +170,18 @@ def test_append_wait_fallback_scan(ops):
               for s in (1.0, 1e-20, 3e5)]
     results = []
     for limit in (0, 1 << 16):
-        ops.set_quantize_spin_limit(limit)
+        ops.set_wait_limit(limit)
         try:
             cache = ops.KVCache(H, D, T_f, 2, 4)
             for k, v in chunks:
                 cache.append(dev(k), dev(v), 2)
             results.append([tuple(host(t) for t in cache.export_chunk(c)) for c in range(3)])
         finally:
-            ops.set_quantize_spin_limit(1 << 16)
+            ops.set_wait_limit(1 << 16)
     for c, (k, v) in enumerate(chunks):
         for r in results:
             kc, ks, vc, vs, sk, sv = r[c]
             assert_codec_equal((kc, ks, sk[0]), quantize_ref(k), f"chunk {c} K")
             assert_codec_equal((vc, vs, sv[0]), quantize_ref(v), f"chunk {c} V")
     with pytest.raises(ops.NVFP4KVError):
-        ops.set_quantize_spin_limit(-1)
+        ops.set_wait_limit(-1)

@@ -89,13 +89,24 @@ def test_error_paths_before_device_work(real):
 
 def test_storage_bytes_budget(real):
     """9/16 byte per cached element for each of K and V (reading note: 9/8 T_c H d
-    bytes for K and V), plus a small fixed table and workspace."""
+    bytes for K and V), plus scratch of a fixed size that does not grow with the
+    cache: the tensor-scale table, the quantizer workspace, and the attention
+    load-balancing slots (one partial query-block result, fp32 output plus per-lane
+    max and sum, and one 8-byte flag per workgroup of a 256-CU launch)."""
     real.kvcache_storage_bytes.restype = ctypes.c_size_t
     real.kvcache_storage_bytes.argtypes = [ctypes.POINTER(Cfg)]
-    cfg = Cfg(12, 128, 1560, 3, 9)
-    n = real.kvcache_storage_bytes(ctypes.byref(cfg))
-    elems = 12 * 128 * 1560 * 12
-    assert 2 * elems * 9 // 16 <= n <= 2 * elems * 9 // 16 + 64 * 1024
+    for D, queries, threads, wgs in ((128, 256, 512, 256), (64, 128, 256, 512)):
+        attn = wgs * (queries * D * 4 + threads * 8 + 8)
+        fixed = None
+        for sink, window in ((3, 9), (6, 18)):
+            cfg = Cfg(12, D, 1560, sink, window)
+            n = real.kvcache_storage_bytes(ctypes.byref(cfg))
+            elems = 12 * D * 1560 * (sink + window)
+            rest = n - 2 * elems * 9 // 16
+            assert attn <= rest <= attn + 64 * 1024, (D, sink, window)
+            if fixed is not None:
+                assert rest == fixed      # independent of the cache length
+            fixed = rest
 
 
 # ------------------------------------------------------------ host stub
