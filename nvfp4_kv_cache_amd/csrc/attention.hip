@@ -43,12 +43,14 @@
 //  * Work distribution (stream-K style): the (query block, key tile) pairs of all
 //    heads form one list, weighted by the measured cost of each tile kind, that is
 //    cut into one equal share per resident workgroup (every CU busy, whatever the
-//    number of query blocks).  A share usually ends inside a query block; the
-//    workgroup holding the block's first tiles processes them last in its share and
-//    merges the partial results (unnormalized output, running max, row sum) that
-//    the workgroups holding the rest published as their first work, long before.
-//    Partials pass through memory with one L2 write-back per publishing workgroup
-//    and one invalidate per merging workgroup (each XCD has its own L2); the wait
+//    number of query blocks).  A share usually ends inside a query block.  Each
+//    workgroup walks its share from the end, so it starts at key tile 0 of its last
+//    block (keeping all workgroups of a head in step, for L2 reuse) and publishes
+//    that range's partial result (unnormalized output, running max, row sum); the
+//    workgroup holding a cut block's last tiles processes them last and merges the
+//    partials, published long before.
+//    Partials pass through memory (each XCD has its own L2): one L2 write-back per
+//    publishing workgroup, device-scope reads by the merging one; the wait
 //    for a partial is bounded, after which the merging workgroup processes the
 //    block's remaining tiles itself.
 //  * Workgroups are numbered so that each XCD (own L2) runs a contiguous run of
@@ -499,6 +501,14 @@ __device__ __forceinline__ void store_partial(float *ps, const f32x16 (&acc)[D /
   *reinterpret_cast<float2 *>(ps + Cfg<D>::kBM * D + 2 * tid) = make_float2(sm.m, sm.l);
 }
 
+// Device-scope (sc1) 64-bit read: coherent across XCDs without invalidating the
+// reader's L2, which holds the K/V tiles every workgroup on that XCD is streaming.
+__device__ __forceinline__ float2 get_pair(const float *p) {
+  const uint64_t v = __hip_atomic_load(reinterpret_cast<const uint64_t *>(p), __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_AGENT);
+  return make_float2(__uint_as_float(uint32_t(v)), __uint_as_float(uint32_t(v >> 32)));
+}
+
 template <int D>
 __device__ __forceinline__ void write_out(const AttnArgs &a, int h, int qi, const f32x16 (&acc)[D / 32],
                                           float fin) {
@@ -534,23 +544,26 @@ __global__ __launch_bounds__(Cfg<D>::kThreads, Cfg<D>::kWgPerCu) void chunk_atte
   const int G = gridDim.x, bid = blockIdx.x;
   const int xcd = bid & 7;
   const int g = xcd * (G >> 3) + min(xcd, G & 7) + (bid >> 3);
-  // this workgroup's share [u, uend) of the weighted list of all (query block, key
+  // this workgroup's share [ubeg, u) of the weighted list of all (query block, key
   // tile) pairs; it processes the tiles that start inside its share (every share is
-  // at least one tile long, so every workgroup has tiles)
+  // at least one tile long, so every workgroup has tiles), one query block at a time
+  // from the share's END: a share usually holds the first tiles of one block and the
+  // last tiles of the one before, so every workgroup starts at key tile 0 and all
+  // workgroups of a head stay within a few tiles of each other (their K/V stays in
+  // L2).
   const int64_t U = a.work;
   const int T = a.tiles, WB = a.w_block;
   const int cache_tiles = a.n_cfull + a.n_ctail;
   const int qblocks = (a.n_q + kBM - 1) / kBM;
-  const int last_w = a.n_otail ? a.w_tail : a.w_ofull;   // weight of a block's last tile
-  int64_t u = U * g / G;
-  const int64_t uend = U * (g + 1) / G;
+  const int64_t ubeg = U * g / G;
+  int64_t u = U * (g + 1) / G;
 
-  while (u < uend) {
-    const int64_t b64 = u / WB;
+  while (u > ubeg) {
+    const int64_t b64 = (u - 1) / WB;
     const int b = int(b64);
-    const int p0 = int(u - b64 * WB);
-    const int p1 = int(min(int64_t(WB), int64_t(p0) + (uend - u)));
-    u = b64 * WB + p1;
+    const int p1 = int(u - b64 * WB);
+    const int p0 = int(max(ubeg - b64 * WB, int64_t(0)));
+    u = b64 * WB + p0;
     const int t0 = tiles_before(a, p0), t1 = tiles_before(a, p1);
     if (t0 == t1) continue;
     const int h = b / qblocks;
@@ -724,11 +737,13 @@ __global__ __launch_bounds__(Cfg<D>::kThreads, Cfg<D>::kWgPerCu) void chunk_atte
         }
       }
 
-      if (r1 == T || t0 > 0) break;
+      if (r0 == 0 || t1 < T) break;
+      // the block's last tiles, its first ones done by workgroups gf..g-1 (each as
+      // the first range it processed): wait, bounded, for their partials
       if (tid == 0) {
-        const int gl = owner_of(b64 * WB + WB - last_w, U, G);
+        const int gf = owner_of(b64 * WB, U, G);
         bool ready = true;
-        for (int gg = g + 1; gg <= gl && ready; ++gg) {
+        for (int gg = gf; gg < g && ready; ++gg) {
           int spin = 0;
           while (__hip_atomic_load(a.flags + gg, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != a.epoch) {
             if (spin++ >= a.spin_limit) {
@@ -738,19 +753,17 @@ __global__ __launch_bounds__(Cfg<D>::kThreads, Cfg<D>::kWgPerCu) void chunk_atte
             __builtin_amdgcn_s_sleep(8);
           }
         }
-        // acquire: drops stale copies of the partials from this XCD's L2 and the L1
-        if (ready) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
         s_ready = ready;
       }
       __syncthreads();
       if (s_ready) break;
-      r0 = r1;
-      r1 = T;
+      r1 = r0;   // one is still missing: process the block's first tiles here
+      r0 = 0;
     }
 
-    if (t0 > 0) {
-      // ---- not the block's first tiles: publish this range's partial result for the
-      // workgroup that owns the block's start (the partial lives in this workgroup's
+    if (t1 < T) {
+      // ---- not the block's last tiles: publish this range's partial result for the
+      // workgroup that holds the block's end (the partial lives in this workgroup's
       // slot; its flag carries the launch's epoch once the slot is complete)
       store_partial<D>(a.partials + size_t(g) * kSlotFloats, acc, vunit, sm);
       __builtin_amdgcn_s_waitcnt(0);   // every wave's stores are in this XCD's L2
@@ -761,43 +774,45 @@ __global__ __launch_bounds__(Cfg<D>::kThreads, Cfg<D>::kWgPerCu) void chunk_atte
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
         __hip_atomic_store(a.flags + g, a.epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
-    } else if (r1 < T) {
-      // ---- the block's first tiles, the rest done by workgroups g+1..gl (each of them
-      // as its first range, published long before this point): merge their partials
-      // with the registers, in workgroup order
-      const int gl = owner_of(b64 * WB + WB - last_w, U, G);   // holds the block's last tile
+    } else if (r0 > 0) {
+      // ---- the block's last tiles: merge the partials of workgroups gf..g-1 with the
+      // registers, in workgroup order
+      const int gf = owner_of(b64 * WB, U, G);   // holds the block's first tile
       float mx = sm.m;
-      for (int gg = g + 1; gg <= gl; ++gg)
-        mx = fmaxf(mx, a.partials[size_t(gg) * kSlotFloats + kBM * D + 2 * tid]);
+      for (int gg = gf; gg < g; ++gg)
+        mx = fmaxf(mx, get_pair(a.partials + size_t(gg) * kSlotFloats + kBM * D + 2 * tid).x);
       const float f0 = __builtin_amdgcn_exp2f(sm.m - mx);
       float lsum = sm.l * f0;
 #pragma unroll
       for (int db = 0; db < D / 32; ++db) acc[db] *= vunit * f0;
-      for (int gg = g + 1; gg <= gl; ++gg) {
+      for (int gg = gf; gg < g; ++gg) {
         // issue every load of the partial before using any (one round trip, not 2 per 16 B)
         const float *ps = a.partials + size_t(gg) * kSlotFloats;
-        float4 o[D / 32][4];
+        float2 o[D / 32][4][2];
 #pragma unroll
         for (int db = 0; db < D / 32; ++db)
 #pragma unroll
-          for (int gq = 0; gq < 4; ++gq)
-            o[db][gq] = *reinterpret_cast<const float4 *>(ps + ((db * 4 + gq) * Cfg<D>::kThreads + tid) * 4);
-        const float2 ml = *reinterpret_cast<const float2 *>(ps + kBM * D + 2 * tid);
+          for (int gq = 0; gq < 4; ++gq) {
+            const float *p = ps + ((db * 4 + gq) * Cfg<D>::kThreads + tid) * 4;
+            o[db][gq][0] = get_pair(p);
+            o[db][gq][1] = get_pair(p + 2);
+          }
+        const float2 ml = get_pair(ps + kBM * D + 2 * tid);
         const float f = __builtin_amdgcn_exp2f(ml.x - mx);
         lsum += ml.y * f;
 #pragma unroll
         for (int db = 0; db < D / 32; ++db)
 #pragma unroll
           for (int gq = 0; gq < 4; ++gq) {
-            acc[db][4 * gq] += o[db][gq].x * f;
-            acc[db][4 * gq + 1] += o[db][gq].y * f;
-            acc[db][4 * gq + 2] += o[db][gq].z * f;
-            acc[db][4 * gq + 3] += o[db][gq].w * f;
+            acc[db][4 * gq] += o[db][gq][0].x * f;
+            acc[db][4 * gq + 1] += o[db][gq][0].y * f;
+            acc[db][4 * gq + 2] += o[db][gq][1].x * f;
+            acc[db][4 * gq + 3] += o[db][gq][1].y * f;
           }
       }
       write_out<D>(a, h, qi, acc, 1.0f / (lsum + __shfl_xor(lsum, 32, 64)));
     } else {
-      // ---- the whole block here (or its rest, after giving up waiting)
+      // ---- the whole block here (or all of it after giving up waiting)
       write_out<D>(a, h, qi, acc, vunit / (sm.l + __shfl_xor(sm.l, 32, 64)));
     }
     __syncthreads();   // LDS buffers and s_ready are reused by the next range
