@@ -98,11 +98,17 @@ int nvfp4_quantize_kv(const uint16_t *x, int64_t H, int64_t T, int64_t D, uint8_
  *
  * A frame slot holds one latent frame (tokens_per_frame tokens, all heads) of K and V
  * in NVFP4.  Slots [0, sink_frames) hold the global sink: the first sink_frames frames
- * ever appended, kept for the life of the cache.  The other window_frames slots form a
- * FIFO ring of the most recent frames.  Eviction only changes host metadata.
+ * ever appended, kept for the life of the cache.  The window is a FIFO of the
+ * window_frames most recent other frames.  The shot-level sink (paper section 4.2,
+ * "Multi-Shot Attention Sink") is the first shot_frames frames of the current shot:
+ * such a frame stays in the cache when the window rolls past it, until the next
+ * scene cut (kvcache_begin_shot), and is never stored or attended twice.  The first
+ * shot starts at the first frame.  The effective key set is global sink U shot-level
+ * sink U window.  Frames are never copied; eviction only changes host metadata.
  *
  * Supported: n_heads >= 1; head_dim 64 or 128; tokens_per_frame >= 8 and a multiple
- * of 8; sink_frames >= 0; window_frames >= 1; sink_frames + window_frames <= 64.
+ * of 8; sink_frames >= 0; window_frames >= 1; shot_frames >= 0 (0: no shot-level
+ * sink); sink_frames + window_frames + shot_frames <= 64.
  * Every bf16 / fp32 tensor argument must be 16-byte aligned.
  * ------------------------------------------------------------------------------ */
 typedef struct {
@@ -111,6 +117,7 @@ typedef struct {
   int32_t tokens_per_frame;
   int32_t sink_frames;
   int32_t window_frames;
+  int32_t shot_frames;
 } kvcache_config;
 
 typedef struct kvcache kvcache; /* opaque host object */
@@ -146,8 +153,21 @@ int kvcache_append(kvcache *c, const uint16_t *k, const uint16_t *v, int32_t n_f
  * Errors: EINVAL (n_frames < 0), ESTATE (fewer than n_frames window frames). */
 int kvcache_evict(kvcache *c, int32_t n_frames);
 
-/* Number of cached tokens in the sink and in the window (host outputs). */
+/* Number of cached tokens in the global sink and in the window (host outputs). */
 int kvcache_tokens(const kvcache *c, int64_t *sink_tokens, int64_t *window_tokens);
+
+/* Scene cut: the next appended frame starts a new shot, whose first shot_frames
+ * frames form the new shot-level sink.  The old shot's sink frames that are no
+ * longer in the window leave the cache (metadata only).  Errors: EINVAL (null). */
+int kvcache_begin_shot(kvcache *c);
+
+/* The shot-level sink as its two pointers (host outputs): start_frame, the index of
+ * the current shot's first frame among all frames ever appended, and n_frames, how
+ * many of its first shot_frames frames have been appended; extra_tokens, the tokens
+ * of those frames that are in neither the global sink nor the window (attended in
+ * addition to kvcache_tokens' two counts).  Errors: EINVAL (null). */
+int kvcache_shot_sink(const kvcache *c, int64_t *start_frame, int32_t *n_frames,
+                      int64_t *extra_tokens);
 
 /* Number of chunks appended so far (the next chunk's index) (host output). */
 int kvcache_chunk_count(const kvcache *c, int32_t *n_chunks);

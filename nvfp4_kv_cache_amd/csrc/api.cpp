@@ -40,10 +40,10 @@ bool config_ok(const kvcache_config *c) {
   if (c->tokens_per_frame < 8 || c->tokens_per_frame % 8 != 0 ||
       c->tokens_per_frame > (1 << 20))
     return false;
-  if (c->sink_frames < 0 || c->window_frames < 1) return false;
-  if (c->sink_frames + c->window_frames > kMaxFrames) return false;
+  if (c->sink_frames < 0 || c->window_frames < 1 || c->shot_frames < 0) return false;
+  if (c->sink_frames + c->window_frames + c->shot_frames > kMaxFrames) return false;
   // per-head planes are addressed with 32-bit offsets
-  if (int64_t(c->sink_frames + c->window_frames) * c->tokens_per_frame * c->head_dim >=
+  if (int64_t(c->sink_frames + c->window_frames + c->shot_frames) * c->tokens_per_frame * c->head_dim >=
       (int64_t(1) << 31))
     return false;
   return true;
@@ -52,7 +52,7 @@ bool config_ok(const kvcache_config *c) {
 bool make_layout(const kvcache_config *c, Layout *L) {
   if (!config_ok(c)) return false;
   const int64_t H = c->n_heads, D = c->head_dim;
-  L->rows = int64_t(c->sink_frames + c->window_frames) * c->tokens_per_frame;
+  L->rows = int64_t(c->sink_frames + c->window_frames + c->shot_frames) * c->tokens_per_frame;
   if (H * L->rows * D > (int64_t(1) << 40)) return false;
   size_t off = 0;
   L->kcodes = off;  off = round_up(off + size_t(H * L->rows * D / 2));
@@ -70,6 +70,7 @@ bool make_layout(const kvcache_config *c, Layout *L) {
 struct FrameRec {
   int32_t chunk;
   int32_t frame_in_chunk;
+  int64_t frame;              // index among all frames ever appended
 };
 
 struct ChunkRec {
@@ -79,12 +80,21 @@ struct ChunkRec {
   int32_t slot[kMaxFrames];   // slot of each frame, -1 once evicted
 };
 
+// Slots [0, sink_frames) hold the global sink.  The other slots form a pool shared by
+// the window (a FIFO of at most window_frames frames) and the shot-level sink: a
+// frame among the first shot_frames frames of the current shot keeps its slot after
+// it leaves the window, until the next scene cut.  The pool has window_frames +
+// shot_frames slots, which is always enough.
 struct State {
   int32_t sink_used = 0;
-  int32_t win_head = 0;       // ring position of the oldest window frame
+  int32_t win[kMaxFrames];    // window slots, oldest first, as a ring
+  int32_t win_head = 0;
   int32_t win_count = 0;
+  int64_t next_frame = 0;     // frames appended so far
+  int64_t shot_start = 0;     // first frame of the current shot
   int32_t next_chunk = 0;
   FrameRec slot_frame[kMaxFrames];
+  bool slot_used[kMaxFrames] = {false};   // pool slots holding a resident frame
   int32_t scale_ref[kScaleSlots] = {0};
   std::map<int32_t, ChunkRec> chunks;   // resident chunks only
 };
@@ -107,35 +117,67 @@ struct kvcache {
   QuantWorkspace *ws() const { return reinterpret_cast<QuantWorkspace *>(base + L.ws); }
   uint64_t *attn_flags() const { return reinterpret_cast<uint64_t *>(base + L.attn_flags); }
   float *attn_partials() const { return reinterpret_cast<float *>(base + L.attn_part); }
-  int32_t window_slot(const State &s, int32_t i) const {
-    return cfg.sink_frames + (s.win_head + i) % cfg.window_frames;
+  int32_t window_slot(const State &s, int32_t i) const { return s.win[(s.win_head + i) % kMaxFrames]; }
+  bool in_shot_sink(const State &s, int64_t frame) const {
+    return frame >= s.shot_start && frame < s.shot_start + cfg.shot_frames;
+  }
+  bool in_window(const State &s, int32_t slot) const {
+    for (int32_t i = 0; i < s.win_count; ++i)
+      if (window_slot(s, i) == slot) return true;
+    return false;
   }
 };
 
 namespace {
 
-// Drops the oldest n window frames of `s` (metadata only).
+// Frees a pool slot: its frame leaves the cache (metadata only).
+void release_slot(State &s, int32_t slot) {
+  const FrameRec fr = s.slot_frame[slot];
+  auto it = s.chunks.find(fr.chunk);
+  if (it != s.chunks.end()) {
+    ChunkRec &rec = it->second;
+    rec.slot[fr.frame_in_chunk] = -1;
+    rec.resident -= 1;
+    s.scale_ref[rec.scale_slot] -= 1;
+    if (rec.resident == 0) s.chunks.erase(it);
+  }
+  s.slot_used[slot] = false;
+}
+
+// Drops the oldest n window frames of `s`; a frame of the current shot-level sink
+// keeps its slot (it stays in the effective key set).
 void evict_oldest(const kvcache *c, State &s, int32_t n) {
   for (int32_t i = 0; i < n; ++i) {
     const int32_t slot = c->window_slot(s, 0);
-    const FrameRec fr = s.slot_frame[slot];
-    auto it = s.chunks.find(fr.chunk);
-    if (it != s.chunks.end()) {
-      ChunkRec &rec = it->second;
-      rec.slot[fr.frame_in_chunk] = -1;
-      rec.resident -= 1;
-      s.scale_ref[rec.scale_slot] -= 1;
-      if (rec.resident == 0) s.chunks.erase(it);
-    }
-    s.win_head = (s.win_head + 1) % c->cfg.window_frames;
+    s.win_head = (s.win_head + 1) % kMaxFrames;
     s.win_count -= 1;
+    if (!c->in_shot_sink(s, s.slot_frame[slot].frame)) release_slot(s, slot);
   }
 }
 
-// Resident frames in effective-key order: sinks, then the window oldest first.
+// Pool slots of shot-level-sink frames that are no longer in the window, in frame
+// order.
+int pinned_frames(const kvcache *c, const State &s, int32_t *slots) {
+  int n = 0;
+  const int32_t lo = c->cfg.sink_frames, hi = lo + c->cfg.window_frames + c->cfg.shot_frames;
+  for (int32_t sl = lo; sl < hi; ++sl)
+    if (s.slot_used[sl] && !c->in_window(s, sl)) slots[n++] = sl;
+  for (int i = 1; i < n; ++i)   // insertion sort by frame index (n <= 64)
+    for (int j = i; j > 0 && s.slot_frame[slots[j]].frame < s.slot_frame[slots[j - 1]].frame; --j) {
+      const int32_t t = slots[j];
+      slots[j] = slots[j - 1];
+      slots[j - 1] = t;
+    }
+  return n;
+}
+
+// Resident frames in effective-key order: global sink, shot-level-sink frames that
+// left the window (virtually prepended to it), then the window oldest first.  Each
+// frame appears once.
 int collect_frames(const kvcache *c, int32_t *slots) {
   int n = 0;
   for (int32_t i = 0; i < c->st.sink_used; ++i) slots[n++] = i;
+  n += pinned_frames(c, c->st, slots + n);
   for (int32_t i = 0; i < c->st.win_count; ++i) slots[n++] = c->window_slot(c->st, i);
   return n;
 }
@@ -255,21 +297,27 @@ int kvcache_append(kvcache *c, const uint16_t *k, const uint16_t *v, int32_t n_f
   rec.resident = n_frames;
   QuantArgs a;
   memset(&a, 0, sizeof(a));
+  const int32_t pool_lo = cfg.sink_frames, pool_hi = pool_lo + cfg.window_frames + cfg.shot_frames;
   for (int32_t f = 0; f < n_frames; ++f) {
     int32_t slot;
     if (f < to_sink) {
       slot = s.sink_used++;
     } else {
-      slot = c->window_slot(s, s.win_count);
+      slot = pool_lo;
+      while (slot < pool_hi && s.slot_used[slot]) ++slot;
+      if (slot == pool_hi) return NVFP4KV_ESTATE;   // unreachable: the pool is large enough
+      s.slot_used[slot] = true;
+      s.win[(s.win_head + s.win_count) % kMaxFrames] = slot;
       s.win_count += 1;
     }
-    s.slot_frame[slot] = FrameRec{cid, f};
+    s.slot_frame[slot] = FrameRec{cid, f, s.next_frame + f};
     rec.slot[f] = slot;
     a.frame_slot[f] = slot;
   }
   s.scale_ref[sslot] = n_frames;
   s.chunks[cid] = rec;
   s.next_chunk = cid + 1;
+  s.next_frame += n_frames;
 
   float *tab = c->table();
   a.t[0] = QuantTensor{k, c->kcodes(), c->kscales(), tab + 2 * sslot, 0, 0};
@@ -301,6 +349,29 @@ int kvcache_tokens(const kvcache *c, int64_t *sink_tokens, int64_t *window_token
   if (!c || !sink_tokens || !window_tokens) return NVFP4KV_EINVAL;
   *sink_tokens = int64_t(c->st.sink_used) * c->cfg.tokens_per_frame;
   *window_tokens = int64_t(c->st.win_count) * c->cfg.tokens_per_frame;
+  return NVFP4KV_OK;
+}
+
+int kvcache_begin_shot(kvcache *c) {
+  if (!c) return NVFP4KV_EINVAL;
+  State &s = c->st;
+  // the old shot's sink frames that already left the window leave the cache
+  int32_t pinned[kMaxFrames];
+  const int n = pinned_frames(c, s, pinned);
+  for (int i = 0; i < n; ++i) release_slot(s, pinned[i]);
+  s.shot_start = s.next_frame;
+  return NVFP4KV_OK;
+}
+
+int kvcache_shot_sink(const kvcache *c, int64_t *start_frame, int32_t *n_frames,
+                      int64_t *extra_tokens) {
+  if (!c || !start_frame || !n_frames || !extra_tokens) return NVFP4KV_EINVAL;
+  const State &s = c->st;
+  *start_frame = s.shot_start;
+  const int64_t seen = s.next_frame - s.shot_start;
+  *n_frames = int32_t(seen < c->cfg.shot_frames ? seen : c->cfg.shot_frames);
+  int32_t pinned[kMaxFrames];
+  *extra_tokens = int64_t(pinned_frames(c, s, pinned)) * c->cfg.tokens_per_frame;
   return NVFP4KV_OK;
 }
 

@@ -25,7 +25,7 @@ class NVFP4KVError(RuntimeError):
 class KVCacheConfig(ctypes.Structure):
     _fields_ = [("n_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
                 ("tokens_per_frame", ctypes.c_int32), ("sink_frames", ctypes.c_int32),
-                ("window_frames", ctypes.c_int32)]
+                ("window_frames", ctypes.c_int32), ("shot_frames", ctypes.c_int32)]
 
 
 def lib():
@@ -49,6 +49,9 @@ def lib():
             "kvcache_append": (I, [P, P, P, ctypes.c_int32, P]),
             "kvcache_evict": (I, [P, ctypes.c_int32]),
             "kvcache_tokens": (I, [P, ctypes.POINTER(I64), ctypes.POINTER(I64)]),
+            "kvcache_begin_shot": (I, [P]),
+            "kvcache_shot_sink": (I, [P, ctypes.POINTER(I64), ctypes.POINTER(ctypes.c_int32),
+                                      ctypes.POINTER(I64)]),
             "kvcache_chunk_count": (I, [P, ctypes.POINTER(ctypes.c_int32)]),
             "kvcache_chunk_frames": (I, [P, ctypes.c_int32, ctypes.POINTER(ctypes.c_int32)]),
             "chunk_attention": (I, [P, P, P, P, I64, F, P, P]),
@@ -121,8 +124,9 @@ class KVCache:
     """Sink + window NVFP4 KV cache on one device (see include/nvfp4kv.h)."""
 
     def __init__(self, n_heads, head_dim, tokens_per_frame, sink_frames, window_frames,
-                 device=None):
-        self.cfg = KVCacheConfig(n_heads, head_dim, tokens_per_frame, sink_frames, window_frames)
+                 device=None, shot_frames=0):
+        self.cfg = KVCacheConfig(n_heads, head_dim, tokens_per_frame, sink_frames, window_frames,
+                                 shot_frames)
         n = lib().kvcache_storage_bytes(ctypes.byref(self.cfg))
         if n == 0:
             raise ValueError("unsupported cache configuration")
@@ -166,6 +170,17 @@ class KVCache:
         s, w = ctypes.c_int64(), ctypes.c_int64()
         _check(lib().kvcache_tokens(self._h, ctypes.byref(s), ctypes.byref(w)), "kvcache_tokens")
         return s.value, w.value
+
+    def begin_shot(self):
+        """Scene cut: the next appended frame starts a new shot."""
+        _check(lib().kvcache_begin_shot(self._h), "kvcache_begin_shot")
+
+    def shot_sink(self):
+        """(start_frame, n_frames, extra_tokens) of the shot-level sink."""
+        st, n, ex = ctypes.c_int64(), ctypes.c_int32(), ctypes.c_int64()
+        _check(lib().kvcache_shot_sink(self._h, ctypes.byref(st), ctypes.byref(n), ctypes.byref(ex)),
+               "kvcache_shot_sink")
+        return st.value, n.value, ex.value
 
     def chunk_count(self):
         n = ctypes.c_int32()

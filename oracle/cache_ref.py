@@ -1,18 +1,26 @@
-"""Sink + sliding-window KV cache, as an ordered frame list (test infrastructure).
+"""Sink + sliding-window KV cache with a shot-level sink, as an ordered frame list
+(test infrastructure).
 
 Paper text, section 4.2 "Inference with Multi-Shot Attention Sink": inference
 keeps a sliding window of cached chunks (per-step cost O(W * L_c)); the global
-sink is the first S_g frames of the video, kept permanently; the effective key
-set is the union of the sink and the window with duplicate tokens removed.
-Reading note, "The inference infrastructure": each appended frame chunk is
-quantized to NVFP4 on its own (one tensor scale per chunk tensor).
+sink is the first S_g frames of the video, kept permanently; the shot-level sink
+is the first S_s frames of the current shot, re-bound at every scene cut, tracked
+by a (start, len) pair and kept once the window has rolled past it; the effective
+key set is the union of the global sink, the shot-level sink and the window, with
+duplicate tokens removed.  Reading note, "The inference infrastructure": each
+appended frame chunk is quantized to NVFP4 on its own (one tensor scale per chunk
+tensor).
 
-Model: the first ``sink_frames`` frames ever appended are sinks; every later
-frame joins a FIFO window of at most ``window_frames`` frames; when a frame
-arrives at a full window the oldest window frame leaves.  A sink frame is
-stored once and never enters the window, so the union is duplicate-free.  The
-effective key order is sinks, then window frames oldest first (attention is
-invariant to key order, so this order is a convention only).
+Model: frames are numbered in append order.  The first ``sink_frames`` frames are
+the global sink; every later frame joins a FIFO window of at most
+``window_frames`` frames; when a frame arrives at a full window the oldest window
+frame leaves the window.  A frame leaving the window stays (is "pinned") if its
+number lies in [shot_start, shot_start + shot_frames); ``begin_shot`` drops the
+pinned frames and moves shot_start to the next frame.  A global-sink frame is
+stored once and never enters the window, and a pinned frame is no longer in the
+window, so the union is duplicate-free.  The effective key order is global sink,
+pinned frames, window oldest first (attention is invariant to key order, so this
+order is a convention only).
 """
 
 from collections import deque
@@ -33,19 +41,38 @@ class Frame:
     v_scales: np.ndarray
     s_k: np.float32
     s_v: np.float32
+    index: int = -1       # number of the frame in append order
 
 
 class CacheModel:
-    def __init__(self, n_heads, head_dim, tokens_per_frame, sink_frames, window_frames):
+    def __init__(self, n_heads, head_dim, tokens_per_frame, sink_frames, window_frames,
+                 shot_frames=0):
         self.H = n_heads
         self.D = head_dim
         self.T_f = tokens_per_frame
         self.S_g = sink_frames
         self.W_f = window_frames
+        self.S_s = shot_frames
         self.sinks = []
         self.window = deque()
+        self.pinned = []        # shot-level-sink frames that left the window
+        self.n_frames = 0       # frames appended so far
+        self.shot_start = 0     # number of the current shot's first frame
         self.n_chunks = 0
         self.chunk_codes = {}   # chunk id -> (k_codes, k_scales, s_k, v_codes, v_scales, s_v)
+
+    def _in_shot_sink(self, fr):
+        return self.shot_start <= fr.index < self.shot_start + self.S_s
+
+    def _leave_window(self):
+        fr = self.window.popleft()
+        if self._in_shot_sink(fr):
+            self.pinned.append(fr)
+
+    def begin_shot(self):
+        """Scene cut: the next appended frame starts a new shot."""
+        self.pinned = []
+        self.shot_start = self.n_frames
 
     def append(self, k_bits, v_bits):
         """Quantize one chunk's K and V (bf16 bits [H, n*T_f, D]) and push its
@@ -63,23 +90,25 @@ class CacheModel:
         self.chunk_codes[cid] = (kc, ks, sk, vc, vs, sv)
         for f in range(n_frames):
             sl = slice(f * self.T_f, (f + 1) * self.T_f)
-            fr = Frame(cid, f, kc[:, sl], ks[:, sl], vc[:, sl], vs[:, sl], sk, sv)
+            fr = Frame(cid, f, kc[:, sl], ks[:, sl], vc[:, sl], vs[:, sl], sk, sv, self.n_frames)
+            self.n_frames += 1
             if len(self.sinks) < self.S_g:
                 self.sinks.append(fr)
             else:
                 if len(self.window) == self.W_f:
-                    self.window.popleft()
+                    self._leave_window()
                 self.window.append(fr)
         return cid
 
     def evict(self, n_frames):
-        """Drop the oldest ``n_frames`` window frames (never sinks)."""
+        """Drop the oldest ``n_frames`` window frames (never global sinks; a
+        shot-level-sink frame stays, pinned)."""
         assert 0 <= n_frames <= len(self.window)
         for _ in range(n_frames):
-            self.window.popleft()
+            self._leave_window()
 
     def frames(self):
-        return list(self.sinks) + list(self.window)
+        return list(self.sinks) + list(self.pinned) + list(self.window)
 
     def n_tokens(self):
         return len(self.frames()) * self.T_f

@@ -197,3 +197,47 @@ def test_cut_blocks_wait_fallback(ops, D):
             run_case(ops, cache, model, q, ko, vo, 1.0 / np.sqrt(D), what=f"D{D} wait limit {limit}")
     finally:
         ops.set_wait_limit(1 << 16)
+
+
+@pytest.mark.parametrize("D", [64, 128])
+def test_multi_shot_sink(ops, D):
+    """Global sink + shot-level sink + window (paper text, section 4.2): scene cuts
+    re-bind the shot-level sink, whose frames stay attended after the window rolls
+    past them; attention after every append matches the oracle's cache model, and a
+    pinned chunk's codes are still byte-exact."""
+    from gpu_util import dev, host
+    from oracle import quantize_ref
+    rng = np.random.default_rng(60 + D)
+    H, T_f, sink, window, shot = 2, 24, 1, 3, 2
+    cache = ops.KVCache(H, D, T_f, sink, window, shot_frames=shot)
+    model = CacheModel(H, D, T_f, sink, window, shot_frames=shot)
+    schedule = [1, 2, "cut", 1, 2, 2, "cut", 1, 1, 3, 2]
+    chunks = []
+    for i, op in enumerate(schedule):
+        if op == "cut":
+            cache.begin_shot()
+            model.begin_shot()
+            continue
+        k, v = rand_bits(rng, (H, op * T_f, D)), rand_bits(rng, (H, op * T_f, D))
+        chunks.append((k, v))
+        cache.append(dev(k), dev(v), op)
+        model.append(k, v)
+        st, n, extra = cache.shot_sink()
+        assert (st, n, extra) == (model.shot_start, min(shot, model.n_frames - model.shot_start),
+                                  len(model.pinned) * T_f)
+        s_tok, w_tok = cache.tokens()
+        assert s_tok + w_tok + extra == model.n_tokens()
+        q, ko, vo = (rand_bits(rng, (H, 70, D)) for _ in range(3))
+        run_case(ops, cache, model, q, ko, vo, 1.0 / np.sqrt(D),
+                 what=f"D{D} step {i} frames {model.n_frames} pinned {len(model.pinned)}")
+    # chunk 6 (frame 9, the second frame after the second cut) is held only as the
+    # shot-level sink: the window rolled past it two appends ago
+    idx = 6
+    assert [f.index for f in model.pinned] == [8, 9] and model.window[0].index > 9
+    kc, ks, vc, vs, sk, sv = cache.export_chunk(idx)
+    k, v = chunks[idx]
+    for got, want, what in (((host(kc), host(ks), host(sk)[0]), quantize_ref(k), "K"),
+                            ((host(vc), host(vs), host(sv)[0]), quantize_ref(v), "V")):
+        gc, gs, gt = got
+        wc, ws_, wt = want
+        assert np.array_equal(gc, wc) and np.array_equal(gs, ws_) and np.float32(gt) == wt, what

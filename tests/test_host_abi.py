@@ -24,7 +24,8 @@ OK, EINVAL, ESHAPE, ECAPACITY, ESTATE, EHIP = 0, -1, -2, -3, -4, -5
 
 class Cfg(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in
-                ("n_heads", "head_dim", "tokens_per_frame", "sink_frames", "window_frames")]
+                ("n_heads", "head_dim", "tokens_per_frame", "sink_frames", "window_frames",
+                 "shot_frames")]
 
 
 def declared_functions():
@@ -70,7 +71,8 @@ def test_error_paths_before_device_work(real):
     real.kvcache_storage_bytes.restype = ctypes.c_size_t
     real.kvcache_storage_bytes.argtypes = [ctypes.POINTER(Cfg)]
     for bad in [Cfg(1, 96, 64, 1, 3), Cfg(1, 128, 60, 1, 3), Cfg(0, 128, 64, 1, 3),
-                Cfg(1, 128, 64, -1, 3), Cfg(1, 128, 64, 1, 0), Cfg(1, 128, 64, 40, 30)]:
+                Cfg(1, 128, 64, -1, 3), Cfg(1, 128, 64, 1, 0), Cfg(1, 128, 64, 40, 30),
+                Cfg(1, 128, 64, 1, 3, -1), Cfg(1, 128, 64, 30, 30, 5)]:
         assert real.kvcache_storage_bytes(ctypes.byref(bad)) == 0
     h = P()
     real.kvcache_create.argtypes = [ctypes.POINTER(Cfg), P, ctypes.c_size_t, ctypes.POINTER(P)]
@@ -127,6 +129,9 @@ def stub():
     L.kvcache_destroy.argtypes = [P]
     L.chunk_attention.argtypes = [P, P, P, P, ctypes.c_int64, ctypes.c_float, P, P]
     L.kvcache_tokens.argtypes = [P, ctypes.POINTER(ctypes.c_int64), ctypes.POINTER(ctypes.c_int64)]
+    L.kvcache_begin_shot.argtypes = [P]
+    L.kvcache_shot_sink.argtypes = [P, ctypes.POINTER(ctypes.c_int64), ctypes.POINTER(ctypes.c_int32),
+                                    ctypes.POINTER(ctypes.c_int64)]
     L.kvcache_export_chunk.argtypes = [P, ctypes.c_int32] + [P] * 7
     L.stub_last_segments.argtypes = [ctypes.POINTER(ctypes.c_int32), ctypes.c_int]
     L.stub_last_quant_slots.argtypes = [ctypes.POINTER(ctypes.c_int32), ctypes.c_int,
@@ -164,21 +169,26 @@ class StubCache:
         return list(buf[:n]), nt.value, rows.value
 
 
-@pytest.mark.parametrize("seed", range(10))
+@pytest.mark.parametrize("seed", range(16))
 def test_cache_metadata_matches_frame_list_model(stub, seed):
-    """Random append/evict sequences: the tokens the attention kernel would read
-    (segment list, in order) are exactly the frames of the oracle's cache model,
-    each frame's slot being where its chunk's quantize launch wrote it, and each
-    segment carrying its chunk's tensor-scale slot."""
+    """Random append/evict/scene-cut sequences: the tokens the attention kernel would
+    read (segment list, in order) are exactly the frames of the oracle's cache model
+    (global sink, shot-level sink, window), each frame's slot being where its chunk's
+    quantize launch wrote it, and each segment carrying its chunk's tensor-scale
+    slot.  Seeds 0-7 run without a shot-level sink."""
     rng = np.random.default_rng(seed)
     sink, window = int(rng.integers(0, 4)), int(rng.integers(1, 8))
+    shot = 0 if seed < 8 else int(rng.integers(1, 4))
     T_f = 8 * int(rng.integers(1, 5))
-    c = StubCache(stub, Cfg(1, 64, T_f, sink, window))
-    model = CacheModel(1, 64, T_f, sink, window)
+    c = StubCache(stub, Cfg(1, 64, T_f, sink, window, shot))
+    model = CacheModel(1, 64, T_f, sink, window, shot_frames=shot)
     where = {}          # (chunk, frame) -> slot
     scale_of = {}       # chunk -> table offset of its K scale
     chunk = 0
-    for step in range(40):
+    for step in range(60):
+        if shot and rng.random() < 0.15:
+            assert stub.kvcache_begin_shot(c.h) == OK
+            model.begin_shot()
         if rng.random() < 0.2 and len(model.window) > 0:
             e = int(rng.integers(1, len(model.window) + 1))
             assert stub.kvcache_evict(c.h, e) == OK
@@ -186,7 +196,7 @@ def test_cache_metadata_matches_frame_list_model(stub, seed):
         nf = int(rng.integers(1, window + 1))
         assert c.append(nf) == OK
         slots, nt, rows = c.quant_slots()
-        assert nt == 2 and rows == (sink + window) * T_f and len(slots) == nf
+        assert nt == 2 and rows == (sink + window + shot) * T_f and len(slots) == nf
         for f, s in enumerate(slots):
             where[(chunk, f)] = s
         scale_of[chunk] = stub.stub_last_scale_ptr(0) - StubCache.BASE
@@ -220,6 +230,11 @@ def test_cache_metadata_matches_frame_list_model(stub, seed):
         s_tok, w_tok = ctypes.c_int64(), ctypes.c_int64()
         stub.kvcache_tokens(c.h, ctypes.byref(s_tok), ctypes.byref(w_tok))
         assert s_tok.value == len(model.sinks) * T_f and w_tok.value == len(model.window) * T_f
+        st, nsh, extra = ctypes.c_int64(), ctypes.c_int32(), ctypes.c_int64()
+        assert stub.kvcache_shot_sink(c.h, ctypes.byref(st), ctypes.byref(nsh), ctypes.byref(extra)) == OK
+        assert st.value == model.shot_start
+        assert nsh.value == min(shot, model.n_frames - model.shot_start)
+        assert extra.value == len(model.pinned) * T_f
     stub.kvcache_destroy(c.h)
 
 

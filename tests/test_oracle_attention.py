@@ -127,3 +127,66 @@ def test_cache_model_matches_keff_definition(seed):
         want = list(range(min(n, sink))) + list(range(max(lo, sink), n))
         assert ids == want
         assert cm.n_tokens() == len(want) * T_f
+
+
+def _frame_numbers(cm):
+    starts, acc = {}, 0
+    for c in sorted(cm.chunk_codes):
+        starts[c] = acc
+        acc += cm.chunk_codes[c][0].shape[1] // cm.T_f
+    return [starts[f.chunk_id] + f.frame_in_chunk for f in cm.frames()]
+
+
+def test_shot_sink_hand_schedule():
+    """The hand-worked multi-shot schedule of tests/golden/shot_sink_schedule.json
+    (paper text, section 4.2, 'Multi-Shot Attention Sink')."""
+    import json, os
+    g = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "shot_sink_schedule.json")))
+    c = g["config"]
+    T_f = 8
+    cm = CacheModel(1, 16, T_f, c["sink_frames"], c["window_frames"], shot_frames=c["shot_frames"])
+    for st in g["steps"]:
+        if st["op"] == "cut":
+            cm.begin_shot()
+            continue
+        if st["op"] == "append":
+            k = np.zeros((1, st["frames"] * T_f, 16), dtype=np.uint16)
+            cm.append(k, k)
+        else:
+            cm.evict(st["frames"])
+        assert _frame_numbers(cm) == st["keff"], st.get("why")
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_cache_model_shot_sink_matches_keff_definition(seed):
+    """Paper text, section 4.2: K_eff = A_g U A_s U window, duplicates removed, with
+    A_g the first S_g frames, A_s = [s0, s0 + S_s) for the current shot's first frame
+    s0 (moved to the next frame number at a scene cut) and the window the run of
+    non-sink frame numbers [lo, n) (lo moves forward by evictions and overflow).
+    Set arithmetic on frame numbers, independent of the model's frame lists."""
+    rng = np.random.default_rng(100 + seed)
+    sink, window, shot, T_f = int(rng.integers(0, 4)), int(rng.integers(1, 7)), int(rng.integers(0, 5)), 8
+    cm = CacheModel(1, 16, T_f, sink, window, shot_frames=shot)
+    n, lo, s0 = 0, sink, 0
+    for _ in range(40):
+        if rng.random() < 0.2:
+            cm.begin_shot()
+            s0 = n
+        n_win = max(0, n - max(lo, sink))
+        if rng.random() < 0.2 and n_win > 0:
+            e = int(rng.integers(1, n_win + 1))
+            cm.evict(e)
+            lo = max(lo, sink) + e
+        nf = int(rng.integers(1, window + 1))
+        k = np.zeros((1, nf * T_f, 16), dtype=np.uint16)
+        cm.append(k, k)
+        n += nf
+        lo = max(lo, n - window, sink)
+        a_g = list(range(min(n, sink)))
+        win = list(range(max(lo, sink), n))
+        a_s_out = [f for f in range(s0, min(s0 + shot, n)) if sink <= f < lo]
+        want = a_g + a_s_out + win
+        got = _frame_numbers(cm)
+        assert got == want
+        assert len(set(got)) == len(got)
+        assert cm.n_tokens() == len(want) * T_f
