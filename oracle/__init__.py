@@ -7,7 +7,8 @@ tables or constants with it: the two meet only on the seeded inputs.
 
 Contents (each function cites the passage of the pages it follows):
 
-* ``nvfp4_ref``     -- E2M1 / E4M3 codecs, the NVFP4 quantizer and dequantizer.
+* ``nvfp4_ref``     -- E2M1 / E4M3 codecs, the NVFP4 quantizer and dequantizer,
+  with the optional K-smoothing and adaptive 4/6 block scales.
 * ``cache_ref``     -- sink + sliding-window frame list (the effective key set).
 * ``attention_ref`` -- softmax attention of a noisy chunk over the dequantized
   cache plus its own bf16 K/V, in float64.
@@ -26,6 +27,7 @@ from .nvfp4_ref import (  # noqa: F401
     e4m3_encode,
     quantize_ref,
     dequantize_ref,
+    channel_mean_ref,
 )
 from .cache_ref import CacheModel  # noqa: F401
 from .attention_ref import chunk_attention_ref, attention_from_kv  # noqa: F401

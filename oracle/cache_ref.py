@@ -9,7 +9,8 @@ by a (start, len) pair and kept once the window has rolled past it; the effectiv
 key set is the union of the global sink, the shot-level sink and the window, with
 duplicate tokens removed.  Reading note, "The inference infrastructure": each
 appended frame chunk is quantized to NVFP4 on its own (one tensor scale per chunk
-tensor).
+tensor), optionally with K-smoothing for K and adaptive scale selection for V
+(see nvfp4_ref; the smoothing means are added back to the dequantized K).
 
 Model: frames are numbered in append order.  The first ``sink_frames`` frames are
 the global sink; every later frame joins a FIFO window of at most
@@ -28,7 +29,7 @@ from dataclasses import dataclass
 
 import numpy as np
 
-from .nvfp4_ref import quantize_ref, dequantize_ref
+from .nvfp4_ref import quantize_ref, dequantize_ref, channel_mean_ref
 
 
 @dataclass
@@ -42,17 +43,21 @@ class Frame:
     s_k: np.float32
     s_v: np.float32
     index: int = -1       # number of the frame in append order
+    k_mean: np.ndarray = None   # K-smoothing channel means of the frame's chunk [H, D]
 
 
 class CacheModel:
     def __init__(self, n_heads, head_dim, tokens_per_frame, sink_frames, window_frames,
-                 shot_frames=0):
+                 shot_frames=0, k_smooth=False, v_adaptive=False):
         self.H = n_heads
         self.D = head_dim
         self.T_f = tokens_per_frame
         self.S_g = sink_frames
         self.W_f = window_frames
         self.S_s = shot_frames
+        self.k_smooth = k_smooth      # K quantized after subtracting its chunk's channel means
+        self.v_adaptive = v_adaptive  # V blocks take the better of the 6- and 4-scaled encodings
+        self.chunk_mean = {}          # chunk id -> K channel means [H, D] (K-smoothing only)
         self.sinks = []
         self.window = deque()
         self.pinned = []        # shot-level-sink frames that left the window
@@ -83,14 +88,17 @@ class CacheModel:
         assert (H, D) == (self.H, self.D) and v_bits.shape == k_bits.shape
         assert T % self.T_f == 0
         n_frames = T // self.T_f
-        kc, ks, sk = quantize_ref(k_bits)
-        vc, vs, sv = quantize_ref(v_bits)
+        mu = channel_mean_ref(k_bits) if self.k_smooth else None
+        kc, ks, sk = quantize_ref(k_bits, mean=mu)
+        vc, vs, sv = quantize_ref(v_bits, adaptive=self.v_adaptive)
         cid = self.n_chunks
         self.n_chunks += 1
         self.chunk_codes[cid] = (kc, ks, sk, vc, vs, sv)
+        if mu is not None:
+            self.chunk_mean[cid] = mu
         for f in range(n_frames):
             sl = slice(f * self.T_f, (f + 1) * self.T_f)
-            fr = Frame(cid, f, kc[:, sl], ks[:, sl], vc[:, sl], vs[:, sl], sk, sv, self.n_frames)
+            fr = Frame(cid, f, kc[:, sl], ks[:, sl], vc[:, sl], vs[:, sl], sk, sv, self.n_frames, mu)
             self.n_frames += 1
             if len(self.sinks) < self.S_g:
                 self.sinks.append(fr)
@@ -119,6 +127,7 @@ class CacheModel:
         if not frs:
             z = np.zeros((self.H, 0, self.D))
             return z, z.copy()
-        ks = [dequantize_ref(f.k_codes, f.k_scales, f.s_k) for f in frs]
+        ks = [dequantize_ref(f.k_codes, f.k_scales, f.s_k)
+              + (0.0 if f.k_mean is None else f.k_mean.astype(np.float64)[:, None, :]) for f in frs]
         vs = [dequantize_ref(f.v_codes, f.v_scales, f.s_v) for f in frs]
         return np.concatenate(ks, axis=1), np.concatenate(vs, axis=1)

@@ -33,6 +33,25 @@ Readings taken where the pages are silent (each is also listed in the design doc)
 
 All fp32 steps use numpy float32 arithmetic, which is IEEE-754 correctly
 rounded with subnormals kept, so the steps above define every bit.
+
+Optional steps for the KV cache (reading note, "The inference infrastructure":
+within each frame chunk, K-smoothing is applied to K and adaptive scale selection
+to V; the paper text, section 2.2 and related work, cites Four Over Six as the
+adaptive block-scale selection with candidate scale magnitudes {4, 6}).  The
+pages give no formulas; the readings are:
+* K-smoothing: subtract from every K element its channel mean over the chunk's
+  tokens, mu[h, d], before quantizing; mu is kept in fp32 and added back on
+  dequantization.  mu is fixed bit for bit: the channel's values (fp32), padded
+  with +0.0 to a power-of-two count, are summed pairwise level by level
+  (v'[i] = v[2i] + v[2i+1], each an fp32 add), and the root is divided by the
+  token count (one fp32 division).  The smoothed element is x - mu (one fp32
+  subtraction) and the recipe above runs on those fp32 values (their amax gives
+  s_t, their sign bit the code's sign).
+* Adaptive block scale (V): each block is encoded twice, with the block maximum
+  mapped to 6 (the plain recipe) and to 4 (bs = (amax_b / 4) / s_t, the same
+  rounding), keeping s_t; the candidate with the smaller squared error wins, ties
+  going to 6.  The error of a candidate is the sum over the block's 16 elements,
+  in order, of (|x| - value * eff)^2, every operation an fp32 operation.
 """
 
 import numpy as np
@@ -127,11 +146,56 @@ F32 = np.float32
 BLOCK = 16
 
 
-def quantize_ref(x_bits):
+def channel_mean_ref(x_bits):
+    """K-smoothing channel means mu[h, d] of one chunk tensor x_bits [H, T, D]
+    (bf16 bits): pairwise fp32 sums over the +0.0-padded power-of-two token
+    count, then one fp32 division by T (module docstring)."""
+    x = bf16_bits_to_f32(np.asarray(x_bits, dtype=np.uint16))
+    H, T, D = x.shape
+    assert T >= 1
+    P = 1
+    while P < T:
+        P *= 2
+    v = np.zeros((H, P, D), dtype=F32)
+    v[:, :T] = x
+    while v.shape[1] > 1:
+        v = (v[:, 0::2] + v[:, 1::2]).astype(F32)
+    return (v[:, 0] / F32(T)).astype(F32)
+
+
+def _encode_blocks(ax, amax_b, s_t, M):
+    """One candidate: block maxima mapped to M (6 or 4).  Returns the scale bytes
+    [..., nb], the magnitude codes [..., nb, 16] and the per-block squared error
+    (fp32, summed over the 16 elements in order)."""
+    with np.errstate(divide="ignore", invalid="ignore", over="ignore"):
+        if s_t > 0:
+            bs = ((amax_b / F32(M)) / s_t).astype(F32)   # two fp32 divisions
+        else:
+            bs = np.zeros_like(amax_b)
+    scale_codes = e4m3_encode(bs)
+    eff = (E4M3_VALUES[scale_codes].astype(F32) * s_t).astype(F32)   # fp32 multiply
+    live = eff > 0
+    with np.errstate(divide="ignore", invalid="ignore", over="ignore"):
+        q = (ax / np.where(live, eff, F32(1.0))[..., None]).astype(F32)
+    mag = e2m1_encode(q)
+    mag = np.where(live[..., None], mag, 0).astype(np.uint8)
+    val = (E2M1_VALUES[mag].astype(F32) * eff[..., None]).astype(F32)
+    d = (ax - val).astype(F32)
+    e = (d * d).astype(F32)
+    err = np.zeros(amax_b.shape, dtype=F32)
+    for i in range(BLOCK):
+        err = (err + e[..., i]).astype(F32)
+    return scale_codes, mag, err
+
+
+def quantize_ref(x_bits, mean=None, adaptive=False):
     """Quantize one chunk tensor to NVFP4.
 
     x_bits: uint16 bf16 bit patterns, shape [..., D] with D % 16 == 0 (the
     whole array is one tensor: one fp32 tensor scale for all of it).
+    mean:   optional K-smoothing channel means, fp32 [H, D] for x [H, T, D]; the
+            tensor quantized is then x - mean (fp32).
+    adaptive: choose each block's scale between the 6- and 4-candidates.
 
     Returns (codes uint8 [..., D/2], scales uint8 [..., D/16], s_t float32).
     Steps follow the module docstring, in order.
@@ -141,6 +205,11 @@ def quantize_ref(x_bits):
     assert D % BLOCK == 0
     x = bf16_bits_to_f32(x_bits)
     assert np.all(np.isfinite(x)), "inputs must be finite"
+    if mean is not None:
+        x = (x - np.asarray(mean, dtype=F32)[:, None, :]).astype(F32)   # fp32 subtraction
+        sign_bits = np.signbit(x).astype(np.uint8)
+    else:
+        sign_bits = ((x_bits >> 15) & 1).astype(np.uint8)
     ax = np.abs(x)                                   # float32, exact
 
     # tensor scale
@@ -152,22 +221,14 @@ def quantize_ref(x_bits):
     blocks = ax.reshape(lead + (nb, BLOCK))
     amax_b = blocks.max(axis=-1)                     # float32
 
-    with np.errstate(divide="ignore", invalid="ignore", over="ignore"):
-        if s_t > 0:
-            bs = (amax_b / F32(6.0)) / s_t           # two fp32 divisions
-            bs = bs.astype(F32)
-        else:
-            bs = np.zeros_like(amax_b)
-    scale_codes = e4m3_encode(bs)                    # uint8 [..., nb]
+    scale_codes, mag, err6 = _encode_blocks(blocks, amax_b, s_t, 6)
+    if adaptive:
+        sc4, mag4, err4 = _encode_blocks(blocks, amax_b, s_t, 4)
+        four = err4 < err6                           # ties keep 6
+        scale_codes = np.where(four, sc4, scale_codes)
+        mag = np.where(four[..., None], mag4, mag)
 
-    eff = (E4M3_VALUES[scale_codes].astype(F32) * s_t).astype(F32)   # fp32 multiply
-    live = eff > 0
-    with np.errstate(divide="ignore", invalid="ignore", over="ignore"):
-        q = (blocks / np.where(live, eff, F32(1.0))[..., None]).astype(F32)
-    mag = e2m1_encode(q)
-    mag = np.where(live[..., None], mag, 0).astype(np.uint8)
-
-    sign = ((x_bits >> 15) & 1).astype(np.uint8).reshape(lead + (nb, BLOCK))
+    sign = sign_bits.reshape(lead + (nb, BLOCK))
     code = (sign << 3) | mag                         # 4-bit codes
     code = code.reshape(lead + (D,))
     packed = (code[..., 0::2] | (code[..., 1::2] << 4)).astype(np.uint8)

@@ -229,3 +229,97 @@ def test_dequantize_exact_rational():
             sv = Fraction(sm, 512) if se == 0 else (1 + Fraction(sm, 8)) * Fraction(2) ** (se - 7)
             want = (-1 if code >> 3 else 1) * mag * sv * Fraction(float(s_t))
             assert Fraction(float(xh[0, t, d])) == want
+
+
+# ---------------------------------------------------------------- K-smoothing, adaptive 4/6
+
+from nvfp4_kv_cache_amd import workloads as W
+
+quantize_ref, dequantize_ref, unpack_codes = R.quantize_ref, R.dequantize_ref, R.unpack_codes
+bf16_to_f32 = R.bf16_bits_to_f32
+
+GOLDEN_KA = os.path.join(os.path.dirname(__file__), "golden", "kv_smoothing_adaptive_example.json")
+
+
+def test_channel_mean_hand_cases():
+    from oracle import channel_mean_ref
+    for case in json.load(open(GOLDEN_KA))["channel_mean"]:
+        ch = np.array(case["channel"], dtype=np.float32)
+        x = W.f32_to_bf16_bits(ch.reshape(1, -1, 1) * np.ones((1, 1, 16), np.float32))
+        mu = channel_mean_ref(x)
+        assert mu.shape == (1, 16)
+        assert np.all(mu == np.float32(case["mu"])), case["name"]
+
+
+@pytest.mark.parametrize("T", [1, 2, 3, 7, 64, 100, 1000, 4680])
+def test_channel_mean_exact_cases(T):
+    """Constant channels give the constant; small-integer channels (every partial
+    sum an exact fp32 integer) give RN(exact sum / T), the sum taken in Python
+    integers."""
+    from oracle import channel_mean_ref
+    rng = np.random.default_rng(T)
+    c = W.f32_to_bf16_bits(rng.standard_normal((2, 1, 16)).astype(np.float32))
+    x = np.repeat(c, T, axis=1)
+    assert np.array_equal(channel_mean_ref(x), bf16_to_f32(c[:, 0]))
+    ints = rng.integers(-100, 101, size=(3, T, 32))
+    xb = W.f32_to_bf16_bits(ints.astype(np.float32))
+    mu = channel_mean_ref(xb)
+    want = np.array([[np.float32(int(ints[h, :, d].sum())) / np.float32(T) for d in range(32)]
+                     for h in range(3)], dtype=np.float32)
+    assert np.array_equal(mu, want)
+
+
+def test_adaptive_hand_case():
+    g = json.load(open(GOLDEN_KA))["adaptive"]
+    bits = W.f32_to_bf16_bits(np.array(g["x"], dtype=np.float32).reshape(g["shape"]))
+    c0, s0, t0 = quantize_ref(bits)
+    c1, s1, t1 = quantize_ref(bits, adaptive=True)
+    assert t0 == t1 == np.float32(g["s_t"])
+    assert list(s0.reshape(-1)) == g["plain_scales"]
+    assert list(s1.reshape(-1)) == g["adaptive_scales"]
+    assert list(unpack_codes(c1)[0, 1]) == g["adaptive_codes_token1"]
+    assert np.array_equal(unpack_codes(c1)[0, 0], unpack_codes(c0)[0, 0])   # tie: 6 kept
+
+
+def test_adaptive_never_worse_than_plain():
+    """Per block, the adaptive choice's reconstruction error (fp64) is not above
+    the plain recipe's, and every block either keeps the plain encoding or takes
+    a strictly smaller fp64 error (the fp32 comparison can only flip near-ties)."""
+    rng = np.random.default_rng(5)
+    x = (rng.standard_t(4, size=(3, 200, 64)) * 2.0).astype(np.float32)
+    bits = W.f32_to_bf16_bits(x)
+    xf = bf16_to_f32(bits).astype(np.float64)
+    out = {}
+    for ad in (False, True):
+        c, s, t = quantize_ref(bits, adaptive=ad)
+        xh = dequantize_ref(c, s, t)
+        out[ad] = ((xh - xf) ** 2).reshape(3, 200, 4, 16).sum(-1), s
+    e0, s0 = out[False]
+    e1, s1 = out[True]
+    changed = s0 != s1
+    assert changed.any() and not changed.all()
+    assert np.all(e1[~changed] == e0[~changed])
+    assert np.all(e1[changed] <= e0[changed] * (1 + 1e-6))
+    assert e1.sum() < e0.sum()
+
+
+def test_smoothing_reconstruction():
+    """x_hat = dequant(codes of x - mu) + mu is within the per-block error bound of
+    the smoothed values, and removing a per-channel offset makes the error
+    independent of that offset's size."""
+    from oracle import channel_mean_ref
+    rng = np.random.default_rng(6)
+    base = rng.standard_normal((2, 96, 32)).astype(np.float32)
+    offs = (rng.standard_normal((2, 1, 32)) * 40).astype(np.float32)
+    bits = W.f32_to_bf16_bits(base + offs)
+    mu = channel_mean_ref(bits)
+    c, s, t = quantize_ref(bits, mean=mu)
+    xs = (bf16_to_f32(bits) - mu[:, None, :]).astype(np.float32).astype(np.float64)
+    xh = dequantize_ref(c, s, t)
+    from oracle import E4M3_VALUES
+    eff = np.repeat(E4M3_VALUES[s] * float(t), 16, axis=-1)
+    assert np.all(np.abs(xh - xs) <= eff + 1e-30)
+    err_s = np.abs(xh + mu[:, None, :] - bf16_to_f32(bits)).max()
+    c2, s2, t2 = quantize_ref(bits)
+    err_p = np.abs(dequantize_ref(c2, s2, t2) - bf16_to_f32(bits)).max()
+    assert err_s < 0.25 * err_p
