@@ -17,7 +17,8 @@ Prints progress on stderr and ONE JSON line on stdout:
                  dense MFMA peak
   quantize       the append (quantize + pack) kernel on the quantize-only
                  workload, cache-cold inputs: algorithmic GB/s vs 8 TB/s HBM
-  configs        the other workloads (tiny, 1.3B-shaped, 5B-shaped)
+  configs        the other workloads (tiny, 1.3B-shaped, 5B-shaped), and the append and
+                 the 1.3B-shaped attention with K-smoothing + adaptive V scales
   cpu_baseline   the CPU oracle on a bounded sample of the same attention
 """
 
@@ -208,15 +209,17 @@ def roofline_only(args, torch, ops, W, device):
             "cache_tokens": sum(cache.tokens())}
 
 
-def quantize_leg(args, torch, ops, W, device):
+def quantize_leg(args, torch, ops, W, device, k_smooth=False, v_adaptive=False, sets=None):
     """Append of one 3-frame chunk of K and V [12, 4680, 128] into a full cache,
-    cycling 10 distinct input sets (287.5 MB > the 256 MB Infinity Cache)."""
+    cycling 10 distinct input sets (287.5 MB > the 256 MB Infinity Cache).  With
+    k_smooth / v_adaptive the cache applies K-smoothing / adaptive V scales."""
     wl = W.WORKLOADS["quantize"]
     n_sets = 10
-    log(f"quantize: drawing {n_sets} Student-t input sets on the host")
-    sets = [tuple(dev_bits(torch, b, device) for b in W.clean_chunk(wl, c)) for c in range(n_sets)]
+    if sets is None:
+        log(f"quantize: drawing {n_sets} Student-t input sets on the host")
+        sets = [tuple(dev_bits(torch, b, device) for b in W.clean_chunk(wl, c)) for c in range(n_sets)]
     cache = ops.KVCache(wl.n_heads, wl.head_dim, wl.tokens_per_frame, wl.sink_frames,
-                        wl.window_frames, device=device)
+                        wl.window_frames, device=device, k_smooth=k_smooth, v_adaptive=v_adaptive)
     for c in range(4):
         cache.append(*sets[c], wl.chunk_frames)
     it = [0]
@@ -231,16 +234,18 @@ def quantize_leg(args, torch, ops, W, device):
     elems = wl.n_heads * wl.chunk_tokens * wl.head_dim
     nbytes = 2 * W.quantize_bytes(elems)
     gbps = nbytes / (ms * 1e-3) / 1e9
-    return {"us_per_append": ms * 1e3, "bytes_per_append": nbytes, "GB_per_s": gbps,
-            "roofline": {"bound": "hbm", "achieved": gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                         "frac": gbps / HBM_PEAK_GBPS, "traffic": measured_traffic("quantize")}}
+    out = {"us_per_append": ms * 1e3, "bytes_per_append": nbytes, "GB_per_s": gbps,
+           "roofline": {"bound": "hbm", "achieved": gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                        "frac": gbps / HBM_PEAK_GBPS,
+                        "traffic": None if (k_smooth or v_adaptive) else measured_traffic("quantize")}}
+    return out, sets
 
 
-def attention_config(name, args, torch, ops, W, device):
+def attention_config(name, args, torch, ops, W, device, k_smooth=False, v_adaptive=False):
     wl = W.WORKLOADS[name]
     log(f"{name}: building the cache from {wl.n_cache_chunks} host-drawn chunks")
     cache = ops.KVCache(wl.n_heads, wl.head_dim, wl.tokens_per_frame, wl.sink_frames,
-                        wl.window_frames, device=device)
+                        wl.window_frames, device=device, k_smooth=k_smooth, v_adaptive=v_adaptive)
     for c in range(wl.n_cache_chunks):
         k, v = W.clean_chunk(wl, c)
         cache.append(dev_bits(torch, k, device), dev_bits(torch, v, device), wl.chunk_frames)
@@ -327,7 +332,7 @@ def main():
                           "ms": ms, "GB_per_s": 2 * src.numel() * 4 / (ms * 1e-3) / 1e9}), flush=True)
         return
     if args.only == "quantize":
-        qz = quantize_leg(args, torch, ops, W, device)
+        qz, _ = quantize_leg(args, torch, ops, W, device)
         print(json.dumps({"leg": "quantize", "workload": "quantize", **qz}), flush=True)
         return
 
@@ -335,13 +340,20 @@ def main():
     log(f"rollout: {r['ms_per_step']:.3f} ms/step, {r['tflops']:.1f} TFLOP/s, "
         f"{r['frames_per_s']:.1f} frames/s; attention kernel {r['attn_ms']*1e3:.1f} us "
         f"= {r['attn_tflops']:.1f} TFLOP/s")
-    qz = quantize_leg(args, torch, ops, W, device)
+    qz, qsets = quantize_leg(args, torch, ops, W, device)
     log(f"quantize: {qz['us_per_append']:.2f} us/append = {qz['GB_per_s']:.1f} GB/s")
     configs = {}
     if not args.skip_configs:
         for name in ("tiny", "wan13b", "wan5b"):
             configs[name] = attention_config(name, args, torch, ops, W, device)
             log(f"{name}: {configs[name]['us']:.1f} us, {configs[name]['tflops']:.1f} TFLOP/s")
+        # the cache options (K-smoothing for K, adaptive 4/6 scales for V)
+        qo, _ = quantize_leg(args, torch, ops, W, device, k_smooth=True, v_adaptive=True, sets=qsets)
+        configs["quantize_k_smooth_v_adaptive"] = {k: qo[k] for k in ("us_per_append", "GB_per_s")}
+        log(f"quantize, K-smoothing + adaptive V: {qo['us_per_append']:.2f} us/append")
+        configs["wan13b_k_smooth_v_adaptive"] = attention_config("wan13b", args, torch, ops, W, device,
+                                                                 k_smooth=True, v_adaptive=True)
+        log(f"wan13b, K-smoothing + adaptive V: {configs['wan13b_k_smooth_v_adaptive']['us']:.1f} us")
     configs["quantize"] = {k: qz[k] for k in ("us_per_append", "GB_per_s", "bytes_per_append")}
     configs["quantize"]["frac_hbm_peak"] = qz["roofline"]["frac"]
 

@@ -106,11 +106,28 @@ int nvfp4_quantize_kv(const uint16_t *x, int64_t H, int64_t T, int64_t D, uint8_
  * shot starts at the first frame.  The effective key set is global sink U shot-level
  * sink U window.  Frames are never copied; eviction only changes host metadata.
  *
+ * Options (reading note, "The inference infrastructure": within each chunk,
+ * K-smoothing for K and adaptive scale selection for V):
+ *   NVFP4KV_K_SMOOTH    each appended chunk's K has its per-head channel means
+ *                       (over the chunk's tokens) subtracted before quantization;
+ *                       the means are kept in fp32 and attention adds q . mean back
+ *                       to every logit of that chunk's keys.  The mean is a pairwise
+ *                       fp32 tree over the tokens padded with +0.0 to a power of two,
+ *                       divided by the token count.
+ *   NVFP4KV_V_ADAPTIVE  each V block is encoded with its maximum mapped to 6 and to 4
+ *                       (same tensor scale) and keeps the encoding with the smaller
+ *                       fp32 squared error (ties: 6).  Decoding is unchanged.
+ * Appends with options run the two-pass quantizer (plus the mean reduction).
+ *
  * Supported: n_heads >= 1; head_dim 64 or 128; tokens_per_frame >= 8 and a multiple
  * of 8; sink_frames >= 0; window_frames >= 1; shot_frames >= 0 (0: no shot-level
- * sink); sink_frames + window_frames + shot_frames <= 64.
+ * sink); sink_frames + window_frames + shot_frames <= 64; options a combination of
+ * the flags above.
  * Every bf16 / fp32 tensor argument must be 16-byte aligned.
  * ------------------------------------------------------------------------------ */
+#define NVFP4KV_K_SMOOTH 1
+#define NVFP4KV_V_ADAPTIVE 2
+
 typedef struct {
   int32_t n_heads;
   int32_t head_dim;
@@ -118,6 +135,7 @@ typedef struct {
   int32_t sink_frames;
   int32_t window_frames;
   int32_t shot_frames;
+  int32_t options;   /* NVFP4KV_K_SMOOTH | NVFP4KV_V_ADAPTIVE, or 0 */
 } kvcache_config;
 
 typedef struct kvcache kvcache; /* opaque host object */
@@ -194,6 +212,12 @@ int chunk_attention(const kvcache *c, const uint16_t *q, const uint16_t *k_own,
 int kvcache_export_chunk(const kvcache *c, int32_t chunk_index, uint8_t *k_codes,
                          uint8_t *k_scales, uint8_t *v_codes, uint8_t *v_scales,
                          float *k_scale, float *v_scale, void *stream);
+
+/* K-smoothing means of a resident chunk: k_mean fp32 [H, D] (device), the values
+ * subtracted from its K before quantization.  Device-to-device, on `stream`.
+ * Errors: EINVAL (null, or the cache has no NVFP4KV_K_SMOOTH), ESTATE (chunk not
+ * resident), EHIP. */
+int kvcache_export_k_mean(const kvcache *c, int32_t chunk_index, float *k_mean, void *stream);
 
 /* Frame count of a resident chunk (host output); ESTATE if not resident. */
 int kvcache_chunk_frames(const kvcache *c, int32_t chunk_index, int32_t *n_frames);

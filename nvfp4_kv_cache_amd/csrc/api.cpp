@@ -30,7 +30,7 @@ bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p
 
 struct Layout {
   int64_t rows;   // token capacity per head
-  size_t kcodes, kscales, vcodes, vscales, table, ws, attn_flags, attn_part, total;
+  size_t kcodes, kscales, vcodes, vscales, table, ws, attn_flags, attn_part, kmean, kmean_ws, total;
 };
 
 bool config_ok(const kvcache_config *c) {
@@ -41,6 +41,7 @@ bool config_ok(const kvcache_config *c) {
       c->tokens_per_frame > (1 << 20))
     return false;
   if (c->sink_frames < 0 || c->window_frames < 1 || c->shot_frames < 0) return false;
+  if (c->options & ~(NVFP4KV_K_SMOOTH | NVFP4KV_V_ADAPTIVE)) return false;
   if (c->sink_frames + c->window_frames + c->shot_frames > kMaxFrames) return false;
   // per-head planes are addressed with 32-bit offsets
   if (int64_t(c->sink_frames + c->window_frames + c->shot_frames) * c->tokens_per_frame * c->head_dim >=
@@ -63,6 +64,16 @@ bool make_layout(const kvcache_config *c, Layout *L) {
   L->ws = off;      off = round_up(off + sizeof(QuantWorkspace));
   L->attn_flags = off; off = round_up(off + sizeof(uint64_t) * attn_max_grid(int(D)));
   L->attn_part = off; off = round_up(off + attn_max_grid(int(D)) * attn_slot_bytes(int(D)));
+  L->kmean = off;
+  L->kmean_ws = off;
+  if (c->options & NVFP4KV_K_SMOOTH) {
+    // per scale slot, the K channel means of its chunk; and the reduction's workspace
+    // for the longest chunk an append accepts (sink + window frames)
+    off = round_up(off + sizeof(float) * kScaleSlots * H * D);
+    L->kmean_ws = off;
+    const int64_t t_max = int64_t(c->sink_frames + c->window_frames) * c->tokens_per_frame;
+    off = round_up(off + sizeof(float) * channel_mean_ws_floats(int(H), int(t_max), int(D)));
+  }
   L->total = off;
   return true;
 }
@@ -117,6 +128,11 @@ struct kvcache {
   QuantWorkspace *ws() const { return reinterpret_cast<QuantWorkspace *>(base + L.ws); }
   uint64_t *attn_flags() const { return reinterpret_cast<uint64_t *>(base + L.attn_flags); }
   float *attn_partials() const { return reinterpret_cast<float *>(base + L.attn_part); }
+  bool k_smooth() const { return (cfg.options & NVFP4KV_K_SMOOTH) != 0; }
+  float *kmean(int32_t scale_slot) const {
+    return reinterpret_cast<float *>(base + L.kmean) + int64_t(scale_slot) * cfg.n_heads * cfg.head_dim;
+  }
+  float *kmean_ws() const { return reinterpret_cast<float *>(base + L.kmean_ws); }
   int32_t window_slot(const State &s, int32_t i) const { return s.win[(s.win_head + i) % kMaxFrames]; }
   bool in_shot_sink(const State &s, int64_t frame) const {
     return frame >= s.shot_start && frame < s.shot_start + cfg.shot_frames;
@@ -320,8 +336,10 @@ int kvcache_append(kvcache *c, const uint16_t *k, const uint16_t *v, int32_t n_f
   s.next_frame += n_frames;
 
   float *tab = c->table();
-  a.t[0] = QuantTensor{k, c->kcodes(), c->kscales(), tab + 2 * sslot, 0, 0};
-  a.t[1] = QuantTensor{v, c->vcodes(), c->vscales(), tab + 2 * sslot + 1, 1, 0};
+  const bool v_adaptive = (cfg.options & NVFP4KV_V_ADAPTIVE) != 0;
+  a.t[0] = QuantTensor{k, c->kcodes(), c->kscales(), tab + 2 * sslot, 0, 0,
+                       c->k_smooth() ? c->kmean(sslot) : nullptr};
+  a.t[1] = QuantTensor{v, c->vcodes(), c->vscales(), tab + 2 * sslot + 1, 1, v_adaptive ? 1 : 0, nullptr};
   a.n_tensors = 2;
   a.H = cfg.n_heads;
   a.T = n_frames * cfg.tokens_per_frame;
@@ -332,6 +350,11 @@ int kvcache_append(kvcache *c, const uint16_t *k, const uint16_t *v, int32_t n_f
   a.ws = c->ws();
   a.epoch = ++c->epoch;   // never reused, even if the launch fails
   a.spin_limit = g_spin_limit.load(std::memory_order_relaxed);
+  if (cfg.options) a.epoch = 0;   // smoothing / adaptive scales: the two-pass kernels
+  if (c->k_smooth()) {
+    const int rm = launch_channel_mean(k, cfg.n_heads, a.T, cfg.head_dim, c->kmean(sslot), c->kmean_ws(), stream);
+    if (rm != NVFP4KV_OK) return rm;
+  }
   const int rc = launch_quantize(a, stream);
   if (rc != NVFP4KV_OK) return rc;
   c->st = s;
@@ -381,6 +404,15 @@ int kvcache_chunk_count(const kvcache *c, int32_t *n_chunks) {
   return NVFP4KV_OK;
 }
 
+int kvcache_export_k_mean(const kvcache *c, int32_t chunk_index, float *k_mean, void *stream) {
+  if (!c || !k_mean) return NVFP4KV_EINVAL;
+  if (!c->k_smooth()) return NVFP4KV_EINVAL;
+  auto it = c->st.chunks.find(chunk_index);
+  if (it == c->st.chunks.end()) return NVFP4KV_ESTATE;
+  return copy_device_floats(k_mean, c->kmean(it->second.scale_slot),
+                            size_t(c->cfg.n_heads) * c->cfg.head_dim, stream);
+}
+
 int kvcache_chunk_frames(const kvcache *c, int32_t chunk_index, int32_t *n_frames) {
   if (!c || !n_frames) return NVFP4KV_EINVAL;
   auto it = c->st.chunks.find(chunk_index);
@@ -413,6 +445,7 @@ int chunk_attention(const kvcache *c, const uint16_t *q, const uint16_t *k_own,
   a.D = c->cfg.head_dim;
   a.n_q = int32_t(n_q);
   a.sm_scale_log2 = softmax_scale * 1.4426950408889634f;
+  a.k_mean = c->k_smooth() ? c->kmean(0) : nullptr;
   a.partials = c->attn_partials();
   a.flags = c->attn_flags();
   a.epoch = ++c->attn_epoch;   // never reused, even if the launch fails

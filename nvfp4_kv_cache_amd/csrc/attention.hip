@@ -323,9 +323,11 @@ __device__ __forceinline__ void qk_tile(const uint16_t *Ks, const u32x4 (&qr)[D 
 }
 
 // Online softmax of S^T, then O^T += V^T P^T.
+// `bias` (per lane, i.e. per query; log2 units) is added to every logit of the
+// tile: the K-smoothing term q . mean of the tile's chunk, or 0.
 template <int D, bool MASK>
-__device__ __forceinline__ void softmax_pv(const uint16_t *Vs, f32x16 (&s)[2], float cmul, int nval,
-                                           Softmax &sm, f32x16 (&acc)[D / 32]) {
+__device__ __forceinline__ void softmax_pv(const uint16_t *Vs, f32x16 (&s)[2], float cmul, float bias,
+                                           int nval, Softmax &sm, f32x16 (&acc)[D / 32]) {
   const int lane = threadIdx.x & 63, half = lane >> 5, l32 = lane & 31;
   // keys past the end of the segment (only in a segment's last tile): excluded
   // from the maximum here and given probability 0 below
@@ -342,7 +344,7 @@ __device__ __forceinline__ void softmax_pv(const uint16_t *Vs, f32x16 (&s)[2], f
 #pragma unroll
   for (int r = 1; r < 16; ++r) mx = fmaxf(mx, fmaxf(s[0][r], s[1][r]));
   mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-  const float tmax = mx * cmul;
+  const float tmax = mx * cmul + bias;
   // raise the running max only when this tile exceeds it by more than kLazy
   if (__any(tmax > sm.m + kLazy)) {
     const float mnew = fmaxf(sm.m, tmax);
@@ -358,7 +360,7 @@ __device__ __forceinline__ void softmax_pv(const uint16_t *Vs, f32x16 (&s)[2], f
 #pragma unroll
     for (int db = 0; db < D / 32; ++db)
       vf[db][ks] = *reinterpret_cast<const f16x8 *>(Vs + vs_off(db * 32 + l32, 2 * ks + half));
-  const float mneg = -sm.m;
+  const float mneg = bias - sm.m;
   float lsum = 0.0f;
   f16x8 p[4];    // [16-key step]
 #pragma unroll
@@ -622,6 +624,7 @@ __global__ __launch_bounds__(Cfg<D>::kThreads, Cfg<D>::kWgPerCu) void chunk_atte
         // per segment: s_K folds into the logit multiplier; the accumulator moves to
         // units of the segment's s_V (an all-zero V chunk has s_V = 0 and contributes
         // nothing: keep the current units)
+        float kbias = 0.0f;
         auto enter_segment = [&](int sg) {
           if (sg == cur_seg) return;
           cur_seg = sg;
@@ -629,6 +632,22 @@ __global__ __launch_bounds__(Cfg<D>::kThreads, Cfg<D>::kWgPerCu) void chunk_atte
           const float sk = a.scale_table[2 * slot];
           const float sv = a.scale_table[2 * slot + 1];
           cmul = a.sm_scale_log2 * sk * cq;
+          if (a.k_mean) {
+            // K-smoothing: the chunk's K was quantized minus its channel means mu, so
+            // every logit of its keys gains q . mu (the same for all of them)
+            const float *mu = a.k_mean + (int64_t(slot) * a.H + h) * D + 8 * half;
+            float dot = 0.0f;
+#pragma unroll
+            for (int st = 0; st < D / 16; ++st) {
+              const f16x8 qv = __builtin_bit_cast(f16x8, qr[st]);
+              const float4 m0 = *reinterpret_cast<const float4 *>(mu + 16 * st);
+              const float4 m1 = *reinterpret_cast<const float4 *>(mu + 16 * st + 4);
+              dot += float(qv[0]) * m0.x + float(qv[1]) * m0.y + float(qv[2]) * m0.z + float(qv[3]) * m0.w +
+                     float(qv[4]) * m1.x + float(qv[5]) * m1.y + float(qv[6]) * m1.z + float(qv[7]) * m1.w;
+            }
+            dot += __shfl_xor(dot, 32, 64);
+            kbias = dot * cq * a.sm_scale_log2;
+          }
           if (sv > 0.0f) {
             const float r = vunit / sv;
   #pragma unroll
@@ -662,7 +681,7 @@ __global__ __launch_bounds__(Cfg<D>::kThreads, Cfg<D>::kWgPerCu) void chunk_atte
             const bool have_n2 = have_next && i + 2 < f1 && next_full(a, s2, k2);
             if (have_n2) ltok = a.seg[s2].tok0 + k2;
             load_packed<D>(hp, uint32_t(ltok), kBN, pk);
-            softmax_pv<D, false>(Vs[buf], s, cmul, kBN, sm, acc);
+            softmax_pv<D, false>(Vs[buf], s, cmul, kbias, kBN, sm, acc);
             __syncthreads();
             if (!have_next) break;
             buf ^= 1;
@@ -685,7 +704,7 @@ __global__ __launch_bounds__(Cfg<D>::kThreads, Cfg<D>::kWgPerCu) void chunk_atte
           enter_segment(cs);
           __syncthreads();
           qk_tile<D, false>(Ks[0], qr, s);
-          softmax_pv<D, true>(Vs[0], s, cmul, tn, sm, acc);
+          softmax_pv<D, true>(Vs[0], s, cmul, kbias, tn, sm, acc);
           __syncthreads();
         }
       }
@@ -718,7 +737,7 @@ __global__ __launch_bounds__(Cfg<D>::kThreads, Cfg<D>::kWgPerCu) void chunk_atte
             store_own_v<D>(rv, Vs[buf ^ 1]);
             store_own_k<D>(rk, Ks[buf ^ 1]);
             load_own_v<D>(a, h, min(t + 2, e - 1) * kBN, kBN, rv);
-            softmax_pv<D, false>(Vs[buf], s, cmul, kBN, sm, acc);
+            softmax_pv<D, false>(Vs[buf], s, cmul, 0.0f, kBN, sm, acc);
             __syncthreads();
             buf ^= 1;
           }
@@ -733,7 +752,7 @@ __global__ __launch_bounds__(Cfg<D>::kThreads, Cfg<D>::kWgPerCu) void chunk_atte
           store_own_v<D>(rv, Vs[0]);
           __syncthreads();
           qk_tile<D, true>(Ks[0], qr, s);
-          softmax_pv<D, true>(Vs[0], s, cmul, nval, sm, acc);
+          softmax_pv<D, true>(Vs[0], s, cmul, 0.0f, nval, sm, acc);
         }
       }
 

@@ -47,6 +47,12 @@ int launch_export(const ExportArgs &a, void *stream) {
   return NVFP4KV_HIP_OK(hipGetLastError());
 }
 
+int copy_device_floats(float *dst, const float *src, size_t n, void *stream) {
+  if (n == 0) return NVFP4KV_OK;
+  return NVFP4KV_HIP_OK(hipMemcpyAsync(dst, src, n * sizeof(float), hipMemcpyDeviceToDevice,
+                                       reinterpret_cast<hipStream_t>(stream)));
+}
+
 int zero_device_bytes_blocking(void *ptr, size_t bytes) {
   if (bytes == 0) return NVFP4KV_OK;
   return NVFP4KV_HIP_OK(hipMemset(ptr, 0, bytes));

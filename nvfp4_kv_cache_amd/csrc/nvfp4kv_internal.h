@@ -34,7 +34,8 @@ struct QuantTensor {
   uint8_t *scales;
   float *tensor_scale;   // receives s_t
   int32_t transposed;
-  int32_t pad;
+  int32_t adaptive;      // choose each block's scale between the 6- and 4-candidates
+  const float *mean;     // K-smoothing: channel means [H][D] subtracted first, or null
 };
 
 struct QuantArgs {
@@ -52,6 +53,20 @@ struct QuantArgs {
   QuantWorkspace *ws;
   int32_t frame_slot[kMaxFrames];   // destination slot of each source frame
 };
+
+// One level of the K-smoothing channel sums: a pairwise tree over each channel's
+// tokens (padded with +0.0 to a power of two), `group` leaves per workgroup.
+struct MeanLevel {
+  const uint16_t *src16;      // first level: bf16 K [H][T][D]; leaves past T are +0.0
+  const float *src32;         // later levels: node sums [H][n_in][D]
+  float *dst;                 // node sums [H][n_in / group][D]; at the last level the
+                              // means [H][D] (root / T)
+  int32_t H, D, T;
+  int32_t n_in;               // leaves per head at this level (a power of two)
+  int32_t group;              // leaves per workgroup (a power of two, at most 256)
+  int32_t last;
+};
+constexpr int kMeanGroup = 256;
 
 struct Segment {
   int32_t tok0;        // first token (slot * T_f) in the cache rows
@@ -94,6 +109,7 @@ struct AttnArgs {
   int32_t w_cfull, w_tail, w_ofull, w_block;
   int32_t pad;
   int64_t work;               // query blocks x block weight
+  const float *k_mean;        // K-smoothing means [scale slot][H][D], or null
   float *partials;            // [max grid][slot]
   uint64_t *flags;            // [max grid]: epoch of the last partial published in the slot
   uint64_t epoch;             // > 0, never repeated for one scratch area
@@ -117,6 +133,16 @@ struct ExportArgs {
 int launch_quantize(const QuantArgs &a, void *stream);
 int launch_attention(const AttnArgs &a, void *stream);
 int launch_export(const ExportArgs &a, void *stream);
+// K-smoothing channel means of one chunk tensor k [H][T][D] into mean [H][D]; ws holds
+// at least channel_mean_ws_floats(H, T, D) floats (two buffers of level node sums).
+inline size_t channel_mean_ws_floats(int H, int T, int D) {
+  int64_t P = 1;
+  while (P < T) P *= 2;
+  const int64_t nodes = P > kMeanGroup ? P / kMeanGroup : 1;
+  return size_t(2 * int64_t(H) * nodes * D);
+}
+int launch_channel_mean(const uint16_t *k, int H, int T, int D, float *mean, float *ws, void *stream);
+int copy_device_floats(float *dst, const float *src, size_t n, void *stream);
 int zero_device_bytes_blocking(void *ptr, size_t bytes);
 int zero_device_bytes_async(void *ptr, size_t bytes, void *stream);
 

@@ -109,12 +109,14 @@ __device__ __forceinline__ TensorConsts tensor_consts(float st) {
   return c;
 }
 
-// E4M3 scale byte of one block: bs = (amax / 6) / s_t, nearest-even, saturating.
+// E4M3 scale byte of one block: bs = (amax / M) / s_t, nearest-even, saturating;
+// M = 6 is the recipe, M = 4 the second candidate of the adaptive block scale.
 // Markstein quotients when both are comfortably normal; IEEE division otherwise.
+template <int M = 6>
 __device__ __forceinline__ uint32_t scale_code(float amax, const TensorConsts &tc) {
   float bs;
-  if (amax >= tc.amin) bs = div_rn(div_rn(amax, 6.0f, 1.0f / 6.0f), tc.st, tc.rst);
-  else bs = (amax / 6.0f) / tc.st;
+  if (amax >= tc.amin) bs = div_rn(div_rn(amax, float(M), 1.0f / float(M)), tc.st, tc.rst);
+  else bs = (amax / float(M)) / tc.st;
   short2_ p = {0, 0};
   p = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(p, fminf(bs, 448.0f), 0.0f, 1.0f, false);
   return uint32_t(uint16_t(p[0])) & 0xFFu;
@@ -155,6 +157,39 @@ __device__ __forceinline__ uint32_t cvt_fp4(uint32_t old, float a, float b) {
   return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(old, a, b, 1.0f, SEL);
 }
 
+// Adaptive block scale (V in the cache): squared error of encoding one token's
+// block with scale byte sc, sum over the 16 elements in order of
+// (|x| - value * eff)^2 with eff = E4M3(sc) * s_t, every step an fp32 operation
+// (no contraction: the choice must match the recipe bit for bit).
+template <bool SCALED>
+__device__ __forceinline__ float block_sq_error(const float (&x)[16], uint32_t sc, const TensorConsts &tc,
+                                                const float2 *tab) {
+#pragma clang fp contract(off)
+  const float2 dv = tab[sc];
+  const float eff = __builtin_amdgcn_cvt_f32_fp8(sc, 0) * tc.st;
+  float err = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 16; i += 2) {
+    const uint32_t c = cvt_fp4<0>(0u, quot<SCALED>(x[i], dv.x, dv.y, tc.xs),
+                                  quot<SCALED>(x[i + 1], dv.x, dv.y, tc.xs));
+    const auto v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c, 1.0f, 0);
+    const float da = fabsf(x[i]) - fabsf(v[0]) * eff;
+    err = err + da * da;
+    const float db = fabsf(x[i + 1]) - fabsf(v[1]) * eff;
+    err = err + db * db;
+  }
+  return err;
+}
+
+// The 4-candidate wins only with a strictly smaller error (ties keep 6).
+template <bool SCALED>
+__device__ __forceinline__ uint32_t choose_scale46(const float (&x)[16], float amax, uint32_t sc6,
+                                                   const TensorConsts &tc, const float2 *tab) {
+  const uint32_t sc4 = scale_code<4>(amax, tc);
+  if (sc4 == sc6) return sc6;
+  return block_sq_error<SCALED>(x, sc4, tc, tab) < block_sq_error<SCALED>(x, sc6, tc, tab) ? sc4 : sc6;
+}
+
 // Codec layout: one token's 16 values -> 8 bytes (element 2k in the low nibble).
 template <bool SCALED>
 __device__ __forceinline__ uint2 encode_token(const float (&x)[16], float eff, float r, float xs) {
@@ -188,16 +223,33 @@ struct Octet {
 };
 
 // Canonical item: per token, block max -> scale byte -> divisor -> 8 code bytes.
-template <bool SCALED>
+// MEAN: K-smoothing, the block's 16 channel means are subtracted first (fp32).
+template <bool SCALED, bool MEAN = false>
 __device__ __forceinline__ void item_canonical(const QuantArgs &a, const Octet &o, int b,
                                                const uint4 (&u)[kOctet][2],
                                                const TensorConsts &tc, const float2 *tab) {
   const QuantTensor &qt = a.t[o.tensor];
   const int nb = a.D >> 4;
+  float mu[16];
+  if constexpr (MEAN) {
+    const float4 *mp = reinterpret_cast<const float4 *>(qt.mean + int64_t(o.h) * a.D + 16 * b);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const float4 m4 = mp[k];
+      mu[4 * k] = m4.x;
+      mu[4 * k + 1] = m4.y;
+      mu[4 * k + 2] = m4.z;
+      mu[4 * k + 3] = m4.w;
+    }
+  }
 #pragma unroll
   for (int j = 0; j < kOctet; ++j) {
     float x[16];
     unpack16(u[j], x);
+    if constexpr (MEAN) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) x[i] = x[i] - mu[i];
+    }
     const uint32_t sc = scale_code(absmax16(x), tc);
     const float2 dv = tab[sc];
     const uint2 c = encode_token<SCALED>(x, dv.x, dv.y, tc.xs);
@@ -212,7 +264,7 @@ __device__ __forceinline__ void item_canonical(const QuantArgs &a, const Octet &
 // Transposed item (V in the cache; full octets only): 16 words of 8 tokens, one per
 // d of the block, and the octet's 8 scale bytes of this block.  Token pairs are
 // taken in load order: scale bytes and divisors of a pair right before its codes.
-template <bool SCALED>
+template <bool SCALED, bool ADAPT = false>
 __device__ __forceinline__ void item_transposed(const QuantArgs &a, const Octet &o, int b,
                                                 const uint4 (&u)[kOctet][2],
                                                 const TensorConsts &tc, const float2 *tab) {
@@ -227,8 +279,13 @@ __device__ __forceinline__ void item_transposed(const QuantArgs &a, const Octet 
     float xa[16], xb[16];                                                            \
     unpack16(u[2 * SEL], xa);                                                        \
     unpack16(u[2 * SEL + 1], xb);                                                    \
-    sc[2 * SEL] = scale_code(absmax16(xa), tc);                                      \
-    sc[2 * SEL + 1] = scale_code(absmax16(xb), tc);                                  \
+    const float ma = absmax16(xa), mb = absmax16(xb);                                \
+    sc[2 * SEL] = scale_code(ma, tc);                                                \
+    sc[2 * SEL + 1] = scale_code(mb, tc);                                            \
+    if constexpr (ADAPT) {                                                           \
+      sc[2 * SEL] = choose_scale46<SCALED>(xa, ma, sc[2 * SEL], tc, tab);            \
+      sc[2 * SEL + 1] = choose_scale46<SCALED>(xb, mb, sc[2 * SEL + 1], tc, tab);    \
+    }                                                                                \
     const float2 da = tab[sc[2 * SEL]], db = tab[sc[2 * SEL + 1]];                   \
     encode_pair_transposed<SEL, SCALED>(xa, xb, da.x, da.y, db.x, db.y, tc.xs, out); \
   }
@@ -277,8 +334,9 @@ __device__ __forceinline__ void load_octet(const QuantArgs &a, const Octet &o, i
 }  // namespace
 
 // Pass 1: per-workgroup maxima of |x| over the flat K and V tensors (no atomics:
-// each workgroup owns one slot of the partials array).  Each thread keeps up to
-// 4 vectors of K and 4 of V in flight.
+// each workgroup owns one slot of the partials array), as fp32 bit patterns.  Each
+// thread keeps up to 4 vectors of K and 4 of V in flight.  With K-smoothing the K
+// maximum is taken over x - mean (fp32), the mean of each element's channel.
 __global__ __launch_bounds__(kAmaxThreads) void quantize_amax_kernel(QuantArgs a) {
   __shared__ uint32_t s_red[2][kAmaxThreads / 64];
   const int64_t n16 = int64_t(a.H) * a.T * a.D / 8;   // uint4 vectors per tensor
@@ -286,7 +344,9 @@ __global__ __launch_bounds__(kAmaxThreads) void quantize_amax_kernel(QuantArgs a
   const uint4 *pk = reinterpret_cast<const uint4 *>(a.t[0].src);
   const uint4 *pv = reinterpret_cast<const uint4 *>(a.n_tensors > 1 ? a.t[1].src : a.t[0].src);
   const bool two = a.n_tensors > 1;
-  uint32_t mk = 0, mv = 0;
+  const float *kmean = a.t[0].mean;
+  const int64_t head_vecs = int64_t(a.T) * a.D / 8;
+  uint32_t mk = 0, mv = 0;   // fp32 bit patterns of |x|
   for (int64_t base = int64_t(blockIdx.x) * kAmaxThreads + threadIdx.x; base < n16;
        base += 4 * stride) {
     uint4 uk[4], uv[4];
@@ -302,12 +362,30 @@ __global__ __launch_bounds__(kAmaxThreads) void quantize_amax_kernel(QuantArgs a
     }
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const uint32_t q = vmax4(uk[j]), w = vmax4(uv[j]);
-      mk = max(mk, max(q & 0xFFFFu, q >> 16));
-      mv = max(mv, max(w & 0xFFFFu, w >> 16));
+      const int64_t i = base + j * stride;
+      if (kmean) {
+        if (i < n16) {
+          const int64_t hh = i / head_vecs;
+          const int d0 = int((i - hh * head_vecs) % (a.D / 8)) * 8;
+          const float4 *mp = reinterpret_cast<const float4 *>(kmean + hh * a.D + d0);
+          const float4 m0 = mp[0], m1 = mp[1];
+          const float mu[8] = {m0.x, m0.y, m0.z, m0.w, m1.x, m1.y, m1.z, m1.w};
+          const uint32_t w[4] = {uk[j].x, uk[j].y, uk[j].z, uk[j].w};
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const float x = __uint_as_float(e & 1 ? (w[e >> 1] & 0xFFFF0000u) : (w[e >> 1] << 16));
+            mk = max(mk, __float_as_uint(x - mu[e]) & 0x7FFFFFFFu);
+          }
+        }
+      } else {
+        const uint32_t q = vmax4(uk[j]);
+        mk = max(mk, max(q & 0xFFFFu, q >> 16) << 16);
+      }
+      const uint32_t w = vmax4(uv[j]);
+      mv = max(mv, max(w & 0xFFFFu, w >> 16) << 16);
     }
   }
-  uint32_t m[2] = {wave_max_u32(mk << 16), wave_max_u32(mv << 16)};   // fp32 bit patterns
+  uint32_t m[2] = {wave_max_u32(mk), wave_max_u32(mv)};
   const int w = threadIdx.x >> 6;
   if ((threadIdx.x & 63) == 0) {
     s_red[0][w] = m[0];
@@ -368,13 +446,24 @@ __global__ __launch_bounds__(kQuantThreads) void quantize_encode_kernel(QuantArg
     if (act) {
       const TensorConsts &tc = oc.tensor ? tc1 : tc0;
       const float2 *tab = s_tab[oc.tensor];
-      const bool tr = a.t[oc.tensor].transposed != 0;
+      const QuantTensor &qt = a.t[oc.tensor];
+      const bool tr = qt.transposed != 0;
       if (tc.xs == 1.0f) {
-        if (tr) item_transposed<false>(a, oc, b, u, tc, tab);
-        else item_canonical<false>(a, oc, b, u, tc, tab);
+        if (tr) {
+          if (qt.adaptive) item_transposed<false, true>(a, oc, b, u, tc, tab);
+          else item_transposed<false>(a, oc, b, u, tc, tab);
+        } else {
+          if (qt.mean) item_canonical<false, true>(a, oc, b, u, tc, tab);
+          else item_canonical<false>(a, oc, b, u, tc, tab);
+        }
       } else {
-        if (tr) item_transposed<true>(a, oc, b, u, tc, tab);
-        else item_canonical<true>(a, oc, b, u, tc, tab);
+        if (tr) {
+          if (qt.adaptive) item_transposed<true, true>(a, oc, b, u, tc, tab);
+          else item_transposed<true>(a, oc, b, u, tc, tab);
+        } else {
+          if (qt.mean) item_canonical<true, true>(a, oc, b, u, tc, tab);
+          else item_canonical<true>(a, oc, b, u, tc, tab);
+        }
       }
     }
     tile += gridDim.x;
@@ -518,6 +607,67 @@ __global__ __launch_bounds__(kQuantThreads) void quantize_fused_kernel(QuantArgs
   }
 }
 
+// K-smoothing channel sums, one level of the pairwise tree (reading note, "The
+// inference infrastructure": K-smoothing inside each frame chunk).  A workgroup
+// reduces `group` consecutive leaves of one head for all D channels: each of its
+// waves sums R = group / active-waves consecutive leaves per channel pair in
+// registers, pairwise (v[i] = v[2i] + v[2i+1], level by level), then the waves'
+// results are combined pairwise through LDS.  Leaf order and pairing are those of
+// the full tree over the padded token count, so the result is the same fp32 value
+// as that tree, whatever the number of levels and workgroups.
+template <int R>
+__global__ __launch_bounds__(1024) void channel_sum_kernel(MeanLevel a) {
+  __shared__ float2 s_part[16][64];
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int nodes = a.n_in / a.group;
+  const int h = blockIdx.x / nodes, node = blockIdx.x - h * nodes;
+  const int waves = a.group / R;           // a power of two, at most 16
+  const bool col = 2 * lane < a.D;         // lane = channel pair (2 lane, 2 lane + 1)
+  if (w < waves && col) {
+    float2 v[R];
+    const int leaf0 = node * a.group + w * R;
+#pragma unroll
+    for (int i = 0; i < R; ++i) {
+      const int leaf = leaf0 + i;
+      if (a.src16) {
+        v[i] = make_float2(0.0f, 0.0f);   // padding leaves are +0.0
+        if (leaf < a.T) {
+          const uint32_t x =
+              *reinterpret_cast<const uint32_t *>(a.src16 + (int64_t(h) * a.T + leaf) * a.D + 2 * lane);
+          v[i] = make_float2(__uint_as_float(x << 16), __uint_as_float(x & 0xFFFF0000u));
+        }
+      } else {
+        v[i] = *reinterpret_cast<const float2 *>(a.src32 + (int64_t(h) * a.n_in + leaf) * a.D + 2 * lane);
+      }
+    }
+#pragma unroll
+    for (int width = R; width > 1; width >>= 1)
+#pragma unroll
+      for (int i = 0; i < width / 2; ++i) v[i] = make_float2(v[2 * i].x + v[2 * i + 1].x, v[2 * i].y + v[2 * i + 1].y);
+    s_part[w][lane] = v[0];
+  }
+  __syncthreads();
+  for (int width = waves; width > 1; width >>= 1) {
+    float2 r = make_float2(0.0f, 0.0f);
+    if (w < width / 2 && col) {
+      const float2 p = s_part[2 * w][lane], q = s_part[2 * w + 1][lane];
+      r = make_float2(p.x + q.x, p.y + q.y);
+    }
+    __syncthreads();
+    if (w < width / 2 && col) s_part[w][lane] = r;
+    __syncthreads();
+  }
+  if (w == 0 && col) {
+    float2 r = s_part[0][lane];
+    if (a.last) {
+      const float t = float(a.T);
+      *reinterpret_cast<float2 *>(a.dst + int64_t(h) * a.D + 2 * lane) = make_float2(r.x / t, r.y / t);
+    } else {
+      *reinterpret_cast<float2 *>(a.dst + (int64_t(h) * nodes + node) * a.D + 2 * lane) = r;
+    }
+  }
+}
+
 namespace {
 constexpr int kMaxDevices = 64;
 int g_cu_count[kMaxDevices];
@@ -535,6 +685,49 @@ int cu_count(int dev) {
   return g_cu_count[dev];
 }
 }  // namespace
+
+namespace {
+int64_t pow2_at_least(int64_t n) {
+  int64_t p = 1;
+  while (p < n) p *= 2;
+  return p;
+}
+}  // namespace
+
+int launch_channel_mean(const uint16_t *k, int H, int T, int D, float *mean, float *ws, void *stream) {
+  if (H < 1 || T < 1 || D < 2 || D > 128 || D % 2) return NVFP4KV_EINVAL;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  MeanLevel a;
+  a.src16 = k;
+  a.src32 = nullptr;
+  a.H = H;
+  a.D = D;
+  a.T = T;
+  a.n_in = int32_t(pow2_at_least(T));
+  const size_t half = channel_mean_ws_floats(H, T, D) / 2;
+  int pingpong = 0;
+  while (true) {
+    a.group = a.n_in < kMeanGroup ? a.n_in : kMeanGroup;
+    const int nodes = a.n_in / a.group;
+    a.last = nodes == 1;
+    a.dst = a.last ? mean : ws + pingpong * half;
+    const int r = a.group >= 16 ? a.group / 16 : 1;
+    const dim3 grid(unsigned(int64_t(H) * nodes)), block(1024);
+    switch (r) {
+      case 1: hipLaunchKernelGGL(channel_sum_kernel<1>, grid, block, 0, s, a); break;
+      case 2: hipLaunchKernelGGL(channel_sum_kernel<2>, grid, block, 0, s, a); break;
+      case 4: hipLaunchKernelGGL(channel_sum_kernel<4>, grid, block, 0, s, a); break;
+      case 8: hipLaunchKernelGGL(channel_sum_kernel<8>, grid, block, 0, s, a); break;
+      default: hipLaunchKernelGGL(channel_sum_kernel<16>, grid, block, 0, s, a); break;
+    }
+    if (hipGetLastError() != hipSuccess) return NVFP4KV_EHIP;
+    if (a.last) return NVFP4KV_OK;
+    a.src16 = nullptr;
+    a.src32 = a.dst;
+    a.n_in = nodes;
+    pingpong ^= 1;
+  }
+}
 
 int launch_quantize(const QuantArgs &in, void *stream) {
   QuantArgs a = in;

@@ -25,7 +25,12 @@ class NVFP4KVError(RuntimeError):
 class KVCacheConfig(ctypes.Structure):
     _fields_ = [("n_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
                 ("tokens_per_frame", ctypes.c_int32), ("sink_frames", ctypes.c_int32),
-                ("window_frames", ctypes.c_int32), ("shot_frames", ctypes.c_int32)]
+                ("window_frames", ctypes.c_int32), ("shot_frames", ctypes.c_int32),
+                ("options", ctypes.c_int32)]
+
+
+K_SMOOTH = 1      # NVFP4KV_K_SMOOTH
+V_ADAPTIVE = 2    # NVFP4KV_V_ADAPTIVE
 
 
 def lib():
@@ -50,6 +55,7 @@ def lib():
             "kvcache_evict": (I, [P, ctypes.c_int32]),
             "kvcache_tokens": (I, [P, ctypes.POINTER(I64), ctypes.POINTER(I64)]),
             "kvcache_begin_shot": (I, [P]),
+            "kvcache_export_k_mean": (I, [P, ctypes.c_int32, P, P]),
             "kvcache_shot_sink": (I, [P, ctypes.POINTER(I64), ctypes.POINTER(ctypes.c_int32),
                                       ctypes.POINTER(I64)]),
             "kvcache_chunk_count": (I, [P, ctypes.POINTER(ctypes.c_int32)]),
@@ -124,9 +130,10 @@ class KVCache:
     """Sink + window NVFP4 KV cache on one device (see include/nvfp4kv.h)."""
 
     def __init__(self, n_heads, head_dim, tokens_per_frame, sink_frames, window_frames,
-                 device=None, shot_frames=0):
+                 device=None, shot_frames=0, k_smooth=False, v_adaptive=False):
+        opts = (K_SMOOTH if k_smooth else 0) | (V_ADAPTIVE if v_adaptive else 0)
         self.cfg = KVCacheConfig(n_heads, head_dim, tokens_per_frame, sink_frames, window_frames,
-                                 shot_frames)
+                                 shot_frames, opts)
         n = lib().kvcache_storage_bytes(ctypes.byref(self.cfg))
         if n == 0:
             raise ValueError("unsupported cache configuration")
@@ -222,3 +229,10 @@ class KVCache:
                                         _stream())
         _check(rc, "kvcache_export_chunk")
         return kc, ks, vc, vs, sk, sv
+
+    def export_k_mean(self, chunk_index):
+        """K-smoothing channel means [H, D] (fp32) of a resident chunk."""
+        mu = torch.empty((self.cfg.n_heads, self.cfg.head_dim), dtype=torch.float32, device=self.device)
+        _check(lib().kvcache_export_k_mean(self._h, chunk_index, ctypes.c_void_p(mu.data_ptr()), _stream()),
+               "kvcache_export_k_mean")
+        return mu

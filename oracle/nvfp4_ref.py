@@ -179,12 +179,13 @@ def _encode_blocks(ax, amax_b, s_t, M):
         q = (ax / np.where(live, eff, F32(1.0))[..., None]).astype(F32)
     mag = e2m1_encode(q)
     mag = np.where(live[..., None], mag, 0).astype(np.uint8)
-    val = (E2M1_VALUES[mag].astype(F32) * eff[..., None]).astype(F32)
-    d = (ax - val).astype(F32)
-    e = (d * d).astype(F32)
-    err = np.zeros(amax_b.shape, dtype=F32)
-    for i in range(BLOCK):
-        err = (err + e[..., i]).astype(F32)
+    with np.errstate(over="ignore", invalid="ignore"):   # huge blocks: the error is +inf
+        val = (E2M1_VALUES[mag].astype(F32) * eff[..., None]).astype(F32)
+        d = (ax - val).astype(F32)
+        e = (d * d).astype(F32)
+        err = np.zeros(amax_b.shape, dtype=F32)
+        for i in range(BLOCK):
+            err = (err + e[..., i]).astype(F32)
     return scale_codes, mag, err
 
 

@@ -38,6 +38,13 @@ int launch_export(const ExportArgs &a, void *) {
   ++g_calls[2];
   return 0;
 }
+int g_mean_calls = 0;
+int launch_channel_mean(const uint16_t *, int, int, int, float *, float *, void *) {
+  if (int rc = take_fail()) return rc;
+  ++g_mean_calls;
+  return 0;
+}
+int copy_device_floats(float *, const float *, size_t, void *) { return take_fail(); }
 int zero_device_bytes_blocking(void *, size_t) { return 0; }
 int zero_device_bytes_async(void *, size_t, void *) { return 0; }
 }  // namespace nvfp4kv
@@ -45,7 +52,12 @@ int zero_device_bytes_async(void *, size_t, void *) { return 0; }
 using namespace nvfp4kv;
 
 extern "C" {
-int stub_calls(int kind) { return g_calls[kind]; }
+int stub_calls(int kind) { return kind == 3 ? g_mean_calls : g_calls[kind]; }
+// options of the last quantize launch: bit 0 K mean given, bit 1 V adaptive
+int stub_last_quant_options(void) {
+  return (g_q.t[0].mean ? 1 : 0) | (g_q.n_tensors > 1 && g_q.t[1].adaptive ? 2 : 0);
+}
+int64_t stub_last_attn_k_mean(void) { return reinterpret_cast<int64_t>(g_a.k_mean); }
 void stub_fail_next(int rc) { g_fail_next = rc; }
 // segments of the last attention launch: out[3i..3i+2] = tok0, ntok, scale_slot
 int stub_last_segments(int32_t *out, int max) {

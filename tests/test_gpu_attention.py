@@ -241,3 +241,24 @@ def test_multi_shot_sink(ops, D):
         gc, gs, gt = got
         wc, ws_, wt = want
         assert np.array_equal(gc, wc) and np.array_equal(gs, ws_) and np.float32(gt) == wt, what
+
+
+@pytest.mark.parametrize("D", [64, 128])
+def test_k_smoothing_and_adaptive_v_attention(ops, D):
+    """Attention over a cache built with K-smoothing (the chunk's channel means added
+    back as a per-chunk logit term q . mean) and adaptive V scales matches the
+    oracle's cache model, over several chunks with different means and a wrapped
+    window."""
+    from gpu_util import dev
+    rng = np.random.default_rng(70 + D)
+    H, T_f, sink, window = 2, 40, 1, 4
+    cache = ops.KVCache(H, D, T_f, sink, window, k_smooth=True, v_adaptive=True)
+    model = CacheModel(H, D, T_f, sink, window, k_smooth=True, v_adaptive=True)
+    for nf in (2, 1, 2, 2):
+        T = nf * T_f
+        kx = (rng.standard_normal((H, T, D)) + rng.standard_normal((H, 1, D)) * 3).astype(np.float32)
+        k, v = W.f32_to_bf16_bits(kx), rand_bits(rng, (H, T, D))
+        cache.append(dev(k), dev(v), nf)
+        model.append(k, v)
+        q, ko, vo = (rand_bits(rng, (H, 100, D)) for _ in range(3))
+        run_case(ops, cache, model, q, ko, vo, 1.0 / np.sqrt(D), what=f"smooth D{D} tokens {model.n_tokens()}")

@@ -185,3 +185,39 @@ def test_append_wait_fallback_scan(ops):
             assert_codec_equal((vc, vs, sv[0]), quantize_ref(v), f"chunk {c} V")
     with pytest.raises(ops.NVFP4KVError):
         ops.set_wait_limit(-1)
+
+
+@pytest.mark.parametrize("D,T_f,frames", [(128, 40, [2, 1, 3]), (64, 8, [1, 2, 4]), (128, 1560, [3]),
+                                          (64, 64, [4, 1])])
+def test_append_k_smoothing_and_adaptive_v(ops, D, T_f, frames):
+    """Cache appends with K-smoothing and adaptive 4/6 V scales: the channel means
+    (pairwise fp32 tree; token counts 8 to 4680, padded to powers of two), K codes of
+    x - mean, V codes with the chosen block scales, and both tensor scales equal the
+    oracle's bit for bit.  K has per-channel offsets, a constant channel and a -0
+    channel; V has heavy tails so that both scale candidates occur."""
+    from gpu_util import dev, host
+    from oracle import channel_mean_ref
+    rng = np.random.default_rng(D + T_f)
+    H = 3
+    cache = ops.KVCache(H, D, T_f, 1, 6, k_smooth=True, v_adaptive=True)
+    chunks = []
+    for nf in frames:
+        T = nf * T_f
+        kx = (rng.standard_normal((H, T, D)) + rng.standard_normal((H, 1, D)) * 8).astype(np.float32)
+        kx[0, :, 3] = 1.5
+        kx[1, :, 5] = -0.0
+        k = W.f32_to_bf16_bits(kx)
+        v = t4_bits(rng, (H, T, D), 2.0)
+        cache.append(dev(k), dev(v), nf)
+        chunks.append((k, v))
+    for c, (k, v) in enumerate(chunks):
+        mu_want = channel_mean_ref(k)
+        mu = host(cache.export_k_mean(c))
+        assert np.array_equal(mu.view(np.uint32), mu_want.view(np.uint32)), f"chunk {c} means"
+        kc, ks, vc, vs, sk, sv = cache.export_chunk(c)
+        assert_codec_equal((host(kc), host(ks), host(sk)[0]), quantize_ref(k, mean=mu_want), f"chunk {c} K")
+        want_v = quantize_ref(v, adaptive=True)
+        plain_v = quantize_ref(v)
+        print(f"chunk {c}: {np.count_nonzero(want_v[1] != plain_v[1])} of {want_v[1].size} V blocks take the 4-scale",
+              flush=True)
+        assert_codec_equal((host(vc), host(vs), host(sv)[0]), want_v, f"chunk {c} V")

@@ -25,7 +25,7 @@ OK, EINVAL, ESHAPE, ECAPACITY, ESTATE, EHIP = 0, -1, -2, -3, -4, -5
 class Cfg(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in
                 ("n_heads", "head_dim", "tokens_per_frame", "sink_frames", "window_frames",
-                 "shot_frames")]
+                 "shot_frames", "options")]
 
 
 def declared_functions():
@@ -109,6 +109,14 @@ def test_storage_bytes_budget(real):
             if fixed is not None:
                 assert rest == fixed      # independent of the cache length
             fixed = rest
+    # K-smoothing adds the fp32 channel means of every scale slot (65 x H x D) and the
+    # mean reduction's workspace (two buffers of H x D node sums per 256 padded tokens)
+    plain = real.kvcache_storage_bytes(ctypes.byref(Cfg(12, 128, 1560, 3, 9)))
+    smooth = real.kvcache_storage_bytes(ctypes.byref(Cfg(12, 128, 1560, 3, 9, 0, 1)))
+    adaptive = real.kvcache_storage_bytes(ctypes.byref(Cfg(12, 128, 1560, 3, 9, 0, 2)))
+    assert adaptive == plain
+    assert smooth - plain == 65 * 12 * 128 * 4 + 2 * 12 * (32768 // 256) * 128 * 4
+    assert real.kvcache_storage_bytes(ctypes.byref(Cfg(12, 128, 1560, 3, 9, 0, 4))) == 0
 
 
 # ------------------------------------------------------------ host stub
