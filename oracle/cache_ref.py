@@ -10,7 +10,10 @@ key set is the union of the global sink, the shot-level sink and the window, wit
 duplicate tokens removed.  Reading note, "The inference infrastructure": each
 appended frame chunk is quantized to NVFP4 on its own (one tensor scale per chunk
 tensor), optionally with K-smoothing for K and adaptive scale selection for V
-(see nvfp4_ref; the smoothing means are added back to the dequantized K).
+(see nvfp4_ref; the smoothing means are added back to the dequantized K).  As the
+alternative the paper text's appendix A.2 "FP4 Quantization" sets against NVFP4,
+a cache may hold MXFP4 instead (see mxfp4_ref): 32-element blocks with E8M0
+scales and no tensor scale.
 
 Model: frames are numbered in append order.  The first ``sink_frames`` frames are
 the global sink; every later frame joins a FIFO window of at most
@@ -30,6 +33,7 @@ from dataclasses import dataclass
 import numpy as np
 
 from .nvfp4_ref import quantize_ref, dequantize_ref, channel_mean_ref
+from .mxfp4_ref import mx_quantize_ref, mx_dequantize_ref
 
 
 @dataclass
@@ -37,18 +41,19 @@ class Frame:
     chunk_id: int
     frame_in_chunk: int
     k_codes: np.ndarray   # uint8 [H, T_f, D/2]
-    k_scales: np.ndarray  # uint8 [H, T_f, D/16]
+    k_scales: np.ndarray  # uint8 [H, T_f, D/16] (MXFP4: E8M0 bytes [H, T_f, D/32])
     v_codes: np.ndarray
     v_scales: np.ndarray
     s_k: np.float32
     s_v: np.float32
     index: int = -1       # number of the frame in append order
     k_mean: np.ndarray = None   # K-smoothing channel means of the frame's chunk [H, D]
+    mx: bool = False            # MXFP4 codes and scales (s_k, s_v unused)
 
 
 class CacheModel:
     def __init__(self, n_heads, head_dim, tokens_per_frame, sink_frames, window_frames,
-                 shot_frames=0, k_smooth=False, v_adaptive=False):
+                 shot_frames=0, k_smooth=False, v_adaptive=False, mxfp4=False):
         self.H = n_heads
         self.D = head_dim
         self.T_f = tokens_per_frame
@@ -57,6 +62,8 @@ class CacheModel:
         self.S_s = shot_frames
         self.k_smooth = k_smooth      # K quantized after subtracting its chunk's channel means
         self.v_adaptive = v_adaptive  # V blocks take the better of the 6- and 4-scaled encodings
+        self.mxfp4 = mxfp4            # MXFP4 instead of NVFP4 (no smoothing, no adaptive scales)
+        assert not (mxfp4 and (k_smooth or v_adaptive)), "the options are NVFP4 steps"
         self.chunk_mean = {}          # chunk id -> K channel means [H, D] (K-smoothing only)
         self.sinks = []
         self.window = deque()
@@ -89,8 +96,12 @@ class CacheModel:
         assert T % self.T_f == 0
         n_frames = T // self.T_f
         mu = channel_mean_ref(k_bits) if self.k_smooth else None
-        kc, ks, sk = quantize_ref(k_bits, mean=mu)
-        vc, vs, sv = quantize_ref(v_bits, adaptive=self.v_adaptive)
+        if self.mxfp4:
+            (kc, ks), (vc, vs) = mx_quantize_ref(k_bits), mx_quantize_ref(v_bits)
+            sk = sv = np.float32(1.0)
+        else:
+            kc, ks, sk = quantize_ref(k_bits, mean=mu)
+            vc, vs, sv = quantize_ref(v_bits, adaptive=self.v_adaptive)
         cid = self.n_chunks
         self.n_chunks += 1
         self.chunk_codes[cid] = (kc, ks, sk, vc, vs, sv)
@@ -98,7 +109,8 @@ class CacheModel:
             self.chunk_mean[cid] = mu
         for f in range(n_frames):
             sl = slice(f * self.T_f, (f + 1) * self.T_f)
-            fr = Frame(cid, f, kc[:, sl], ks[:, sl], vc[:, sl], vs[:, sl], sk, sv, self.n_frames, mu)
+            fr = Frame(cid, f, kc[:, sl], ks[:, sl], vc[:, sl], vs[:, sl], sk, sv, self.n_frames, mu,
+                       self.mxfp4)
             self.n_frames += 1
             if len(self.sinks) < self.S_g:
                 self.sinks.append(fr)
@@ -127,7 +139,9 @@ class CacheModel:
         if not frs:
             z = np.zeros((self.H, 0, self.D))
             return z, z.copy()
-        ks = [dequantize_ref(f.k_codes, f.k_scales, f.s_k)
+        def deq(codes, scales, s_t, mx):
+            return mx_dequantize_ref(codes, scales) if mx else dequantize_ref(codes, scales, s_t)
+        ks = [deq(f.k_codes, f.k_scales, f.s_k, f.mx)
               + (0.0 if f.k_mean is None else f.k_mean.astype(np.float64)[:, None, :]) for f in frs]
-        vs = [dequantize_ref(f.v_codes, f.v_scales, f.s_v) for f in frs]
+        vs = [deq(f.v_codes, f.v_scales, f.s_v, f.mx) for f in frs]
         return np.concatenate(ks, axis=1), np.concatenate(vs, axis=1)
