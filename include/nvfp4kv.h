@@ -93,6 +93,25 @@ int nvfp4_quantize_kv(const uint16_t *x, int64_t H, int64_t T, int64_t D, uint8_
                       size_t workspace_bytes, void *stream);
 
 /* ------------------------------------------------------------------------------
+ * Standalone MXFP4 codec of one tensor: the block-scaled FP4 format the paper text's
+ * appendix A.2 ("FP4 Quantization") sets against NVFP4, as defined by the OCP
+ * Microscaling Formats (MX) specification v1.0 it cites.
+ *
+ *   x       bf16 [H, T, D], D % 32 == 0 (32 <= D <= 4096), H, T >= 1; finite.
+ *   codes   uint8 [H, T, D/2]: as for NVFP4 (element 2i in the low nibble, nibble =
+ *           sign << 3 | E2M1 magnitude code).
+ *   scales  uint8 [H, T, D/32]: E8M0 bytes E + 127 of the block scales 2^E.
+ * Recipe: per block of 32 along D, E = floor(log2(block max |x|)) - 2 clamped to
+ *   [-127, 127] (-127 for an all-zero block); code = E2M1(|x| / 2^E) rounded to
+ *   nearest-even, saturating at 6, with x's sign.  No tensor scale; one pass, no
+ *   workspace.
+ * Alignment: x 16 bytes, codes 8 bytes.
+ * Errors: EINVAL (null or misaligned pointer, H/T/D out of range, D % 32 != 0), EHIP.
+ * ------------------------------------------------------------------------------ */
+int mxfp4_quantize_kv(const uint16_t *x, int64_t H, int64_t T, int64_t D, uint8_t *codes,
+                      uint8_t *scales, void *stream);
+
+/* ------------------------------------------------------------------------------
  * Paged sink + window KV cache (paper section 4.2; reading note "The inference
  * infrastructure").
  *
@@ -118,6 +137,13 @@ int nvfp4_quantize_kv(const uint16_t *x, int64_t H, int64_t T, int64_t D, uint8_
  *                       (same tensor scale) and keeps the encoding with the smaller
  *                       fp32 squared error (ties: 6).  Decoding is unchanged.
  * Appends with options run the two-pass quantizer (plus the mean reduction).
+ *   NVFP4KV_MXFP4       the cache holds MXFP4 instead (see mxfp4_quantize_kv: 32-element
+ *                       blocks, E8M0 scales, no tensor scale; the paper text's appendix
+ *                       A.2 contrasts the two formats).  Appends run one single-pass
+ *                       kernel; attention dequantizes these tiles to bf16 and runs their
+ *                       QK^T and PV on the bf16 matrix cores with plain bf16 Q and P
+ *                       rounded to nearest-even.  Not combinable with the two options
+ *                       above (steps of the NVFP4 recipe).
  *
  * Supported: n_heads >= 1; head_dim 64 or 128; tokens_per_frame >= 8 and a multiple
  * of 8; sink_frames >= 0; window_frames >= 1; shot_frames >= 0 (0: no shot-level
@@ -127,6 +153,7 @@ int nvfp4_quantize_kv(const uint16_t *x, int64_t H, int64_t T, int64_t D, uint8_
  * ------------------------------------------------------------------------------ */
 #define NVFP4KV_K_SMOOTH 1
 #define NVFP4KV_V_ADAPTIVE 2
+#define NVFP4KV_MXFP4 4
 
 typedef struct {
   int32_t n_heads;
@@ -135,14 +162,14 @@ typedef struct {
   int32_t sink_frames;
   int32_t window_frames;
   int32_t shot_frames;
-  int32_t options;   /* NVFP4KV_K_SMOOTH | NVFP4KV_V_ADAPTIVE, or 0 */
+  int32_t options;   /* NVFP4KV_K_SMOOTH | NVFP4KV_V_ADAPTIVE, or NVFP4KV_MXFP4, or 0 */
 } kvcache_config;
 
 typedef struct kvcache kvcache; /* opaque host object */
 
 /* Device bytes the cache needs: 9/16 byte per cached K or V element (codes + block
- * scales, i.e. 9/8 T H d for K and V together), plus scratch of a fixed size that does
- * not grow with the cache: a per-chunk tensor-scale table, the quantizer's workspace
+ * scales, i.e. 9/8 T H d for K and V together; 17/32 byte for MXFP4), plus scratch of a
+ * fixed size that does not grow with the cache: a per-chunk tensor-scale table, the quantizer's workspace
  * and chunk_attention's load-balancing slots (one partial query-block result per
  * workgroup of a full-GPU launch: about 34.6 MB for head_dim 128, 17.8 MB for 64).
  * Returns 0 for an unsupported configuration. */
@@ -206,8 +233,9 @@ int chunk_attention(const kvcache *c, const uint16_t *q, const uint16_t *k_own,
 
 /* Copies chunk `chunk_index` (0-based append order), which must be fully resident,
  * out of the cache in the codec's layout: k_codes / v_codes uint8 [H, n*T_f, D/2],
- * k_scales / v_scales uint8 [H, n*T_f, D/16], k_scale / v_scale float[1] (device),
- * with n the chunk's frame count.  Device-to-device, on `stream`.
+ * k_scales / v_scales uint8 [H, n*T_f, D/16] (MXFP4: E8M0 bytes [H, n*T_f, D/32]),
+ * k_scale / v_scale float[1] (device; 1 for MXFP4), with n the chunk's frame count.
+ * Device-to-device, on `stream`.
  * Errors: EINVAL (null), ESTATE (chunk unknown or not fully resident), EHIP. */
 int kvcache_export_chunk(const kvcache *c, int32_t chunk_index, uint8_t *k_codes,
                          uint8_t *k_scales, uint8_t *v_codes, uint8_t *v_scales,

@@ -41,7 +41,9 @@ bool config_ok(const kvcache_config *c) {
       c->tokens_per_frame > (1 << 20))
     return false;
   if (c->sink_frames < 0 || c->window_frames < 1 || c->shot_frames < 0) return false;
-  if (c->options & ~(NVFP4KV_K_SMOOTH | NVFP4KV_V_ADAPTIVE)) return false;
+  if (c->options & ~(NVFP4KV_K_SMOOTH | NVFP4KV_V_ADAPTIVE | NVFP4KV_MXFP4)) return false;
+  // smoothing and adaptive 4/6 scales are steps of the NVFP4 recipe
+  if ((c->options & NVFP4KV_MXFP4) && (c->options & (NVFP4KV_K_SMOOTH | NVFP4KV_V_ADAPTIVE))) return false;
   if (c->sink_frames + c->window_frames + c->shot_frames > kMaxFrames) return false;
   // per-head planes are addressed with 32-bit offsets
   if (int64_t(c->sink_frames + c->window_frames + c->shot_frames) * c->tokens_per_frame * c->head_dim >=
@@ -57,9 +59,10 @@ bool make_layout(const kvcache_config *c, Layout *L) {
   if (H * L->rows * D > (int64_t(1) << 40)) return false;
   size_t off = 0;
   L->kcodes = off;  off = round_up(off + size_t(H * L->rows * D / 2));
-  L->kscales = off; off = round_up(off + size_t(H * L->rows * D / 16));
+  const int64_t block = (c->options & NVFP4KV_MXFP4) ? 32 : 16;   // elements per block scale
+  L->kscales = off; off = round_up(off + size_t(H * L->rows * D / block));
   L->vcodes = off;  off = round_up(off + size_t(H * L->rows * D / 2));
-  L->vscales = off; off = round_up(off + size_t(H * L->rows * D / 16));
+  L->vscales = off; off = round_up(off + size_t(H * L->rows * D / block));
   L->table = off;   off = round_up(off + sizeof(float) * 2 * kScaleSlots);
   L->ws = off;      off = round_up(off + sizeof(QuantWorkspace));
   L->attn_flags = off; off = round_up(off + sizeof(uint64_t) * attn_max_grid(int(D)));
@@ -129,6 +132,7 @@ struct kvcache {
   uint64_t *attn_flags() const { return reinterpret_cast<uint64_t *>(base + L.attn_flags); }
   float *attn_partials() const { return reinterpret_cast<float *>(base + L.attn_part); }
   bool k_smooth() const { return (cfg.options & NVFP4KV_K_SMOOTH) != 0; }
+  bool mx() const { return (cfg.options & NVFP4KV_MXFP4) != 0; }
   float *kmean(int32_t scale_slot) const {
     return reinterpret_cast<float *>(base + L.kmean) + int64_t(scale_slot) * cfg.n_heads * cfg.head_dim;
   }
@@ -247,6 +251,31 @@ int nvfp4_quantize_kv(const uint16_t *x, int64_t H, int64_t T, int64_t D, uint8_
   return launch_quantize(a, stream);
 }
 
+int mxfp4_quantize_kv(const uint16_t *x, int64_t H, int64_t T, int64_t D, uint8_t *codes,
+                      uint8_t *scales, void *stream) {
+  if (!x || !codes || !scales) return NVFP4KV_EINVAL;
+  if (!aligned(x, 16) || !aligned(codes, 8)) return NVFP4KV_EINVAL;
+  if (H < 1 || T < 1 || D < 32 || D % 32 != 0 || D > 4096) return NVFP4KV_EINVAL;
+  if (H * T * D >= (int64_t(1) << 40) || T > (int64_t(1) << 30) || H > (1 << 20))
+    return NVFP4KV_EINVAL;
+  QuantArgs a;
+  memset(&a, 0, sizeof(a));
+  a.t[0].src = x;
+  a.t[0].codes = codes;
+  a.t[0].scales = scales;
+  a.t[0].tensor_scale = nullptr;
+  a.t[0].transposed = 0;
+  a.n_tensors = 1;
+  a.H = int32_t(H);
+  a.T = int32_t(T);
+  a.D = int32_t(D);
+  a.tokens_per_frame = int32_t(T);
+  a.n_frames = 1;
+  a.rows = T;
+  a.frame_slot[0] = 0;
+  return launch_quantize_mx(a, stream);
+}
+
 size_t kvcache_storage_bytes(const kvcache_config *cfg) {
   Layout L;
   if (!make_layout(cfg, &L)) return 0;
@@ -355,7 +384,7 @@ int kvcache_append(kvcache *c, const uint16_t *k, const uint16_t *v, int32_t n_f
     const int rm = launch_channel_mean(k, cfg.n_heads, a.T, cfg.head_dim, c->kmean(sslot), c->kmean_ws(), stream);
     if (rm != NVFP4KV_OK) return rm;
   }
-  const int rc = launch_quantize(a, stream);
+  const int rc = c->mx() ? launch_quantize_mx(a, stream) : launch_quantize(a, stream);
   if (rc != NVFP4KV_OK) return rc;
   c->st = s;
   return NVFP4KV_OK;
@@ -446,6 +475,7 @@ int chunk_attention(const kvcache *c, const uint16_t *q, const uint16_t *k_own,
   a.n_q = int32_t(n_q);
   a.sm_scale_log2 = softmax_scale * 1.4426950408889634f;
   a.k_mean = c->k_smooth() ? c->kmean(0) : nullptr;
+  a.mx = c->mx() ? 1 : 0;
   a.partials = c->attn_partials();
   a.flags = c->attn_flags();
   a.epoch = ++c->attn_epoch;   // never reused, even if the launch fails
@@ -491,6 +521,7 @@ int kvcache_export_chunk(const kvcache *c, int32_t chunk_index, uint8_t *k_codes
   a.D = c->cfg.head_dim;
   a.T_f = c->cfg.tokens_per_frame;
   a.n_frames = rec.n_frames;
+  a.block = c->mx() ? 32 : 16;
   a.rows = c->L.rows;
   a.k_codes_out = k_codes;
   a.k_scales_out = k_scales;

@@ -63,6 +63,8 @@ namespace nvfp4kv {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
@@ -138,9 +140,9 @@ struct HeadPlanes {
   uint32_t rows;
 };
 
-template <int D>
+template <int D, bool MX>
 __device__ __forceinline__ HeadPlanes head_planes(const AttnArgs &a, int h) {
-  constexpr int nb = D / 16;
+  constexpr int nb = D / (MX ? 32 : 16);   // block scales per token
   HeadPlanes p;
   p.rows = uint32_t(a.rows);
   p.kc = a.kcodes + size_t(h) * a.rows * (D / 2);
@@ -153,10 +155,11 @@ __device__ __forceinline__ HeadPlanes head_planes(const AttnArgs &a, int h) {
 // Loads are unconditional: keys past `nval` (a multiple of 8, >= 8) re-read the
 // tile's last valid key or 8-key group, so every loaded byte is a valid code or
 // scale; those keys are masked out of the softmax.
-template <int D>
+template <int D, bool MX>
 __device__ __forceinline__ void load_packed(const HeadPlanes &hp, uint32_t tok, int nval,
                                             Packed<D> &p) {
-  constexpr int nb = D / 16;
+  constexpr int nb = D / 16;                 // 16-element K tasks per key
+  constexpr int nbs = D / (MX ? 32 : 16);    // block scales per key
 #pragma unroll
   for (int i = 0; i < Packed<D>::kTasks; ++i) {
     const int t = threadIdx.x + i * Cfg<D>::kThreads;
@@ -167,7 +170,7 @@ __device__ __forceinline__ void load_packed(const HeadPlanes &hp, uint32_t tok, 
       const uint2 c = *reinterpret_cast<const uint2 *>(hp.kc + (row * (D / 2) + uint32_t(b) * 8));
       p.kc[i][0] = c.x;
       p.kc[i][1] = c.y;
-      p.ks[i] = hp.ks[row * nb + uint32_t(b)];
+      p.ks[i] = hp.ks[row * nbs + uint32_t(MX ? b >> 1 : b)];
     }
     // V task: (d, 16-key group) = (t / 4, t % 4); two 8-key halves
     {
@@ -175,7 +178,7 @@ __device__ __forceinline__ void load_packed(const HeadPlanes &hp, uint32_t tok, 
       const int last8 = (nval >> 3) - 1;                 // last valid 8-key group
       const uint32_t h0 = uint32_t(min(2 * g, last8)), h1 = uint32_t(min(2 * g + 1, last8));
       const uint32_t cbase = uint32_t(d) * (hp.rows / 2) + (tok >> 1);
-      const uint32_t sbase = uint32_t(d >> 4) * hp.rows + tok;
+      const uint32_t sbase = uint32_t(d >> (MX ? 5 : 4)) * hp.rows + tok;
       const uint32_t *cp = reinterpret_cast<const uint32_t *>(hp.vc + cbase);
       const uint2 *sp = reinterpret_cast<const uint2 *>(hp.vs + sbase);
       p.vc[i][0] = cp[h0];
@@ -203,9 +206,61 @@ __device__ __forceinline__ void dequant16(uint32_t w0, uint32_t w1, const f16x2 
   o[7] = as_u32(fp4x2<3>(w1) * s[7]);
 }
 
-template <int D>
+// MXFP4 tiles dequantize to bf16 (exact: E2M1 x 2^e has at most 2 significant bits and
+// bf16 spans every scale the format produces for bf16 inputs).  The E8M0 byte s goes
+// into the converts' fp32 scale operand as its exponent field: the converts multiply
+// by 2^(exponent field - 127), which is exactly the E8M0 value, and read nothing else
+// of the operand (checked on gfx950 for every byte, with the sign and mantissa bits
+// set), so one shift places byte `byte` of a word of four scale bytes.
+template <int BYTE>
+__device__ __forceinline__ float e8m0_operand(uint32_t word) {
+  return __uint_as_float(BYTE < 3 ? word << (23 - 8 * BYTE) : word >> 1);
+}
+template <int SEL>
+__device__ __forceinline__ uint32_t fp4x2_bf16(uint32_t w, float scale) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, SEL));
+}
+// keys (2 SEL, 2 SEL + 1) of word w, each with its own block scale: the low half
+// from the convert with the first key's scale, the high half from the second's
+template <int SEL>
+__device__ __forceinline__ uint32_t fp4x2_bf16_2s(uint32_t w, float sa, float sb) {
+  return (fp4x2_bf16<SEL>(w, sa) & 0xFFFFu) | (fp4x2_bf16<SEL>(w, sb) & 0xFFFF0000u);
+}
+
+template <int D, bool MX>
 __device__ __forceinline__ void dequant_store(const Packed<D> &p, uint16_t *Ks, uint16_t *Vs) {
   constexpr int nb = D / 16;
+  if constexpr (MX) {
+#pragma unroll
+    for (int i = 0; i < Packed<D>::kTasks; ++i) {
+      const int t = threadIdx.x + i * Cfg<D>::kThreads;
+      {
+        const int key = t / nb, b = t % nb;
+        const float sk = e8m0_operand<0>(p.ks[i]);
+        const uint32_t w0 = p.kc[i][0], w1 = p.kc[i][1];
+        *reinterpret_cast<uint4 *>(Ks + ks_off<D>(key, 2 * b)) =
+            make_uint4(fp4x2_bf16<0>(w0, sk), fp4x2_bf16<1>(w0, sk), fp4x2_bf16<2>(w0, sk), fp4x2_bf16<3>(w0, sk));
+        *reinterpret_cast<uint4 *>(Ks + ks_off<D>(key, 2 * b + 1)) =
+            make_uint4(fp4x2_bf16<0>(w1, sk), fp4x2_bf16<1>(w1, sk), fp4x2_bf16<2>(w1, sk), fp4x2_bf16<3>(w1, sk));
+      }
+      {
+        const int d = t >> 2, g = t & 3;
+        const uint32_t w0 = p.vc[i][0], w1 = p.vc[i][1];
+        uint32_t o[8];
+        o[0] = fp4x2_bf16_2s<0>(w0, e8m0_operand<0>(p.vs[i][0]), e8m0_operand<1>(p.vs[i][0]));
+        o[1] = fp4x2_bf16_2s<1>(w0, e8m0_operand<2>(p.vs[i][0]), e8m0_operand<3>(p.vs[i][0]));
+        o[2] = fp4x2_bf16_2s<2>(w0, e8m0_operand<0>(p.vs[i][1]), e8m0_operand<1>(p.vs[i][1]));
+        o[3] = fp4x2_bf16_2s<3>(w0, e8m0_operand<2>(p.vs[i][1]), e8m0_operand<3>(p.vs[i][1]));
+        o[4] = fp4x2_bf16_2s<0>(w1, e8m0_operand<0>(p.vs[i][2]), e8m0_operand<1>(p.vs[i][2]));
+        o[5] = fp4x2_bf16_2s<1>(w1, e8m0_operand<2>(p.vs[i][2]), e8m0_operand<3>(p.vs[i][2]));
+        o[6] = fp4x2_bf16_2s<2>(w1, e8m0_operand<0>(p.vs[i][3]), e8m0_operand<1>(p.vs[i][3]));
+        o[7] = fp4x2_bf16_2s<3>(w1, e8m0_operand<2>(p.vs[i][3]), e8m0_operand<3>(p.vs[i][3]));
+        *reinterpret_cast<uint4 *>(Vs + vs_off(d, 2 * g)) = make_uint4(o[0], o[1], o[4], o[5]);
+        *reinterpret_cast<uint4 *>(Vs + vs_off(d, 2 * g + 1)) = make_uint4(o[2], o[3], o[6], o[7]);
+      }
+    }
+    return;
+  }
 #pragma unroll
   for (int i = 0; i < Packed<D>::kTasks; ++i) {
     const int t = threadIdx.x + i * Cfg<D>::kThreads;
@@ -290,6 +345,21 @@ __device__ __forceinline__ void store_own_v(const uint32_t (&v)[8], uint16_t *Vs
   *reinterpret_cast<uint2 *>(Vs + vs_off(d + 1, 2 * g16 + 1) + off) = make_uint2(hi[2], hi[3]);
 }
 
+// Value of lane l ^ 32 combined with lane l's own, through the lane-half swap
+// (no LDS round trip); both halves get the same result.
+__device__ __forceinline__ float other_half_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float other_half_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ uint32_t other_half_umax(uint32_t x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+  return max(uint32_t(r[0]), uint32_t(r[1]));
+}
+
 struct Softmax {
   float m;      // running max (log2 units) of the lane's query
   float l;      // partial row sum over this lane's keys
@@ -325,7 +395,9 @@ __device__ __forceinline__ void qk_tile(const uint16_t *Ks, const u32x4 (&qr)[D 
 // Online softmax of S^T, then O^T += V^T P^T.
 // `bias` (per lane, i.e. per query; log2 units) is added to every logit of the
 // tile: the K-smoothing term q . mean of the tile's chunk, or 0.
-template <int D, bool MASK>
+// PB: V^T in LDS is bf16 (MXFP4 tiles) and P enters the product as bf16 (rounded to
+// nearest-even); otherwise both are fp16 (P rounded toward zero).
+template <int D, bool MASK, bool PB = false>
 __device__ __forceinline__ void softmax_pv(const uint16_t *Vs, f32x16 (&s)[2], float cmul, float bias,
                                            int nval, Softmax &sm, f32x16 (&acc)[D / 32]) {
   const int lane = threadIdx.x & 63, half = lane >> 5, l32 = lane & 31;
@@ -340,10 +412,16 @@ __device__ __forceinline__ void softmax_pv(const uint16_t *Vs, f32x16 (&s)[2], f
         if (key >= nval) s[kb][r] = -INFINITY;
       }
   }
-  float mx = fmaxf(s[0][0], s[1][0]);
+  // one chain of 3-input maxima over the lane's 32 logits
+  float mx = fmaxf(fmaxf(s[0][0], s[0][1]), s[0][2]);
 #pragma unroll
-  for (int r = 1; r < 16; ++r) mx = fmaxf(mx, fmaxf(s[0][r], s[1][r]));
-  mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+  for (int j = 3; j < 31; j += 2) {
+    const float x0 = j < 16 ? s[0][j] : s[1][j - 16];
+    const float x1 = j + 1 < 16 ? s[0][j + 1] : s[1][j + 1 - 16];
+    mx = fmaxf(fmaxf(mx, x0), x1);
+  }
+  mx = fmaxf(mx, s[1][15]);
+  mx = other_half_max(mx);
   const float tmax = mx * cmul + bias;
   // raise the running max only when this tile exceeds it by more than kLazy
   if (__any(tmax > sm.m + kLazy)) {
@@ -354,20 +432,20 @@ __device__ __forceinline__ void softmax_pv(const uint16_t *Vs, f32x16 (&s)[2], f
 #pragma unroll
     for (int db = 0; db < D / 32; ++db) acc[db] *= alpha;
   }
-  f16x8 vf[D / 32][4];
+  u32x4 vf[D / 32][4];
 #pragma unroll
   for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
     for (int db = 0; db < D / 32; ++db)
-      vf[db][ks] = *reinterpret_cast<const f16x8 *>(Vs + vs_off(db * 32 + l32, 2 * ks + half));
+      vf[db][ks] = *reinterpret_cast<const u32x4 *>(Vs + vs_off(db * 32 + l32, 2 * ks + half));
   const float mneg = bias - sm.m;
   float lsum = 0.0f;
-  f16x8 p[4];    // [16-key step]
+  u32x4 p[4];    // [16-key step], P as fp16 or bf16 pairs
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
     for (int hh = 0; hh < 2; ++hh) {
-      f16x8 v;
+      u32x4 v;
 #pragma unroll
       for (int i = 0; i < 8; i += 2) {
         float e0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][8 * hh + i], cmul, mneg));
@@ -378,10 +456,15 @@ __device__ __forceinline__ void softmax_pv(const uint16_t *Vs, f32x16 (&s)[2], f
           if (key0 >= nval) e0 = 0.0f;
           if (key0 + 1 >= nval) e1 = 0.0f;
         }
-        const f16x2 pr = pkrtz(e0, e1);
-        lsum = __builtin_amdgcn_fdot2(pr, f16x2{1.0f16, 1.0f16}, lsum, false);
-        v[i] = pr[0];
-        v[i + 1] = pr[1];
+        if constexpr (PB) {
+          const bf16x2 pr = __builtin_convertvector(f32x2{e0, e1}, bf16x2);
+          lsum = __builtin_amdgcn_fdot2_f32_bf16(pr, bf16x2{__bf16(1.0f), __bf16(1.0f)}, lsum, false);
+          v[i / 2] = __builtin_bit_cast(uint32_t, pr);
+        } else {
+          const f16x2 pr = pkrtz(e0, e1);
+          lsum = __builtin_amdgcn_fdot2(pr, f16x2{1.0f16, 1.0f16}, lsum, false);
+          v[i / 2] = as_u32(pr);
+        }
       }
       p[2 * kb + hh] = v;
     }
@@ -389,8 +472,14 @@ __device__ __forceinline__ void softmax_pv(const uint16_t *Vs, f32x16 (&s)[2], f
 #pragma unroll
   for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
-    for (int db = 0; db < D / 32; ++db)
-      acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vf[db][ks], p[ks], acc[db], 0, 0, 0);
+    for (int db = 0; db < D / 32; ++db) {
+      if constexpr (PB)
+        acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, vf[db][ks]),
+                                                          __builtin_bit_cast(bf16x8, p[ks]), acc[db], 0, 0, 0);
+      else
+        acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, vf[db][ks]),
+                                                         __builtin_bit_cast(f16x8, p[ks]), acc[db], 0, 0, 0);
+    }
 }
 
 // Loads the wave's 32 query rows as MFMA B operands (bf16 bits).
@@ -529,7 +618,9 @@ __device__ __forceinline__ void write_out(const AttnArgs &a, int h, int qi, cons
 
 }  // namespace
 
-template <int D>
+// MX: the cache holds MXFP4 (dequantized to bf16, QK^T and PV of its tiles on the
+// bf16 matrix cores with plain bf16 Q); otherwise NVFP4.
+template <int D, bool MX>
 __global__ __launch_bounds__(Cfg<D>::kThreads, Cfg<D>::kWgPerCu) void chunk_attention_kernel(AttnArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t Ks[2][kKsElems<D>];
   __shared__ __attribute__((aligned(16))) uint16_t Vs[2][kVsElems<D>];
@@ -592,33 +683,34 @@ __global__ __launch_bounds__(Cfg<D>::kThreads, Cfg<D>::kWgPerCu) void chunk_atte
     while (true) {
       // ---- cache tiles (NVFP4)
       if (r0 < cache_tiles) {
-        // Q as fp16 with a per-query power-of-two scale 2^sh (row max -> [2^14, 2^15))
+        // NVFP4: Q as fp16 with a per-query power-of-two scale 2^sh (row max -> [2^14,
+        // 2^15)); MXFP4: plain bf16 Q
         load_q<D>(a, h, q0, qr);
-        float cq;
-        {
+        float cq = 1.0f;
+        if constexpr (!MX) {
           uint32_t mx = 0;
-  #pragma unroll
+#pragma unroll
           for (int st = 0; st < D / 16; ++st)
-  #pragma unroll
+#pragma unroll
             for (int j = 0; j < 4; ++j) {
               const uint32_t v = qr[st][j] & 0x7FFF7FFFu;
               mx = max(mx, max(v & 0xFFFFu, v >> 16));
             }
-          mx = max(mx, uint32_t(__shfl_xor(int(mx), 32, 64)));
+          mx = other_half_umax(mx);
           const int e = int(mx >> 7) - 127;   // floor(log2(row max)) (bf16 normals)
           int sh = mx ? 14 - e : 0;
           sh = max(-110, min(100, sh));
           cq = __builtin_ldexpf(1.0f, -sh);
-  #pragma unroll
+#pragma unroll
           for (int st = 0; st < D / 16; ++st)
-  #pragma unroll
+#pragma unroll
             for (int j = 0; j < 4; ++j) {
               const uint32_t v = qr[st][j];
               qr[st][j] = as_u32(pkrtz(__builtin_ldexpf(__uint_as_float(v << 16), sh),
                                        __builtin_ldexpf(__uint_as_float(v & 0xFFFF0000u), sh)));
             }
         }
-        const HeadPlanes hp = head_planes<D>(a, h);
+        const HeadPlanes hp = head_planes<D, MX>(a, h);
         int cur_seg = -1;
         float cmul = 0.0f;
         // per segment: s_K folds into the logit multiplier; the accumulator moves to
@@ -645,7 +737,7 @@ __global__ __launch_bounds__(Cfg<D>::kThreads, Cfg<D>::kWgPerCu) void chunk_atte
               dot += float(qv[0]) * m0.x + float(qv[1]) * m0.y + float(qv[2]) * m0.z + float(qv[3]) * m0.w +
                      float(qv[4]) * m1.x + float(qv[5]) * m1.y + float(qv[6]) * m1.z + float(qv[7]) * m1.w;
             }
-            dot += __shfl_xor(dot, 32, 64);
+            dot = other_half_sum(dot);
             kbias = dot * cq * a.sm_scale_log2;
           }
           if (sv > 0.0f) {
@@ -664,24 +756,24 @@ __global__ __launch_bounds__(Cfg<D>::kThreads, Cfg<D>::kWgPerCu) void chunk_atte
           int cs, ck;
           nth_full(a, r0, cs, ck);
           Packed<D> pk;
-          load_packed<D>(hp, uint32_t(a.seg[cs].tok0 + ck), kBN, pk);
-          dequant_store<D>(pk, Ks[0], Vs[0]);
+          load_packed<D, MX>(hp, uint32_t(a.seg[cs].tok0 + ck), kBN, pk);
+          dequant_store<D, MX>(pk, Ks[0], Vs[0]);
           int ns = cs, nk = ck;
           bool have_next = r0 + 1 < f1 && next_full(a, ns, nk);
           int ltok = have_next ? a.seg[ns].tok0 + nk : a.seg[cs].tok0 + ck;
-          load_packed<D>(hp, uint32_t(ltok), kBN, pk);
+          load_packed<D, MX>(hp, uint32_t(ltok), kBN, pk);
           __syncthreads();
           int buf = 0;
           for (int i = r0;; ++i) {
             enter_segment(cs);
-            qk_tile<D, false>(Ks[buf], qr, s);
+            qk_tile<D, MX>(Ks[buf], qr, s);
             // stage tile i+1 while the MFMAs run, then fetch the bytes of tile i+2
-            dequant_store<D>(pk, Ks[buf ^ 1], Vs[buf ^ 1]);
+            dequant_store<D, MX>(pk, Ks[buf ^ 1], Vs[buf ^ 1]);
             int s2 = ns, k2 = nk;
             const bool have_n2 = have_next && i + 2 < f1 && next_full(a, s2, k2);
             if (have_n2) ltok = a.seg[s2].tok0 + k2;
-            load_packed<D>(hp, uint32_t(ltok), kBN, pk);
-            softmax_pv<D, false>(Vs[buf], s, cmul, kbias, kBN, sm, acc);
+            load_packed<D, MX>(hp, uint32_t(ltok), kBN, pk);
+            softmax_pv<D, false, MX>(Vs[buf], s, cmul, kbias, kBN, sm, acc);
             __syncthreads();
             if (!have_next) break;
             buf ^= 1;
@@ -699,12 +791,12 @@ __global__ __launch_bounds__(Cfg<D>::kThreads, Cfg<D>::kWgPerCu) void chunk_atte
           const int tn = a.seg[cs].ntok % kBN;
           const int ck = a.seg[cs].ntok - tn;
           Packed<D> pk;
-          load_packed<D>(hp, uint32_t(a.seg[cs].tok0 + ck), tn, pk);
-          dequant_store<D>(pk, Ks[0], Vs[0]);
+          load_packed<D, MX>(hp, uint32_t(a.seg[cs].tok0 + ck), tn, pk);
+          dequant_store<D, MX>(pk, Ks[0], Vs[0]);
           enter_segment(cs);
           __syncthreads();
-          qk_tile<D, false>(Ks[0], qr, s);
-          softmax_pv<D, true>(Vs[0], s, cmul, kbias, tn, sm, acc);
+          qk_tile<D, MX>(Ks[0], qr, s);
+          softmax_pv<D, true, MX>(Vs[0], s, cmul, kbias, tn, sm, acc);
           __syncthreads();
         }
       }
@@ -829,10 +921,10 @@ __global__ __launch_bounds__(Cfg<D>::kThreads, Cfg<D>::kWgPerCu) void chunk_atte
             acc[db][4 * gq + 3] += o[db][gq][1].y * f;
           }
       }
-      write_out<D>(a, h, qi, acc, 1.0f / (lsum + __shfl_xor(lsum, 32, 64)));
+      write_out<D>(a, h, qi, acc, 1.0f / other_half_sum(lsum));
     } else {
       // ---- the whole block here (or all of it after giving up waiting)
-      write_out<D>(a, h, qi, acc, vunit / (sm.l + __shfl_xor(sm.l, 32, 64)));
+      write_out<D>(a, h, qi, acc, vunit / other_half_sum(sm.l));
     }
     __syncthreads();   // LDS buffers and s_ready are reused by the next range
   }
@@ -884,7 +976,10 @@ int launch_attention_d(AttnArgs a, hipStream_t s) {
   const int64_t wmax = a.w_tail;   // the largest weight
   if (grid > a.work / wmax) grid = a.work / wmax;
   if (grid < 1) grid = 1;
-  hipLaunchKernelGGL(chunk_attention_kernel<D>, dim3(unsigned(grid)), dim3(Cfg<D>::kThreads), 0, s, a);
+  if (a.mx)
+    hipLaunchKernelGGL((chunk_attention_kernel<D, true>), dim3(unsigned(grid)), dim3(Cfg<D>::kThreads), 0, s, a);
+  else
+    hipLaunchKernelGGL((chunk_attention_kernel<D, false>), dim3(unsigned(grid)), dim3(Cfg<D>::kThreads), 0, s, a);
   return NVFP4KV_HIP_OK(hipGetLastError());
 }
 }  // namespace

@@ -1,5 +1,6 @@
 // Copies one resident chunk out of the cache into the codec layout (K and V codes
-// [h][token][D/2], scales [h][token][D/16], and the two fp32 tensor scales), and
+// [h][token][D/2], scales [h][token][D/block] with block 16 for NVFP4 and 32 for
+// MXFP4, and the two fp32 tensor scales, 1 for MXFP4), and
 // small device utilities.  V is stored transposed in the cache ([h][d][token/2]),
 // so its codes are regathered here nibble by nibble.  Not on the hot path.
 
@@ -8,7 +9,7 @@
 namespace nvfp4kv {
 
 __global__ void export_chunk_kernel(ExportArgs a) {
-  const int nb = a.D / 16;
+  const int nb = a.D / a.block;
   const int64_t ntok = int64_t(a.n_frames) * a.T_f;
   const int64_t n_codes = int64_t(a.H) * ntok * (a.D / 2);
   const int64_t n_scales = int64_t(a.H) * ntok * nb;

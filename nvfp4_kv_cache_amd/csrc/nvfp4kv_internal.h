@@ -107,7 +107,7 @@ struct AttnArgs {
   // cost weights of a cache full tile, a ragged tail and an own full tile; a block's
   // total weight; the work list is cut by weight
   int32_t w_cfull, w_tail, w_ofull, w_block;
-  int32_t pad;
+  int32_t mx;                 // 1: the cache holds MXFP4 (E8M0 scales per 32), 0: NVFP4
   int64_t work;               // query blocks x block weight
   const float *k_mean;        // K-smoothing means [scale slot][H][D], or null
   float *partials;            // [max grid][slot]
@@ -123,6 +123,7 @@ struct ExportArgs {
   const float *scale_table;
   int32_t scale_slot;
   int32_t H, D, T_f, n_frames;
+  int32_t block;              // elements per block scale: 16 (NVFP4) or 32 (MXFP4)
   int64_t rows;
   uint8_t *k_codes_out, *k_scales_out, *v_codes_out, *v_scales_out;
   float *k_scale_out, *v_scale_out;
@@ -131,6 +132,8 @@ struct ExportArgs {
 
 // Launchers: return 0 or a negative nvfp4kv_status (EHIP).  `stream` is hipStream_t.
 int launch_quantize(const QuantArgs &a, void *stream);
+// MXFP4 (32-element blocks, E8M0 scales, no tensor scale): one pass
+int launch_quantize_mx(const QuantArgs &a, void *stream);
 int launch_attention(const AttnArgs &a, void *stream);
 int launch_export(const ExportArgs &a, void *stream);
 // K-smoothing channel means of one chunk tensor k [H][T][D] into mean [H][D]; ws holds

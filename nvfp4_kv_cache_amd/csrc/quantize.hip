@@ -607,6 +607,119 @@ __global__ __launch_bounds__(kQuantThreads) void quantize_fused_kernel(QuantArgs
   }
 }
 
+// MXFP4 (paper text, appendix A.2 "FP4 Quantization", and the OCP Microscaling
+// Formats (MX) specification v1.0 it cites): blocks of 32 along head_dim, each with a
+// power-of-two scale 2^E stored as the E8M0 byte E + 127, E = floor(log2(block max))
+// - 2 clamped to [-127, 127] (-127 for an all-zero block); element code =
+// E2M1(x * 2^-E) nearest-even, saturating at 6.  No tensor scale: every block is
+// encoded on its own, so one pass reads the chunk once with no grid-wide step.
+//
+// The items are those of the NVFP4 kernels (an octet of tokens x one 16-element
+// half of an MX block); the two halves of a block are neighbouring lanes (lanes run
+// over 16-element blocks fastest and D/16 is even), which exchange their maxima with
+// one DPP move.  The scaling by 2^-E is exact (2^-E is a normal fp32 and the product
+// can only lose bits far below the first E2M1 threshold 0.25), and the convert
+// rounds to nearest-even and saturates like the recipe.
+
+// E8M0 exponent E of a block whose largest |x| has the bf16 bit pattern m (sign
+// cleared): floor(log2) from the exponent field, or from the mantissa's leading bit
+// for a subnormal; -2; clamped.
+__device__ __forceinline__ int mx_exponent(uint32_t m) {
+  const int ef = int(m >> 7);
+  const int fl = ef > 0 ? ef - 127 : -133 + (31 - __builtin_clz(m | 1u));
+  return m == 0 ? -127 : max(-127, min(127, fl - 2));
+}
+
+// the largest |x| bits of the lane's 16 values of token j, combined with the other
+// half of the block (lane ^ 1)
+__device__ __forceinline__ uint32_t mx_block_max(const uint4 (&u)[2]) {
+  const uint32_t p = vmax4(u[0]), q = vmax4(u[1]);
+  const uint32_t m = max(max(p & 0xFFFFu, p >> 16), max(q & 0xFFFFu, q >> 16));
+  // quad_perm [1, 0, 3, 2]: the neighbouring lane's value
+  const uint32_t o = uint32_t(__builtin_amdgcn_mov_dpp(int(m), 0xB1, 0xF, 0xF, false));
+  return max(m, o);
+}
+
+__device__ __forceinline__ float pow2_neg(int e) { return __uint_as_float(uint32_t(127 - e) << 23); }
+
+__global__ __launch_bounds__(kQuantThreads) void quantize_mx_kernel(QuantArgs a) {
+  const int tid = threadIdx.x;
+  const int nb = a.D >> 4;
+  const int opt = kQuantThreads / nb;
+  const int b = tid % nb, o = tid / nb;
+  for (int tile = blockIdx.x; tile < a.total_tiles; tile += gridDim.x) {
+    // threads past the tile's octets (when D/16 does not divide the workgroup) redo
+    // its last octet, without storing: every lane takes part in the maxima exchange
+    const Octet oc = locate_octet(a, tile, min(o, opt - 1));
+    uint4 u[kOctet][2];
+    load_octet(a, oc, b, u);
+    const QuantTensor &qt = a.t[oc.tensor];
+    const int nmx = a.D >> 5;                 // MX blocks per token
+    const bool lead = (b & 1) == 0;           // writes the block's scale byte(s)
+    if (qt.transposed) {
+      // V in the cache: 16 words of 8 tokens (one per d of this half block) and, from
+      // the lead lane, the octet's 8 scale bytes of the MX block
+      uint32_t out[16];
+      uint32_t sb[kOctet];
+#pragma unroll
+      for (int d = 0; d < 16; ++d) out[d] = 0u;
+#define NVFP4KV_MX_PAIR(SEL)                                                           \
+  {                                                                                    \
+    const int ea = mx_exponent(mx_block_max(u[2 * SEL]));                              \
+    const int eb = mx_exponent(mx_block_max(u[2 * SEL + 1]));                          \
+    sb[2 * SEL] = uint32_t(ea + 127);                                                  \
+    sb[2 * SEL + 1] = uint32_t(eb + 127);                                              \
+    float xa[16], xb[16];                                                              \
+    unpack16(u[2 * SEL], xa);                                                          \
+    unpack16(u[2 * SEL + 1], xb);                                                      \
+    const float ia = pow2_neg(ea), ib = pow2_neg(eb);                                  \
+    _Pragma("unroll") for (int d = 0; d < 16; ++d) out[d] = cvt_fp4<SEL>(out[d], xa[d] * ia, xb[d] * ib); \
+  }
+      NVFP4KV_MX_PAIR(0)
+      NVFP4KV_MX_PAIR(1)
+      NVFP4KV_MX_PAIR(2)
+      NVFP4KV_MX_PAIR(3)
+#undef NVFP4KV_MX_PAIR
+      if (o < opt && oc.nvalid == kOctet) {
+        uint8_t *dst = qt.codes + (int64_t(oc.h) * a.D + 16 * b) * (a.rows / 2) + oc.row / 2;
+#pragma unroll
+        for (int d = 0; d < 16; ++d) *reinterpret_cast<uint32_t *>(dst + d * (a.rows / 2)) = out[d];
+        if (lead)
+          *reinterpret_cast<uint2 *>(qt.scales + (int64_t(oc.h) * nmx + (b >> 1)) * a.rows + oc.row) =
+              make_uint2(sb[0] | (sb[1] << 8) | (sb[2] << 16) | (sb[3] << 24),
+                         sb[4] | (sb[5] << 8) | (sb[6] << 16) | (sb[7] << 24));
+      }
+    } else {
+      // codec layout: per token, 8 code bytes and (lead lane) the block's scale byte
+#pragma unroll
+      for (int j = 0; j < kOctet; ++j) {
+        const int e = mx_exponent(mx_block_max(u[j]));
+        float x[16];
+        unpack16(u[j], x);
+        const float inv = pow2_neg(e);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) x[i] *= inv;
+        uint32_t c[2] = {0u, 0u};
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+          const float *y = x + 8 * hh;
+          c[hh] = cvt_fp4<0>(c[hh], y[0], y[1]);
+          c[hh] = cvt_fp4<1>(c[hh], y[2], y[3]);
+          c[hh] = cvt_fp4<2>(c[hh], y[4], y[5]);
+          c[hh] = cvt_fp4<3>(c[hh], y[6], y[7]);
+        }
+        if (o < opt && j < oc.nvalid) {
+          const int64_t row = int64_t(oc.h) * a.rows + oc.row + j;
+          *reinterpret_cast<uint2 *>(qt.codes + row * (a.D / 2) + b * 8) = make_uint2(c[0], c[1]);
+          if (lead) qt.scales[row * nmx + (b >> 1)] = uint8_t(e + 127);
+        }
+      }
+    }
+  }
+  // no tensor scale: the chunk's scale-table entries read 1
+  if (blockIdx.x == 0 && tid < a.n_tensors && a.t[tid].tensor_scale) *a.t[tid].tensor_scale = 1.0f;
+}
+
 // K-smoothing channel sums, one level of the pairwise tree (reading note, "The
 // inference infrastructure": K-smoothing inside each frame chunk).  A workgroup
 // reduces `group` consecutive leaves of one head for all D channels: each of its
@@ -727,6 +840,26 @@ int launch_channel_mean(const uint16_t *k, int H, int T, int D, float *mean, flo
     a.n_in = nodes;
     pingpong ^= 1;
   }
+}
+
+int launch_quantize_mx(const QuantArgs &in, void *stream) {
+  QuantArgs a = in;
+  const int nb = a.D / 16;
+  if (a.D % 32 != 0 || nb > kQuantThreads || a.tokens_per_frame < 1 || a.n_frames < 1)
+    return NVFP4KV_EINVAL;
+  a.tile_tokens = kOctet * (kQuantThreads / nb);
+  a.tiles_per_head = int32_t((int64_t(a.T) + a.tile_tokens - 1) / a.tile_tokens);
+  const int64_t total = int64_t(a.n_tensors) * a.H * a.tiles_per_head;
+  if (total >= (int64_t(1) << 31)) return NVFP4KV_EINVAL;
+  a.total_tiles = int32_t(total);
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return NVFP4KV_EHIP;
+  // one workgroup per tile, up to 16 per CU, then a grid-stride loop
+  int64_t g = total;
+  if (g > int64_t(cu_count(dev)) * 16) g = int64_t(cu_count(dev)) * 16;
+  hipLaunchKernelGGL(quantize_mx_kernel, dim3(unsigned(g)), dim3(kQuantThreads), 0,
+                     reinterpret_cast<hipStream_t>(stream), a);
+  return NVFP4KV_HIP_OK(hipGetLastError());
 }
 
 int launch_quantize(const QuantArgs &in, void *stream) {

@@ -31,6 +31,7 @@ class KVCacheConfig(ctypes.Structure):
 
 K_SMOOTH = 1      # NVFP4KV_K_SMOOTH
 V_ADAPTIVE = 2    # NVFP4KV_V_ADAPTIVE
+MXFP4 = 4         # NVFP4KV_MXFP4
 
 
 def lib():
@@ -48,6 +49,7 @@ def lib():
             "nvfp4kv_set_wait_limit": (I, [ctypes.c_int32]),
             "nvfp4_quantize_workspace_bytes": (SZ, []),
             "nvfp4_quantize_kv": (I, [P, I64, I64, I64, P, P, P, P, SZ, P]),
+            "mxfp4_quantize_kv": (I, [P, I64, I64, I64, P, P, P]),
             "kvcache_storage_bytes": (SZ, [ctypes.POINTER(KVCacheConfig)]),
             "kvcache_create": (I, [ctypes.POINTER(KVCacheConfig), P, SZ, ctypes.POINTER(P)]),
             "kvcache_destroy": (I, [P]),
@@ -126,12 +128,25 @@ def quantize_kv(x, workspace=None):
     return codes, scales, ts
 
 
+def mxfp4_quantize_kv(x):
+    """MXFP4 codec of one bf16 tensor [H, T, D] (D % 32 == 0): returns (codes uint8
+    [H,T,D/2], scales uint8 E8M0 [H,T,D/32])."""
+    H, T, D = x.shape
+    dev = x.device
+    codes = torch.empty((H, T, D // 2), dtype=torch.uint8, device=dev)
+    scales = torch.empty((H, T, D // 32), dtype=torch.uint8, device=dev)
+    rc = lib().mxfp4_quantize_kv(_bf16_ptr(x, "x"), H, T, D, ctypes.c_void_p(codes.data_ptr()),
+                                 ctypes.c_void_p(scales.data_ptr()), _stream())
+    _check(rc, "mxfp4_quantize_kv")
+    return codes, scales
+
+
 class KVCache:
-    """Sink + window NVFP4 KV cache on one device (see include/nvfp4kv.h)."""
+    """Sink + window NVFP4 (or MXFP4) KV cache on one device (see include/nvfp4kv.h)."""
 
     def __init__(self, n_heads, head_dim, tokens_per_frame, sink_frames, window_frames,
-                 device=None, shot_frames=0, k_smooth=False, v_adaptive=False):
-        opts = (K_SMOOTH if k_smooth else 0) | (V_ADAPTIVE if v_adaptive else 0)
+                 device=None, shot_frames=0, k_smooth=False, v_adaptive=False, mxfp4=False):
+        opts = (K_SMOOTH if k_smooth else 0) | (V_ADAPTIVE if v_adaptive else 0) | (MXFP4 if mxfp4 else 0)
         self.cfg = KVCacheConfig(n_heads, head_dim, tokens_per_frame, sink_frames, window_frames,
                                  shot_frames, opts)
         n = lib().kvcache_storage_bytes(ctypes.byref(self.cfg))
@@ -219,7 +234,7 @@ class KVCache:
         H, D, T = self.cfg.n_heads, self.cfg.head_dim, nf * self.cfg.tokens_per_frame
         dev = self.device
         kc = torch.empty((H, T, D // 2), dtype=torch.uint8, device=dev)
-        ks = torch.empty((H, T, D // 16), dtype=torch.uint8, device=dev)
+        ks = torch.empty((H, T, D // (32 if self.cfg.options & MXFP4 else 16)), dtype=torch.uint8, device=dev)
         vc = torch.empty_like(kc)
         vs = torch.empty_like(ks)
         sk = torch.empty(1, dtype=torch.float32, device=dev)

@@ -26,6 +26,13 @@ int launch_quantize(const QuantArgs &a, void *) {
   ++g_calls[0];
   return 0;
 }
+int g_mx_calls = 0;
+int launch_quantize_mx(const QuantArgs &a, void *) {
+  if (int rc = take_fail()) return rc;
+  g_q = a;
+  ++g_mx_calls;
+  return 0;
+}
 int launch_attention(const AttnArgs &a, void *) {
   if (int rc = take_fail()) return rc;
   g_a = a;
@@ -52,7 +59,10 @@ int zero_device_bytes_async(void *, size_t, void *) { return 0; }
 using namespace nvfp4kv;
 
 extern "C" {
-int stub_calls(int kind) { return kind == 3 ? g_mean_calls : g_calls[kind]; }
+int stub_calls(int kind) { return kind == 4 ? g_mx_calls : kind == 3 ? g_mean_calls : g_calls[kind]; }
+// format seen by the last attention and export launches: 1 / 32 for MXFP4
+int stub_last_attn_mx(void) { return g_a.mx; }
+int stub_last_export_block(void) { return g_e.block; }
 // options of the last quantize launch: bit 0 K mean given, bit 1 V adaptive
 int stub_last_quant_options(void) {
   return (g_q.t[0].mean ? 1 : 0) | (g_q.n_tensors > 1 && g_q.t[1].adaptive ? 2 : 0);

@@ -68,6 +68,11 @@ def test_error_paths_before_device_work(real):
     assert real.nvfp4_quantize_kv(dummy, 1, 1, 40, dummy, dummy, dummy, dummy, ws, None) == EINVAL
     assert real.nvfp4_quantize_kv(dummy, 0, 1, 64, dummy, dummy, dummy, dummy, ws, None) == EINVAL
     assert real.nvfp4_quantize_kv(dummy, 1, 1, 64, dummy, dummy, dummy, dummy, ws - 1, None) == ECAPACITY
+    real.mxfp4_quantize_kv.argtypes = [P, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, P, P, P]
+    assert real.mxfp4_quantize_kv(None, 1, 1, 64, dummy, dummy, None) == EINVAL
+    assert real.mxfp4_quantize_kv(dummy, 1, 1, 48, dummy, dummy, None) == EINVAL   # D % 32 != 0
+    assert real.mxfp4_quantize_kv(dummy, 1, 0, 64, dummy, dummy, None) == EINVAL
+    assert real.mxfp4_quantize_kv(P(0x10008), 1, 1, 64, dummy, dummy, None) == EINVAL
     real.kvcache_storage_bytes.restype = ctypes.c_size_t
     real.kvcache_storage_bytes.argtypes = [ctypes.POINTER(Cfg)]
     for bad in [Cfg(1, 96, 64, 1, 3), Cfg(1, 128, 60, 1, 3), Cfg(0, 128, 64, 1, 3),
@@ -116,7 +121,13 @@ def test_storage_bytes_budget(real):
     adaptive = real.kvcache_storage_bytes(ctypes.byref(Cfg(12, 128, 1560, 3, 9, 0, 2)))
     assert adaptive == plain
     assert smooth - plain == 65 * 12 * 128 * 4 + 2 * 12 * (32768 // 256) * 128 * 4
-    assert real.kvcache_storage_bytes(ctypes.byref(Cfg(12, 128, 1560, 3, 9, 0, 4))) == 0
+    # MXFP4 (option 4): 17/32 byte per cached element (scales per 32 instead of 16);
+    # it does not combine with the NVFP4 options; no other option bits exist
+    mx = real.kvcache_storage_bytes(ctypes.byref(Cfg(12, 128, 1560, 3, 9, 0, 4)))
+    elems = 12 * 128 * 1560 * 12
+    assert plain - mx == 2 * (elems // 16 - elems // 32)
+    for opts in (5, 6, 7, 8, 16):
+        assert real.kvcache_storage_bytes(ctypes.byref(Cfg(12, 128, 1560, 3, 9, 0, opts))) == 0
 
 
 # ------------------------------------------------------------ host stub
@@ -270,3 +281,30 @@ def test_cache_errors_and_rollback(stub):
     assert stub.kvcache_export_chunk(c.h, 1, d, d, d, d, d, d, None) == OK
     assert stub.stub_last_export_slot(buf, 64) == segs[2][2]
     stub.kvcache_destroy(c.h)
+
+
+def test_cache_options_route_to_their_kernels(stub):
+    """Each cache option reaches the launches it changes: K-smoothing runs the mean
+    reduction and hands its means to the quantizer and to attention; adaptive V
+    scales mark V; MXFP4 appends go to the single-pass MXFP4 quantizer (never the
+    NVFP4 one), and its attention and export launches carry the format."""
+    stub.stub_last_attn_k_mean.restype = ctypes.c_int64
+    d = ctypes.c_void_p(0x1000)
+    for opts in (0, 1, 2, 3, 4):
+        before = [stub.stub_calls(k) for k in range(5)]
+        c = StubCache(stub, Cfg(2, 128, 16, 1, 3, 0, opts))
+        assert c.append(2) == OK
+        after = [stub.stub_calls(k) for k in range(5)]
+        calls = [a - b for a, b in zip(after, before)]
+        if opts & 4:
+            assert calls[0] == 0 and calls[4] == 1 and calls[3] == 0
+        else:
+            assert calls[0] == 1 and calls[4] == 0
+            assert calls[3] == (1 if opts & 1 else 0)
+            assert stub.stub_last_quant_options() == opts
+        assert stub.chunk_attention(c.h, d, d, d, 8, 0.125, d, None) == OK
+        assert stub.stub_last_attn_mx() == (1 if opts & 4 else 0)
+        assert (stub.stub_last_attn_k_mean() != 0) == bool(opts & 1)
+        assert stub.kvcache_export_chunk(c.h, 0, d, d, d, d, d, d, None) == OK
+        assert stub.stub_last_export_block() == (32 if opts & 4 else 16)
+        stub.kvcache_destroy(c.h)
