@@ -40,10 +40,12 @@ CSRC = os.path.join(ROOT, "nvfp4_kv_cache_amd", "csrc")
 TRAFFIC_SOURCES = {
     "attention": ("attention.hip", "device_common.h", "nvfp4kv_internal.h"),
     "quantize": ("quantize.hip", "device_common.h", "nvfp4kv_internal.h"),
+    "quantize_mx": ("quantize.hip", "device_common.h", "nvfp4kv_internal.h"),
 }
 TRAFFIC_PROFILES = {
     "attention": "chunk_attention_kernel_rollout_steady_pmc.md",
     "quantize": "quantize_append_quantize_workload_pmc.md",
+    "quantize_mx": "quantize_mx_append_quantize_workload_pmc.md",
 }
 HBM_PEAK_GBPS = 8000.0             # MI355X HBM3E
 METRIC = "NVFP4-KV chunk attention TFLOP/s + latent frames/s; KV-quantize GB/s"
@@ -70,6 +72,8 @@ def parse():
                         "steady-state rollout cache (the roofline leg), the append of the "
                         "quantize-only workload, or a plain 256 MiB device copy (reference for "
                         "the HBM byte counters)")
+    p.add_argument("--mxfp4", action="store_true",
+                   help="with --only attention / quantize: the cache holds MXFP4 instead of NVFP4")
     return p.parse_args()
 
 
@@ -196,7 +200,7 @@ def roofline_only(args, torch, ops, W, device):
     of this command sees only the timed attention launches."""
     wl = W.WORKLOADS["rollout"]
     cache = ops.KVCache(wl.n_heads, wl.head_dim, wl.tokens_per_frame, wl.sink_frames,
-                        wl.window_frames, device=device)
+                        wl.window_frames, device=device, mxfp4=args.mxfp4)
     n_fill = (wl.sink_frames + wl.window_frames + wl.chunk_frames - 1) // wl.chunk_frames
     for c in range(n_fill):
         kc, vc = (W.draw_device_normal(wl, c, W.APPEND_STEP, t, device) for t in (W.K_ID, W.V_ID))
@@ -209,17 +213,19 @@ def roofline_only(args, torch, ops, W, device):
             "cache_tokens": sum(cache.tokens())}
 
 
-def quantize_leg(args, torch, ops, W, device, k_smooth=False, v_adaptive=False, sets=None):
+def quantize_leg(args, torch, ops, W, device, k_smooth=False, v_adaptive=False, sets=None, mxfp4=False):
     """Append of one 3-frame chunk of K and V [12, 4680, 128] into a full cache,
     cycling 10 distinct input sets (287.5 MB > the 256 MB Infinity Cache).  With
-    k_smooth / v_adaptive the cache applies K-smoothing / adaptive V scales."""
+    k_smooth / v_adaptive the cache applies K-smoothing / adaptive V scales; with
+    mxfp4 it holds MXFP4 (single-pass quantizer)."""
     wl = W.WORKLOADS["quantize"]
     n_sets = 10
     if sets is None:
         log(f"quantize: drawing {n_sets} Student-t input sets on the host")
         sets = [tuple(dev_bits(torch, b, device) for b in W.clean_chunk(wl, c)) for c in range(n_sets)]
     cache = ops.KVCache(wl.n_heads, wl.head_dim, wl.tokens_per_frame, wl.sink_frames,
-                        wl.window_frames, device=device, k_smooth=k_smooth, v_adaptive=v_adaptive)
+                        wl.window_frames, device=device, k_smooth=k_smooth, v_adaptive=v_adaptive,
+                        mxfp4=mxfp4)
     for c in range(4):
         cache.append(*sets[c], wl.chunk_frames)
     it = [0]
@@ -232,20 +238,22 @@ def quantize_leg(args, torch, ops, W, device, k_smooth=False, v_adaptive=False, 
     reps = max(args.reps, 50)
     ms = timed(app, reps, torch, warm=10, host_us_per_call=60.0)
     elems = wl.n_heads * wl.chunk_tokens * wl.head_dim
-    nbytes = 2 * W.quantize_bytes(elems)
+    nbytes = 2 * (W.quantize_bytes_mx(elems) if mxfp4 else W.quantize_bytes(elems))
     gbps = nbytes / (ms * 1e-3) / 1e9
     out = {"us_per_append": ms * 1e3, "bytes_per_append": nbytes, "GB_per_s": gbps,
            "roofline": {"bound": "hbm", "achieved": gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                         "frac": gbps / HBM_PEAK_GBPS,
-                        "traffic": None if (k_smooth or v_adaptive) else measured_traffic("quantize")}}
+                        "traffic": None if (k_smooth or v_adaptive) else
+                                   measured_traffic("quantize_mx" if mxfp4 else "quantize")}}
     return out, sets
 
 
-def attention_config(name, args, torch, ops, W, device, k_smooth=False, v_adaptive=False):
+def attention_config(name, args, torch, ops, W, device, k_smooth=False, v_adaptive=False, mxfp4=False):
     wl = W.WORKLOADS[name]
     log(f"{name}: building the cache from {wl.n_cache_chunks} host-drawn chunks")
     cache = ops.KVCache(wl.n_heads, wl.head_dim, wl.tokens_per_frame, wl.sink_frames,
-                        wl.window_frames, device=device, k_smooth=k_smooth, v_adaptive=v_adaptive)
+                        wl.window_frames, device=device, k_smooth=k_smooth, v_adaptive=v_adaptive,
+                        mxfp4=mxfp4)
     for c in range(wl.n_cache_chunks):
         k, v = W.clean_chunk(wl, c)
         cache.append(dev_bits(torch, k, device), dev_bits(torch, v, device), wl.chunk_frames)
@@ -322,7 +330,8 @@ def main():
     log(f"device: {torch.cuda.get_device_name(0)}")
     if args.only == "attention":
         r = roofline_only(args, torch, ops, W, device)
-        print(json.dumps({"leg": "attention", "workload": "rollout steady state", **r}), flush=True)
+        print(json.dumps({"leg": "attention", "workload": "rollout steady state", "mxfp4": args.mxfp4, **r}),
+              flush=True)
         return
     if args.only == "copy":
         src = torch.ones(64 << 20, dtype=torch.float32, device=device)   # 256 MiB
@@ -332,8 +341,8 @@ def main():
                           "ms": ms, "GB_per_s": 2 * src.numel() * 4 / (ms * 1e-3) / 1e9}), flush=True)
         return
     if args.only == "quantize":
-        qz, _ = quantize_leg(args, torch, ops, W, device)
-        print(json.dumps({"leg": "quantize", "workload": "quantize", **qz}), flush=True)
+        qz, _ = quantize_leg(args, torch, ops, W, device, mxfp4=args.mxfp4)
+        print(json.dumps({"leg": "quantize", "workload": "quantize", "mxfp4": args.mxfp4, **qz}), flush=True)
         return
 
     r = rollout(args, torch, ops, W, device)
@@ -354,6 +363,14 @@ def main():
         configs["wan13b_k_smooth_v_adaptive"] = attention_config("wan13b", args, torch, ops, W, device,
                                                                  k_smooth=True, v_adaptive=True)
         log(f"wan13b, K-smoothing + adaptive V: {configs['wan13b_k_smooth_v_adaptive']['us']:.1f} us")
+        # the MXFP4 cache variant (32-element blocks, E8M0 scales, no tensor scale)
+        qm, _ = quantize_leg(args, torch, ops, W, device, mxfp4=True, sets=qsets)
+        configs["quantize_mxfp4"] = {k: qm[k] for k in ("us_per_append", "GB_per_s", "bytes_per_append")}
+        configs["quantize_mxfp4"]["frac_hbm_peak"] = qm["roofline"]["frac"]
+        configs["quantize_mxfp4"]["traffic"] = qm["roofline"]["traffic"]
+        log(f"quantize, MXFP4: {qm['us_per_append']:.2f} us/append = {qm['GB_per_s']:.1f} GB/s")
+        configs["wan13b_mxfp4"] = attention_config("wan13b", args, torch, ops, W, device, mxfp4=True)
+        log(f"wan13b, MXFP4 cache: {configs['wan13b_mxfp4']['us']:.1f} us")
     configs["quantize"] = {k: qz[k] for k in ("us_per_append", "GB_per_s", "bytes_per_append")}
     configs["quantize"]["frac_hbm_peak"] = qz["roofline"]["frac"]
 
@@ -382,7 +399,7 @@ def main():
         },
         "latent_frames_per_s": r["frames_per_s"],
         "wall_ms_per_step": r["wall_ms_per_step"],
-        "roofline": {"bound": "mfma", "kernel": "chunk_attention_kernel<128>",
+        "roofline": {"bound": "mfma", "kernel": "chunk_attention_kernel<128, false> (NVFP4 cache)",
                      "achieved": r["attn_tflops"], "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": r["attn_tflops"] / MFMA_BF16_PEAK_TFLOPS,
                      "traffic": measured_traffic("attention"),

@@ -143,6 +143,12 @@ def quantize_bytes(n_elements):
     return n_elements * (2.0 + 0.5 + 1.0 / 16.0) + 4.0
 
 
+def quantize_bytes_mx(n_elements):
+    """Algorithmic bytes of quantizing one tensor to MXFP4: 2 B read, 1/2 B of codes
+    and 1/32 B of E8M0 scale written per element (no tensor scale)."""
+    return n_elements * (2.0 + 0.5 + 1.0 / 32.0)
+
+
 def device_seed(seed, chunk, step, tensor_id):
     """64-bit seed for a device-side generator, derived from the same
     (cfg_seed, chunk, step, tensor_id) key as the host draws."""
