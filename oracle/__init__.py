@@ -10,7 +10,8 @@ Contents (each function cites the passage of the pages it follows):
 * ``nvfp4_ref``     -- E2M1 / E4M3 codecs, the NVFP4 quantizer and dequantizer,
   with the optional K-smoothing and adaptive 4/6 block scales.
 * ``mxfp4_ref``     -- the MXFP4 quantizer and dequantizer (32-element blocks,
-  E8M0 scales), the format the paper's appendix A.2 sets against NVFP4.
+  E8M0 scales), the format the paper's appendix A.2 sets against NVFP4, and the
+  MXFP8 (E4M3) query quantizer of the MX-scaled matrix-core variant.
 * ``cache_ref``     -- sink + sliding-window frame list (the effective key set).
 * ``attention_ref`` -- softmax attention of a noisy chunk over the dequantized
   cache plus its own bf16 K/V, in float64.
@@ -31,6 +32,6 @@ from .nvfp4_ref import (  # noqa: F401
     dequantize_ref,
     channel_mean_ref,
 )
-from .mxfp4_ref import mx_quantize_ref, mx_dequantize_ref  # noqa: F401
+from .mxfp4_ref import mx_quantize_ref, mx_dequantize_ref, mxfp8_quantize_ref, mxfp8_dequantize_ref  # noqa: F401
 from .cache_ref import CacheModel  # noqa: F401
 from .attention_ref import chunk_attention_ref, attention_from_kv  # noqa: F401

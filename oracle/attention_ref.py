@@ -41,14 +41,30 @@ def attention_from_kv(q64, k64, v64, softmax_scale, rows=None, block=1024):
 
 
 def chunk_attention_ref(q_bits, k_own_bits, v_own_bits, cache_k64, cache_v64,
-                        softmax_scale, rows=None):
+                        softmax_scale, rows=None, q_cache64=None):
     """Noisy-chunk attention over the dequantized cache plus the chunk's own
     bf16 K/V.  q/k_own/v_own: uint16 bf16 bits [H, n_q, D].  cache_k64 /
     cache_v64: float64 [H, n_cache, D] (e.g. ``CacheModel.dequantized_kv()``).
+    q_cache64 (optional, float64 [H, n_q, D]): the queries the cache logits are
+    computed from (e.g. dequantized MXFP8 queries), the own-key logits keeping the
+    bf16 queries; one softmax over both.
     Returns float64 [H, n_q or len(rows), D]."""
     q64 = bf16_bits_to_f32(q_bits).astype(np.float64)
     ko = bf16_bits_to_f32(k_own_bits).astype(np.float64)
     vo = bf16_bits_to_f32(v_own_bits).astype(np.float64)
-    k64 = np.concatenate([cache_k64, ko], axis=1)
-    v64 = np.concatenate([cache_v64, vo], axis=1)
-    return attention_from_kv(q64, k64, v64, softmax_scale, rows=rows)
+    if q_cache64 is None:
+        k64 = np.concatenate([cache_k64, ko], axis=1)
+        v64 = np.concatenate([cache_v64, vo], axis=1)
+        return attention_from_kv(q64, k64, v64, softmax_scale, rows=rows)
+    qc = np.asarray(q_cache64, dtype=np.float64)
+    if rows is not None:
+        q64, qc = q64[:, rows], qc[:, rows]
+    H, Lq, D = q64.shape
+    out = np.empty((H, Lq, D), dtype=np.float64)
+    for h in range(H):
+        s = np.concatenate([qc[h] @ cache_k64[h].T, q64[h] @ ko[h].T], axis=1) * float(softmax_scale)
+        s -= s.max(axis=1, keepdims=True)
+        p = np.exp(s)
+        p /= p.sum(axis=1, keepdims=True)
+        out[h] = p @ np.concatenate([cache_v64[h], vo[h]], axis=0)
+    return out

@@ -25,23 +25,31 @@ Readings (the cited specification's MXFP4, restated; also listed in the design doc)
 * Dequantized value: E2M1(code) * 2^(byte - 127), exact in float64.
 
 Every step is exact or an integer decision, so the steps above define every bit.
+
+MXFP8 queries (for the variant whose cache logits run on gfx950's MX-scaled matrix
+cores, which take both operands in an MX format): the same specification's MXFP8
+with E4M3 elements -- 32-element blocks along head_dim, E = floor(log2(block max))
+- 8 (8 = the exponent of E4M3's largest magnitude 448 = 1.75 * 2^8) clamped to
+[-127, 127], elements E4M3(x / 2^E) nearest-even and saturating at 448 (block maxima
+in (448, 512) * 2^E clip), the sign kept (-0 -> 0x80).
 """
 
 import numpy as np
 
-from .nvfp4_ref import E2M1_VALUES, bf16_bits_to_f32, e2m1_encode, unpack_codes
+from .nvfp4_ref import E2M1_VALUES, E4M3_VALUES, bf16_bits_to_f32, e2m1_encode, e4m3_encode, unpack_codes
 
 MX_BLOCK = 32
 E2M1_EMAX = 2          # 6 = 1.5 * 2^2
+E4M3_EMAX = 8          # 448 = 1.75 * 2^8
 E8M0_BIAS = 127
 
 
-def mx_block_exponent(amax_b):
-    """E = floor(log2(amax_b)) - 2 clamped to [-127, 127]; -127 for a zero block.
-    amax_b: float values >= 0 (finite)."""
+def mx_block_exponent(amax_b, emax=E2M1_EMAX):
+    """E = floor(log2(amax_b)) - emax clamped to [-127, 127]; -127 for a zero block.
+    amax_b: float values >= 0 (finite); emax: the element format's largest exponent."""
     a = np.asarray(amax_b, dtype=np.float64)
     mant, ex = np.frexp(a)              # a = mant * 2^ex, mant in [0.5, 1) for a > 0
-    e = (ex - 1) - E2M1_EMAX            # floor(log2 a) = ex - 1, exactly
+    e = (ex - 1) - emax                 # floor(log2 a) = ex - 1, exactly
     e = np.where(a > 0, e, -E8M0_BIAS)
     return np.clip(e, -E8M0_BIAS, E8M0_BIAS).astype(np.int64)
 
@@ -81,3 +89,32 @@ def mx_dequantize_ref(packed, scales):
     Xv = np.repeat(X, MX_BLOCK, axis=-1)
     assert Xv.shape[-1] == code.shape[-1]
     return sgn * mag * Xv
+
+
+def mxfp8_quantize_ref(x_bits):
+    """Quantize bf16 bit patterns x_bits [..., D] (D % 32 == 0) to MXFP8 (E4M3
+    elements).  Returns (codes uint8 [..., D] as E4M3 bytes, scales uint8 [..., D/32]
+    as E8M0 bytes).  Steps follow the module docstring."""
+    x_bits = np.asarray(x_bits, dtype=np.uint16)
+    D = x_bits.shape[-1]
+    assert D % MX_BLOCK == 0
+    x = bf16_bits_to_f32(x_bits).astype(np.float64)
+    assert np.all(np.isfinite(x)), "inputs must be finite"
+    sign = ((x_bits >> 15) & 1).astype(np.uint8)
+    lead = x.shape[:-1]
+    nb = D // MX_BLOCK
+    ax = np.abs(x).reshape(lead + (nb, MX_BLOCK))
+    E = mx_block_exponent(ax.max(axis=-1), E4M3_EMAX)
+    q = ax * np.exp2(-E.astype(np.float64))[..., None]      # exact power-of-two scaling
+    mag = e4m3_encode(q).reshape(lead + (D,))               # nearest-even, saturating at 448
+    return ((sign << 7) | mag).astype(np.uint8), (E + E8M0_BIAS).astype(np.uint8)
+
+
+def mxfp8_dequantize_ref(codes, scales):
+    """x_hat = E4M3(code) * 2^(scale byte - 127), in float64 (exact)."""
+    codes = np.asarray(codes, dtype=np.uint8)
+    assert np.all((codes & 0x7F) != 0x7F), "E4M3 0x7F / 0xFF is NaN and is never produced"
+    mag = E4M3_VALUES[codes & 0x7F]
+    sgn = np.where(codes >> 7, -1.0, 1.0)
+    X = np.repeat(np.exp2(np.asarray(scales, dtype=np.float64) - E8M0_BIAS), MX_BLOCK, axis=-1)
+    return sgn * mag * X

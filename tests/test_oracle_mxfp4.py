@@ -149,3 +149,75 @@ def test_error_bound():
     blocks = np.abs(x).reshape(4, 50, 4, 32).max(axis=-1)
     r = blocks / np.exp2(scales.astype(np.float64) - 127)
     assert np.all((r >= 4) & (r < 8))
+
+
+# ---------------------------------------------------------------- MXFP8 queries
+
+
+def test_mxfp8_golden_blocks():
+    g = json.load(open(GOLDEN))["mxfp8"]
+    rows, D = g["shape"]
+    x = np.zeros((rows, D), dtype=np.float32)
+    for blk in g["blocks"]:
+        vals = np.array(blk["x"], dtype=np.float32)
+        x[blk["row"], :len(vals)] = vals
+    codes, scales = M.mxfp8_quantize_ref(bf16_bits(x))
+    for blk in g["blocks"]:
+        r, n = blk["row"], len(blk["codes"])
+        assert scales[r, 0] == blk["scale_byte"], blk["name"]
+        assert list(codes[r, :n]) == blk["codes"], blk["name"]
+        assert not np.any(codes[r, n:]), blk["name"]
+
+
+def test_mxfp8_against_torch_e4m3_and_exponent_search():
+    # the elements against torch's float8_e4m3fn cast of x / 2^E (nearest-even; only
+    # where no saturation is involved), saturated ones at 0x7E, E by search
+    rng = np.random.default_rng(21)
+    xb = random_bf16(rng, (5, 40, 128), scale=2.0)
+    codes, scales = M.mxfp8_quantize_ref(xb)
+    x = R.bf16_bits_to_f32(xb).astype(np.float64)
+    X = np.repeat(np.exp2(scales.astype(np.float64) - 127), 32, axis=-1)
+    q = np.abs(x) / X
+    small = q <= 448.0
+    t = torch.from_numpy(q[small]).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(codes[small] & 0x7F, t)
+    assert np.all(codes[~small] & 0x7F == 0x7E)
+    assert np.array_equal(codes >> 7, (xb >> 15).astype(np.uint8))
+    amax = np.abs(x).reshape(5, 40, 4, 32).max(axis=-1)
+    r = amax / np.exp2(scales.astype(np.float64) - 127)
+    assert np.all((r >= 256) & (r < 512))
+
+
+def test_mxfp8_dequantize_every_code():
+    # every non-NaN E4M3 byte times every E8M0 byte, against torch's two decoders
+    codes = np.array([c for c in range(256) if (c & 0x7F) != 0x7F], dtype=np.uint8)
+    e4 = torch.from_numpy(codes).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    for s in (0, 1, 100, 127, 130, 254):
+        e8 = torch.tensor([s], dtype=torch.uint8).view(torch.float8_e8m0fnu).to(torch.float64).item()
+        blk = np.zeros((len(codes) + 31) // 32 * 32, dtype=np.uint8)
+        blk[:len(codes)] = codes
+        xh = M.mxfp8_dequantize_ref(blk.reshape(-1, 32), np.full((blk.size // 32, 1), s, np.uint8))
+        assert np.array_equal(xh.reshape(-1)[:len(codes)], e4 * e8)
+
+
+def test_two_query_attention_reduces_to_plain():
+    # the oracle's cache-query option with the bf16 queries themselves is plain attention,
+    # and with different cache queries it changes only the cache logits
+    from oracle import chunk_attention_ref
+    rng = np.random.default_rng(22)
+    H, nq, nc, D = 2, 5, 7, 32
+    q, ko, vo = (random_bf16(rng, (H, nq, D)) for _ in range(3))
+    kc, vc = rng.standard_normal((H, nc, D)), rng.standard_normal((H, nc, D))
+    plain = chunk_attention_ref(q, ko, vo, kc, vc, 0.3)
+    q64 = R.bf16_bits_to_f32(q).astype(np.float64)
+    assert np.allclose(chunk_attention_ref(q, ko, vo, kc, vc, 0.3, q_cache64=q64), plain, rtol=1e-13, atol=1e-13)
+    # brute force for one row with cache queries scaled by 2
+    got = chunk_attention_ref(q, ko, vo, kc, vc, 0.3, q_cache64=2 * q64, rows=np.array([3]))
+    ko64, vo64 = (R.bf16_bits_to_f32(t).astype(np.float64) for t in (ko, vo))
+    for h in range(H):
+        s = [0.3 * float(np.dot(2 * q64[h, 3], kc[h, j])) for j in range(nc)]
+        s += [0.3 * float(np.dot(q64[h, 3], ko64[h, j])) for j in range(nq)]
+        w = np.exp(np.array(s) - max(s))
+        w /= w.sum()
+        want = w @ np.concatenate([vc[h], vo64[h]], axis=0)
+        assert np.allclose(got[h, 0], want, rtol=1e-12, atol=1e-12)
