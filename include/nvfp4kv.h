@@ -144,6 +144,13 @@ int mxfp4_quantize_kv(const uint16_t *x, int64_t H, int64_t T, int64_t D, uint8_
  *                       QK^T and PV on the bf16 matrix cores with plain bf16 Q and P
  *                       rounded to nearest-even.  Not combinable with the two options
  *                       above (steps of the NVFP4 recipe).
+ *   NVFP4KV_MX_SCALED_QK  (with NVFP4KV_MXFP4) QK^T of the cache tiles runs on gfx950's
+ *                       MX-scaled matrix cores straight from the E2M1 codes and E8M0
+ *                       scales: the queries enter that product quantized to MXFP8
+ *                       (E4M3 elements, E8M0 scale per 32 along head_dim with exponent
+ *                       floor(log2 block max) - 8, nearest-even, saturating at 448).
+ *                       The own-segment logits keep the bf16 queries.  This changes the
+ *                       results beyond the cache format (the queries are quantized).
  *
  * Supported: n_heads >= 1; head_dim 64 or 128; tokens_per_frame >= 8 and a multiple
  * of 8; sink_frames >= 0; window_frames >= 1; shot_frames >= 0 (0: no shot-level
@@ -154,6 +161,7 @@ int mxfp4_quantize_kv(const uint16_t *x, int64_t H, int64_t T, int64_t D, uint8_
 #define NVFP4KV_K_SMOOTH 1
 #define NVFP4KV_V_ADAPTIVE 2
 #define NVFP4KV_MXFP4 4
+#define NVFP4KV_MX_SCALED_QK 8
 
 typedef struct {
   int32_t n_heads;
@@ -162,7 +170,7 @@ typedef struct {
   int32_t sink_frames;
   int32_t window_frames;
   int32_t shot_frames;
-  int32_t options;   /* NVFP4KV_K_SMOOTH | NVFP4KV_V_ADAPTIVE, or NVFP4KV_MXFP4, or 0 */
+  int32_t options;   /* NVFP4KV_K_SMOOTH | NVFP4KV_V_ADAPTIVE, or NVFP4KV_MXFP4 [| NVFP4KV_MX_SCALED_QK], or 0 */
 } kvcache_config;
 
 typedef struct kvcache kvcache; /* opaque host object */

@@ -41,7 +41,8 @@ bool config_ok(const kvcache_config *c) {
       c->tokens_per_frame > (1 << 20))
     return false;
   if (c->sink_frames < 0 || c->window_frames < 1 || c->shot_frames < 0) return false;
-  if (c->options & ~(NVFP4KV_K_SMOOTH | NVFP4KV_V_ADAPTIVE | NVFP4KV_MXFP4)) return false;
+  if (c->options & ~(NVFP4KV_K_SMOOTH | NVFP4KV_V_ADAPTIVE | NVFP4KV_MXFP4 | NVFP4KV_MX_SCALED_QK)) return false;
+  if ((c->options & NVFP4KV_MX_SCALED_QK) && !(c->options & NVFP4KV_MXFP4)) return false;
   // smoothing and adaptive 4/6 scales are steps of the NVFP4 recipe
   if ((c->options & NVFP4KV_MXFP4) && (c->options & (NVFP4KV_K_SMOOTH | NVFP4KV_V_ADAPTIVE))) return false;
   if (c->sink_frames + c->window_frames + c->shot_frames > kMaxFrames) return false;
@@ -475,7 +476,7 @@ int chunk_attention(const kvcache *c, const uint16_t *q, const uint16_t *k_own,
   a.n_q = int32_t(n_q);
   a.sm_scale_log2 = softmax_scale * 1.4426950408889634f;
   a.k_mean = c->k_smooth() ? c->kmean(0) : nullptr;
-  a.mx = c->mx() ? 1 : 0;
+  a.mx = c->mx() ? ((c->cfg.options & NVFP4KV_MX_SCALED_QK) ? 2 : 1) : 0;
   a.partials = c->attn_partials();
   a.flags = c->attn_flags();
   a.epoch = ++c->attn_epoch;   // never reused, even if the launch fails

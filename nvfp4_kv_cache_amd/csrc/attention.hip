@@ -67,6 +67,7 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
 
 namespace {
 
@@ -95,6 +96,15 @@ __device__ __forceinline__ int ks_off(int row, int chunk) {
 }
 template <int D>
 constexpr int kKsElems = kBN * (D + 8);
+// MXFP4 with MX-scaled QK^T: the Ks buffer holds the tile's raw K codes, rows of
+// D/2 bytes padded by 16 (8 consecutive rows of a b128 read phase land on distinct
+// banks: a row stride of 80 or 48 bytes moves 20 or 12 banks), then the E8M0
+// scale bytes [kBN][D/32].
+template <int D>
+constexpr int kRawRow = D / 2 + 16;
+template <int D>
+constexpr int kRawScales = kBN * kRawRow<D>;
+
 // Vs: [D][kBN + 8] 16-bit (V^T rows).
 __device__ __forceinline__ int vs_off(int row, int chunk) {
   return row * (kBN + 8) + (chunk << 3);
@@ -227,14 +237,21 @@ __device__ __forceinline__ uint32_t fp4x2_bf16_2s(uint32_t w, float sa, float sb
   return (fp4x2_bf16<SEL>(w, sa) & 0xFFFFu) | (fp4x2_bf16<SEL>(w, sb) & 0xFFFF0000u);
 }
 
-template <int D, bool MX>
+template <int D, bool MX, bool MXS = false>
 __device__ __forceinline__ void dequant_store(const Packed<D> &p, uint16_t *Ks, uint16_t *Vs) {
   constexpr int nb = D / 16;
   if constexpr (MX) {
 #pragma unroll
     for (int i = 0; i < Packed<D>::kTasks; ++i) {
       const int t = threadIdx.x + i * Cfg<D>::kThreads;
-      {
+      if constexpr (MXS) {
+        // K stays E2M1 codes for the MX-scaled matrix cores: copy the 8 code bytes
+        // and (one thread per 32-element block) the block's E8M0 byte
+        const int key = t / nb, b = t % nb;
+        uint8_t *raw = reinterpret_cast<uint8_t *>(Ks);
+        *reinterpret_cast<uint2 *>(raw + key * kRawRow<D> + 8 * b) = make_uint2(p.kc[i][0], p.kc[i][1]);
+        if ((b & 1) == 0) raw[kRawScales<D> + key * (D / 32) + (b >> 1)] = uint8_t(p.ks[i]);
+      } else {
         const int key = t / nb, b = t % nb;
         const float sk = e8m0_operand<0>(p.ks[i]);
         const uint32_t w0 = p.kc[i][0], w1 = p.kc[i][1];
@@ -390,6 +407,108 @@ __device__ __forceinline__ void qk_tile(const uint16_t *Ks, const u32x4 (&qr)[D 
         s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
             __builtin_bit_cast(f16x8, kf[kb][st]), __builtin_bit_cast(f16x8, qr[st]), s[kb], 0, 0, 0);
     }
+}
+
+// ---- MX-scaled QK^T (MXFP4 cache, queries in MXFP8)
+// v_mfma_scale_f32_32x32x64_f8f6f4 with A = the K tile's E2M1 codes and B = the
+// queries in E4M3, both with E8M0 scales per 32 elements of the reduction.  Operand
+// layouts (checked on gfx950 with one-hot probes): for E2M1, lane (row, h) holds the
+// 32 elements 32h + [0, 32) of the 64-wide k-step and its scale operand scales all of
+// them; for E4M3, lane (column, h) holds bytes 0-15 = elements 16h + [0, 16) and
+// bytes 16-31 = 32 + 16h + [0, 16), and the elements of 32-block c are scaled by
+// the operand of lane (column, c).  The op_sel immediate picks the operand's byte.
+
+typedef short short2_ __attribute__((ext_vector_type(2)));
+
+// The wave's queries as MXFP8 B operands: q[s] for k-step s, and one scale operand
+// per lane whose byte 2s is the E8M0 byte of block 2s + h.
+template <int D>
+struct QFp8 {
+  i32x8 q[D / 64];
+  uint32_t scale;
+};
+
+// E8M0 exponent of an E4M3 block whose largest |x| has the bf16 bit pattern m:
+// floor(log2 m) - 8 (448 = 1.75 * 2^8), clamped to [-127, 127]; -127 for zero.
+__device__ __forceinline__ int e4m3_block_exponent(uint32_t m) {
+  const int ef = int(m >> 7);
+  const int fl = ef > 0 ? ef - 127 : -133 + (31 - __builtin_clz(m | 1u));
+  return m == 0 ? -127 : max(-127, min(127, fl - 8));
+}
+
+template <int D>
+__device__ __forceinline__ void quantize_q_mxfp8(const AttnArgs &a, int h, int q0, QFp8<D> &qf) {
+  const int lane = threadIdx.x & 63, half = lane >> 5, l32 = lane & 31;
+  const int qi = q0 + l32;
+  const bool ok = qi < a.n_q;
+  const uint16_t *qp = a.q + (int64_t(h) * a.n_q + (ok ? qi : 0)) * D + 16 * half;
+  qf.scale = 0;
+#pragma unroll
+  for (int st = 0; st < D / 64; ++st) {
+    uint32_t out[8];
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      // 16 values d = 64 st + 32 c + 16 h + [0, 16) of block 2 st + c; the other 16 of
+      // the block are the other lane half's
+      const uint4 *src = reinterpret_cast<const uint4 *>(qp + 64 * st + 32 * c);
+      const uint4 u0 = ok ? src[0] : make_uint4(0, 0, 0, 0), u1 = ok ? src[1] : make_uint4(0, 0, 0, 0);
+      const uint32_t w[8] = {u0.x, u0.y, u0.z, u0.w, u1.x, u1.y, u1.z, u1.w};
+      uint32_t m = 0;
+#pragma unroll
+      for (int k = 0; k < 8; ++k) m = max(m, max(w[k] & 0x7FFFu, (w[k] >> 16) & 0x7FFFu));
+      const int e = e4m3_block_exponent(other_half_umax(m));
+      const float inv = __uint_as_float(uint32_t(127 - e) << 23);   // 2^-e, a normal fp32
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        short2_ pk = {0, 0};
+        const float x0 = __uint_as_float(w[2 * k] << 16) * inv, x1 = __uint_as_float(w[2 * k] & 0xFFFF0000u) * inv;
+        const float x2 = __uint_as_float(w[2 * k + 1] << 16) * inv, x3 = __uint_as_float(w[2 * k + 1] & 0xFFFF0000u) * inv;
+        pk = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(pk, fminf(fmaxf(x0, -448.0f), 448.0f),
+                                                      fminf(fmaxf(x1, -448.0f), 448.0f), 1.0f, false);
+        pk = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(pk, fminf(fmaxf(x2, -448.0f), 448.0f),
+                                                      fminf(fmaxf(x3, -448.0f), 448.0f), 1.0f, true);
+        out[4 * c + k] = __builtin_bit_cast(uint32_t, pk);
+      }
+      if (c == half) qf.scale |= uint32_t(e + 127) << (16 * st);
+    }
+#pragma unroll
+    for (int k = 0; k < 8; ++k) qf.q[st][k] = int(out[k]);
+  }
+}
+
+// D += A B with A in E2M1 and B in E4M3, scaled by byte SEL of each lane's operands
+template <int SEL>
+__device__ __forceinline__ f32x16 mfma_e2m1_e4m3(const i32x8 &A, const i32x8 &B, const f32x16 &C, uint32_t sa,
+                                                 uint32_t sb) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(A, B, C, 4, 0, SEL, int(sa), SEL, int(sb));
+}
+
+// S^T = K Q^T for the wave's 32 queries from the tile's raw K codes.
+template <int D>
+__device__ __forceinline__ void qk_tile_mxs(const uint16_t *Ks, const QFp8<D> &qf, f32x16 (&s)[2]) {
+  const int lane = threadIdx.x & 63, half = lane >> 5, l32 = lane & 31;
+  const uint8_t *raw = reinterpret_cast<const uint8_t *>(Ks);
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) s[kb][r] = 0.0f;
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb) {
+    const int key = kb * 32 + l32;
+    // the key's E8M0 bytes, shifted so that this lane's block of k-step st is byte 2 st
+    uint32_t sw;
+    if constexpr (D == 128)
+      sw = *reinterpret_cast<const uint32_t *>(raw + kRawScales<D> + key * 4) >> (8 * half);
+    else
+      sw = uint32_t(*reinterpret_cast<const uint16_t *>(raw + kRawScales<D> + key * 2)) >> (8 * half);
+#pragma unroll
+    for (int st = 0; st < D / 64; ++st) {
+      const u32x4 c = *reinterpret_cast<const u32x4 *>(raw + key * kRawRow<D> + 32 * st + 16 * half);
+      const i32x8 A = {int(c.x), int(c.y), int(c.z), int(c.w), 0, 0, 0, 0};
+      s[kb] = st == 0 ? mfma_e2m1_e4m3<0>(A, qf.q[st], s[kb], sw, qf.scale)
+                      : mfma_e2m1_e4m3<2>(A, qf.q[st], s[kb], sw, qf.scale);
+    }
+  }
 }
 
 // Online softmax of S^T, then O^T += V^T P^T.
@@ -619,12 +738,15 @@ __device__ __forceinline__ void write_out(const AttnArgs &a, int h, int qi, cons
 }  // namespace
 
 // MX: the cache holds MXFP4 (dequantized to bf16, QK^T and PV of its tiles on the
-// bf16 matrix cores with plain bf16 Q); otherwise NVFP4.
-template <int D, bool MX>
+// bf16 matrix cores with plain bf16 Q); otherwise NVFP4.  MXS (with MX): QK^T of the
+// cache tiles on the MX-scaled matrix cores from the raw codes, queries in MXFP8.
+template <int D, bool MX, bool MXS>
 __global__ __launch_bounds__(Cfg<D>::kThreads, Cfg<D>::kWgPerCu) void chunk_attention_kernel(AttnArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t Ks[2][kKsElems<D>];
   __shared__ __attribute__((aligned(16))) uint16_t Vs[2][kVsElems<D>];
   __shared__ int s_ready;
+  static_assert(kRawScales<D> + kBN * (D / 32) <= 2 * kKsElems<D>, "raw K tile fits the Ks buffer");
+  static_assert(!MXS || MX, "the MX-scaled product reads MXFP4 codes");
   constexpr int kBM = Cfg<D>::kBM;
   constexpr size_t kSlotFloats = attn_slot_bytes(D) / 4;
   static_assert(kBM == attn_block_queries(D) && Cfg<D>::kThreads == attn_threads(D) &&
@@ -685,7 +807,9 @@ __global__ __launch_bounds__(Cfg<D>::kThreads, Cfg<D>::kWgPerCu) void chunk_atte
       if (r0 < cache_tiles) {
         // NVFP4: Q as fp16 with a per-query power-of-two scale 2^sh (row max -> [2^14,
         // 2^15)); MXFP4: plain bf16 Q
-        load_q<D>(a, h, q0, qr);
+        QFp8<D> qf;
+        if constexpr (MXS) quantize_q_mxfp8<D>(a, h, q0, qf);
+        else load_q<D>(a, h, q0, qr);
         float cq = 1.0f;
         if constexpr (!MX) {
           uint32_t mx = 0;
@@ -757,7 +881,7 @@ __global__ __launch_bounds__(Cfg<D>::kThreads, Cfg<D>::kWgPerCu) void chunk_atte
           nth_full(a, r0, cs, ck);
           Packed<D> pk;
           load_packed<D, MX>(hp, uint32_t(a.seg[cs].tok0 + ck), kBN, pk);
-          dequant_store<D, MX>(pk, Ks[0], Vs[0]);
+          dequant_store<D, MX, MXS>(pk, Ks[0], Vs[0]);
           int ns = cs, nk = ck;
           bool have_next = r0 + 1 < f1 && next_full(a, ns, nk);
           int ltok = have_next ? a.seg[ns].tok0 + nk : a.seg[cs].tok0 + ck;
@@ -766,9 +890,10 @@ __global__ __launch_bounds__(Cfg<D>::kThreads, Cfg<D>::kWgPerCu) void chunk_atte
           int buf = 0;
           for (int i = r0;; ++i) {
             enter_segment(cs);
-            qk_tile<D, MX>(Ks[buf], qr, s);
+            if constexpr (MXS) qk_tile_mxs<D>(Ks[buf], qf, s);
+            else qk_tile<D, MX>(Ks[buf], qr, s);
             // stage tile i+1 while the MFMAs run, then fetch the bytes of tile i+2
-            dequant_store<D, MX>(pk, Ks[buf ^ 1], Vs[buf ^ 1]);
+            dequant_store<D, MX, MXS>(pk, Ks[buf ^ 1], Vs[buf ^ 1]);
             int s2 = ns, k2 = nk;
             const bool have_n2 = have_next && i + 2 < f1 && next_full(a, s2, k2);
             if (have_n2) ltok = a.seg[s2].tok0 + k2;
@@ -792,10 +917,11 @@ __global__ __launch_bounds__(Cfg<D>::kThreads, Cfg<D>::kWgPerCu) void chunk_atte
           const int ck = a.seg[cs].ntok - tn;
           Packed<D> pk;
           load_packed<D, MX>(hp, uint32_t(a.seg[cs].tok0 + ck), tn, pk);
-          dequant_store<D, MX>(pk, Ks[0], Vs[0]);
+          dequant_store<D, MX, MXS>(pk, Ks[0], Vs[0]);
           enter_segment(cs);
           __syncthreads();
-          qk_tile<D, MX>(Ks[0], qr, s);
+          if constexpr (MXS) qk_tile_mxs<D>(Ks[0], qf, s);
+          else qk_tile<D, MX>(Ks[0], qr, s);
           softmax_pv<D, true, MX>(Vs[0], s, cmul, kbias, tn, sm, acc);
           __syncthreads();
         }
@@ -976,10 +1102,14 @@ int launch_attention_d(AttnArgs a, hipStream_t s) {
   const int64_t wmax = a.w_tail;   // the largest weight
   if (grid > a.work / wmax) grid = a.work / wmax;
   if (grid < 1) grid = 1;
-  if (a.mx)
-    hipLaunchKernelGGL((chunk_attention_kernel<D, true>), dim3(unsigned(grid)), dim3(Cfg<D>::kThreads), 0, s, a);
+  if (a.mx == 2)
+    hipLaunchKernelGGL((chunk_attention_kernel<D, true, true>), dim3(unsigned(grid)), dim3(Cfg<D>::kThreads), 0, s, a);
+  else if (a.mx == 1)
+    hipLaunchKernelGGL((chunk_attention_kernel<D, true, false>), dim3(unsigned(grid)), dim3(Cfg<D>::kThreads), 0, s,
+                       a);
   else
-    hipLaunchKernelGGL((chunk_attention_kernel<D, false>), dim3(unsigned(grid)), dim3(Cfg<D>::kThreads), 0, s, a);
+    hipLaunchKernelGGL((chunk_attention_kernel<D, false, false>), dim3(unsigned(grid)), dim3(Cfg<D>::kThreads), 0,
+                       s, a);
   return NVFP4KV_HIP_OK(hipGetLastError());
 }
 }  // namespace

@@ -107,7 +107,7 @@ struct AttnArgs {
   // cost weights of a cache full tile, a ragged tail and an own full tile; a block's
   // total weight; the work list is cut by weight
   int32_t w_cfull, w_tail, w_ofull, w_block;
-  int32_t mx;                 // 1: the cache holds MXFP4 (E8M0 scales per 32), 0: NVFP4
+  int32_t mx;                 // 0: NVFP4 cache; 1: MXFP4 (E8M0 scales per 32); 2: MXFP4 with MX-scaled QK^T
   int64_t work;               // query blocks x block weight
   const float *k_mean;        // K-smoothing means [scale slot][H][D], or null
   float *partials;            // [max grid][slot]

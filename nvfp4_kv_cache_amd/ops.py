@@ -32,6 +32,7 @@ class KVCacheConfig(ctypes.Structure):
 K_SMOOTH = 1      # NVFP4KV_K_SMOOTH
 V_ADAPTIVE = 2    # NVFP4KV_V_ADAPTIVE
 MXFP4 = 4         # NVFP4KV_MXFP4
+MX_SCALED_QK = 8  # NVFP4KV_MX_SCALED_QK
 
 
 def lib():
@@ -145,8 +146,10 @@ class KVCache:
     """Sink + window NVFP4 (or MXFP4) KV cache on one device (see include/nvfp4kv.h)."""
 
     def __init__(self, n_heads, head_dim, tokens_per_frame, sink_frames, window_frames,
-                 device=None, shot_frames=0, k_smooth=False, v_adaptive=False, mxfp4=False):
+                 device=None, shot_frames=0, k_smooth=False, v_adaptive=False, mxfp4=False,
+                 mx_scaled_qk=False):
         opts = (K_SMOOTH if k_smooth else 0) | (V_ADAPTIVE if v_adaptive else 0) | (MXFP4 if mxfp4 else 0)
+        opts |= MX_SCALED_QK if mx_scaled_qk else 0
         self.cfg = KVCacheConfig(n_heads, head_dim, tokens_per_frame, sink_frames, window_frames,
                                  shot_frames, opts)
         n = lib().kvcache_storage_bytes(ctypes.byref(self.cfg))

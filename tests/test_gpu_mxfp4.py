@@ -177,3 +177,80 @@ def test_mx_attention_wan13b_sampled_rows(ops):
     ck, cv = model.dequantized_kv()
     want = chunk_attention_ref(q, ko, vo, ck, cv, wl.softmax_scale, rows=rows)
     check_attention(out[:, rows], want, "mx wan13b")
+
+
+# ---- MX-scaled QK^T: the cache logits from MXFP8 queries on the MX-scaled matrix cores
+
+
+def q_mxfp8(q_bits):
+    from oracle import mxfp8_dequantize_ref, mxfp8_quantize_ref
+    return mxfp8_dequantize_ref(*mxfp8_quantize_ref(q_bits))
+
+
+def build_scaled(ops, H, D, T_f, sink, window, chunks, shot=0):
+    from gpu_util import dev
+    cache = ops.KVCache(H, D, T_f, sink, window, shot_frames=shot, mxfp4=True, mx_scaled_qk=True)
+    model = CacheModel(H, D, T_f, sink, window, shot_frames=shot, mxfp4=True)
+    for k, v in chunks:
+        cache.append(dev(k), dev(v), k.shape[1] // T_f)
+        model.append(k, v)
+    return cache, model
+
+
+def run_scaled(cache, model, q, ko, vo, scale, rows=None, what=""):
+    from gpu_util import dev, host, check_attention
+    print(f"[{what}] n_q={q.shape[1]} cache_tokens={model.n_tokens()}", flush=True)
+    out = host(cache.attention(dev(q), dev(ko), dev(vo), scale))
+    ck, cv = model.dequantized_kv()
+    want = chunk_attention_ref(q, ko, vo, ck, cv, scale, rows=rows, q_cache64=q_mxfp8(q))
+    got = out if rows is None else out[:, rows]
+    return check_attention(got, want, what)
+
+
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("n_q", [1, 257])
+def test_mx_scaled_qk_ragged_multi_segment(ops, D, n_q):
+    rng = np.random.default_rng(50 + D + n_q)
+    H, T_f, sink, window = 3, 40, 2, 5
+    chunks = [(rand_bits(rng, (H, nf * T_f, D)), rand_bits(rng, (H, nf * T_f, D))) for nf in (3, 2, 1, 3, 2)]
+    cache, model = build_scaled(ops, H, D, T_f, sink, window, chunks)
+    q, ko, vo = (rand_bits(rng, (H, n_q, D)) for _ in range(3))
+    run_scaled(cache, model, q, ko, vo, 1.0 / np.sqrt(D), what=f"mx scaled-qk ragged D{D} nq{n_q}")
+
+
+def test_mx_scaled_qk_special_queries_and_shot_sink(ops):
+    """Queries with zero blocks, bf16 subnormals, large and tiny rows (MXFP8 exponent
+    clamps and saturation at 448) over chunks of very different scales, across a
+    scene cut."""
+    from gpu_util import dev
+    rng = np.random.default_rng(61)
+    H, D, T_f = 2, 128, 64
+    chunks = []
+    for sc in (1.0, 2.0 ** -20, 0.0, 2.0 ** 6, 1.0):
+        x = (rng.standard_normal((H, T_f, D)) * sc).astype(np.float32)
+        chunks.append((W.f32_to_bf16_bits(x), rand_bits(rng, (H, T_f, D))))
+    cache, model = build_scaled(ops, H, D, T_f, 1, 2, chunks[:3], shot=1)
+    cache.begin_shot()
+    model.begin_shot()
+    for k, v in chunks[3:]:
+        cache.append(dev(k), dev(v), 1)
+        model.append(k, v)
+    qf = rng.standard_normal((H, 100, D)).astype(np.float32)
+    qf[0, 0, :32] = 0.0
+    qf[0, 1, :] = np.float32(2.0 ** -130) * rng.integers(-100, 100, D)
+    qf[0, 2, :] *= 30.0
+    qf[1, 3, :] *= 1e-30
+    qf[1, 4, :32] = np.array([448, 464, 480, 500, 1, -1, 0.5, 3] * 4, dtype=np.float32)
+    q = W.f32_to_bf16_bits(qf)
+    ko, vo = rand_bits(rng, (H, 100, D)), rand_bits(rng, (H, 100, D))
+    run_scaled(cache, model, q, ko, vo, 0.0884, what="mx scaled-qk special queries + shot")
+
+
+def test_mx_scaled_qk_wan13b_sampled_rows(ops):
+    wl = W.WORKLOADS["wan13b"]
+    chunks = [W.clean_chunk(wl, c) for c in range(wl.n_cache_chunks)]
+    cache, model = build_scaled(ops, wl.n_heads, wl.head_dim, wl.tokens_per_frame, wl.sink_frames,
+                                wl.window_frames, chunks)
+    q, ko, vo = W.noisy_chunk(wl, wl.n_cache_chunks)
+    rows = np.unique(np.concatenate([np.arange(0, 40), np.linspace(0, wl.n_q - 1, 60).astype(int)]))
+    run_scaled(cache, model, q, ko, vo, wl.softmax_scale, rows=rows, what="mx scaled-qk wan13b")

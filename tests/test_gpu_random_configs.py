@@ -1,19 +1,21 @@
 """Seeded random cache configurations and schedules on the GPU, each checked against
 the oracle: head count, head_dim, frame size, sink / window / shot-level-sink sizes,
-the cache format and options (NVFP4 plain, K-smoothing, adaptive V, both, MXFP4),
+the cache format and options (NVFP4 plain, K-smoothing, adaptive V, both, MXFP4, MXFP4
+with the MX-scaled QK^T),
 chunk sizes, evictions, scene cuts and query counts are drawn per seed.  Resident
 chunks must export bit-exact codes and scales; attention must meet the tolerance."""
 
 import numpy as np
 import pytest
 
-from oracle import CacheModel, chunk_attention_ref, mx_quantize_ref, quantize_ref, channel_mean_ref
+from oracle import (CacheModel, channel_mean_ref, chunk_attention_ref, mx_quantize_ref, mxfp8_dequantize_ref,
+                    mxfp8_quantize_ref, quantize_ref)
 from nvfp4_kv_cache_amd import workloads as W
 
 pytestmark = pytest.mark.gpu
 
 FORMATS = [dict(), dict(k_smooth=True), dict(v_adaptive=True), dict(k_smooth=True, v_adaptive=True),
-           dict(mxfp4=True)]
+           dict(mxfp4=True), dict(mxfp4=True, mx_scaled_qk=True)]
 
 
 @pytest.fixture(scope="module")
@@ -45,7 +47,8 @@ def test_random_config(ops, seed):
     fmt = FORMATS[seed % len(FORMATS)]
     print(f"[seed {seed}] H={H} D={D} T_f={T_f} sink={sink} window={window} shot={shot} {fmt}", flush=True)
     cache = ops.KVCache(H, D, T_f, sink, window, shot_frames=shot, **fmt)
-    model = CacheModel(H, D, T_f, sink, window, shot_frames=shot, **fmt)
+    model = CacheModel(H, D, T_f, sink, window, shot_frames=shot,
+                       **{k: v for k, v in fmt.items() if k != "mx_scaled_qk"})
     chunk = 0
     for step in range(int(rng.integers(3, 8))):
         if shot and rng.random() < 0.3:
@@ -74,6 +77,7 @@ def test_random_config(ops, seed):
         scale = float(rng.uniform(0.02, 0.2))
         out = host(cache.attention(dev(q), dev(ko), dev(vo), scale))
         ck, cv = model.dequantized_kv()
-        want = chunk_attention_ref(q, ko, vo, ck, cv, scale)
+        qc = mxfp8_dequantize_ref(*mxfp8_quantize_ref(q)) if fmt.get("mx_scaled_qk") else None
+        want = chunk_attention_ref(q, ko, vo, ck, cv, scale, q_cache64=qc)
         check_attention(out, want, f"seed {seed} step {step} n_q={n_q} cache={model.n_tokens()}")
     cache.close()

@@ -126,8 +126,10 @@ def test_storage_bytes_budget(real):
     mx = real.kvcache_storage_bytes(ctypes.byref(Cfg(12, 128, 1560, 3, 9, 0, 4)))
     elems = 12 * 128 * 1560 * 12
     assert plain - mx == 2 * (elems // 16 - elems // 32)
-    for opts in (5, 6, 7, 8, 16):
+    for opts in (5, 6, 7, 8, 9, 10, 16):
         assert real.kvcache_storage_bytes(ctypes.byref(Cfg(12, 128, 1560, 3, 9, 0, opts))) == 0
+    # the MX-scaled QK^T needs the MXFP4 cache, whose storage it shares
+    assert real.kvcache_storage_bytes(ctypes.byref(Cfg(12, 128, 1560, 3, 9, 0, 12))) == mx
 
 
 # ------------------------------------------------------------ host stub
@@ -290,7 +292,7 @@ def test_cache_options_route_to_their_kernels(stub):
     NVFP4 one), and its attention and export launches carry the format."""
     stub.stub_last_attn_k_mean.restype = ctypes.c_int64
     d = ctypes.c_void_p(0x1000)
-    for opts in (0, 1, 2, 3, 4):
+    for opts in (0, 1, 2, 3, 4, 12):
         before = [stub.stub_calls(k) for k in range(5)]
         c = StubCache(stub, Cfg(2, 128, 16, 1, 3, 0, opts))
         assert c.append(2) == OK
@@ -303,7 +305,7 @@ def test_cache_options_route_to_their_kernels(stub):
             assert calls[3] == (1 if opts & 1 else 0)
             assert stub.stub_last_quant_options() == opts
         assert stub.chunk_attention(c.h, d, d, d, 8, 0.125, d, None) == OK
-        assert stub.stub_last_attn_mx() == (1 if opts & 4 else 0)
+        assert stub.stub_last_attn_mx() == (2 if opts & 8 else 1 if opts & 4 else 0)
         assert (stub.stub_last_attn_k_mean() != 0) == bool(opts & 1)
         assert stub.kvcache_export_chunk(c.h, 0, d, d, d, d, d, d, None) == OK
         assert stub.stub_last_export_block() == (32 if opts & 4 else 16)
