@@ -74,6 +74,8 @@ def parse():
                         "the HBM byte counters)")
     p.add_argument("--mxfp4", action="store_true",
                    help="with --only attention / quantize: the cache holds MXFP4 instead of NVFP4")
+    p.add_argument("--mx-scaled-qk", action="store_true",
+                   help="with --only attention --mxfp4: QK^T on the MX-scaled matrix cores (MXFP8 queries)")
     return p.parse_args()
 
 
@@ -200,7 +202,8 @@ def roofline_only(args, torch, ops, W, device):
     of this command sees only the timed attention launches."""
     wl = W.WORKLOADS["rollout"]
     cache = ops.KVCache(wl.n_heads, wl.head_dim, wl.tokens_per_frame, wl.sink_frames,
-                        wl.window_frames, device=device, mxfp4=args.mxfp4)
+                        wl.window_frames, device=device, mxfp4=args.mxfp4,
+                        mx_scaled_qk=args.mxfp4 and args.mx_scaled_qk)
     n_fill = (wl.sink_frames + wl.window_frames + wl.chunk_frames - 1) // wl.chunk_frames
     for c in range(n_fill):
         kc, vc = (W.draw_device_normal(wl, c, W.APPEND_STEP, t, device) for t in (W.K_ID, W.V_ID))
@@ -248,12 +251,13 @@ def quantize_leg(args, torch, ops, W, device, k_smooth=False, v_adaptive=False, 
     return out, sets
 
 
-def attention_config(name, args, torch, ops, W, device, k_smooth=False, v_adaptive=False, mxfp4=False):
+def attention_config(name, args, torch, ops, W, device, k_smooth=False, v_adaptive=False, mxfp4=False,
+                     mx_scaled_qk=False):
     wl = W.WORKLOADS[name]
     log(f"{name}: building the cache from {wl.n_cache_chunks} host-drawn chunks")
     cache = ops.KVCache(wl.n_heads, wl.head_dim, wl.tokens_per_frame, wl.sink_frames,
                         wl.window_frames, device=device, k_smooth=k_smooth, v_adaptive=v_adaptive,
-                        mxfp4=mxfp4)
+                        mxfp4=mxfp4, mx_scaled_qk=mx_scaled_qk)
     for c in range(wl.n_cache_chunks):
         k, v = W.clean_chunk(wl, c)
         cache.append(dev_bits(torch, k, device), dev_bits(torch, v, device), wl.chunk_frames)
@@ -371,6 +375,10 @@ def main():
         log(f"quantize, MXFP4: {qm['us_per_append']:.2f} us/append = {qm['GB_per_s']:.1f} GB/s")
         configs["wan13b_mxfp4"] = attention_config("wan13b", args, torch, ops, W, device, mxfp4=True)
         log(f"wan13b, MXFP4 cache: {configs['wan13b_mxfp4']['us']:.1f} us")
+        configs["wan13b_mxfp4_scaled_qk"] = attention_config("wan13b", args, torch, ops, W, device, mxfp4=True,
+                                                             mx_scaled_qk=True)
+        log(f"wan13b, MXFP4 cache, MX-scaled QK^T with MXFP8 queries: "
+            f"{configs['wan13b_mxfp4_scaled_qk']['us']:.1f} us")
     configs["quantize"] = {k: qz[k] for k in ("us_per_append", "GB_per_s", "bytes_per_append")}
     configs["quantize"]["frac_hbm_peak"] = qz["roofline"]["frac"]
 
@@ -399,7 +407,7 @@ def main():
         },
         "latent_frames_per_s": r["frames_per_s"],
         "wall_ms_per_step": r["wall_ms_per_step"],
-        "roofline": {"bound": "mfma", "kernel": "chunk_attention_kernel<128, false> (NVFP4 cache)",
+        "roofline": {"bound": "mfma", "kernel": "chunk_attention_kernel<128, false, false> (NVFP4 cache)",
                      "achieved": r["attn_tflops"], "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": r["attn_tflops"] / MFMA_BF16_PEAK_TFLOPS,
                      "traffic": measured_traffic("attention"),
