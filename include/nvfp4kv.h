@@ -227,7 +227,8 @@ int kvcache_chunk_count(const kvcache *c, int32_t *n_chunks);
 
 /* Noisy-chunk attention (paper sections 2.1 and 4.2): for every head,
  *   out = softmax(q K^T * softmax_scale) V,  K = [cache K ; k_own],  V = [cache V ; v_own]
- * over all cached tokens (sink and window, NVFP4, dequantized inside the kernel) and
+ * over all cached tokens (global sink, shot-level sink and window; NVFP4, or MXFP4 with
+ * NVFP4KV_MXFP4, dequantized inside the kernel) and
  * the chunk's own n_q bf16 tokens, with no mask (bidirectional inside the chunk).
  *   q, k_own, v_own  bf16 [H, n_q, D] (finite; |v_own| < 65504);
  *   out              fp32 [H, n_q, D];  n_q >= 1;  softmax_scale > 0 and finite.
