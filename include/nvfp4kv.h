@@ -230,7 +230,7 @@ int kvcache_chunk_count(const kvcache *c, int32_t *n_chunks);
  * over all cached tokens (global sink, shot-level sink and window; NVFP4, or MXFP4 with
  * NVFP4KV_MXFP4, dequantized inside the kernel) and
  * the chunk's own n_q bf16 tokens, with no mask (bidirectional inside the chunk).
- *   q, k_own, v_own  bf16 [H, n_q, D] (finite; |v_own| < 65504);
+ *   q, k_own, v_own  bf16 [H, n_q, D] (finite);
  *   out              fp32 [H, n_q, D];  n_q >= 1;  softmax_scale > 0 and finite.
  * The work (query blocks x key tiles) is spread evenly over every CU; query blocks
  * cut between workgroups are merged through the cache's scratch, so attention calls

@@ -31,10 +31,10 @@
 //    owns one query column and 16 keys, which is also exactly the lane layout of the
 //    B operand of O^T = V^T P^T, so P never leaves registers.  V is stored in LDS as
 //    V^T with the keys of each 16-key group permuted to match.
-//  * The own segment runs after the cache with Q reloaded as bf16 and K_own in
-//    bf16 (v_mfma_f32_32x32x16_bf16); V_own is converted to fp16 for the PV product
-//    (|v| < 65504 required).  V_own is prefetched into registers one tile ahead;
-//    K_own is fetched at the top of the iteration that stores it.
+//  * The own segment runs after the cache with Q reloaded as bf16, K_own and V_own
+//    in bf16 as given (v_mfma_f32_32x32x16_bf16 for QK^T and PV, P rounded to bf16
+//    nearest-even).  V_own is prefetched into registers one tile ahead (transposed
+//    there); K_own is fetched at the top of the iteration that stores it.
 //  * Online softmax in fp32 with exp2 (log2 e folded into the multiplier).  The
 //    running maximum is raised only when a tile's maximum exceeds it by more than
 //    8 (in log2 units), so the accumulator rescale is rare; probabilities are then
@@ -340,17 +340,17 @@ __device__ __forceinline__ void store_own_k(const uint4 (&k)[2], uint16_t *Ks) {
   *reinterpret_cast<uint4 *>(Ks + ks_off<D>(key, 2 * c + 1)) = k[1];
 }
 
-// V^T as fp16 in the permuted key order
+// V^T as bf16 (the values as given) in the permuted key order
 template <int D>
 __device__ __forceinline__ void store_own_v(const uint32_t (&v)[8], uint16_t *Vs) {
   const int t = threadIdx.x;
   const int dp = t % (D / 2), g = t / (D / 2);
   const int d = 2 * dp;
-  uint32_t lo[4], hi[4];   // fp16 pairs (key 2i, key 2i+1) of row d and of row d+1
+  uint32_t lo[4], hi[4];   // bf16 pairs (key 2i, key 2i+1) of row d and of row d+1
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    lo[i] = as_u32(pkrtz(__uint_as_float(v[2 * i] << 16), __uint_as_float(v[2 * i + 1] << 16)));
-    hi[i] = as_u32(pkrtz(__uint_as_float(v[2 * i] & 0xFFFF0000u), __uint_as_float(v[2 * i + 1] & 0xFFFF0000u)));
+    lo[i] = (v[2 * i] & 0xFFFFu) | (v[2 * i + 1] << 16);
+    hi[i] = (v[2 * i] >> 16) | (v[2 * i + 1] & 0xFFFF0000u);
   }
   // 8-key group g is half (g & 1) of 16-key group g >> 1: its pairs (0,1),(2,3) go
   // to chunk 2(g>>1) and its pairs (4,5),(6,7) to chunk 2(g>>1)+1, at 8-byte offset
@@ -955,7 +955,7 @@ __global__ __launch_bounds__(Cfg<D>::kThreads, Cfg<D>::kWgPerCu) void chunk_atte
             store_own_v<D>(rv, Vs[buf ^ 1]);
             store_own_k<D>(rk, Ks[buf ^ 1]);
             load_own_v<D>(a, h, min(t + 2, e - 1) * kBN, kBN, rv);
-            softmax_pv<D, false>(Vs[buf], s, cmul, 0.0f, kBN, sm, acc);
+            softmax_pv<D, false, true>(Vs[buf], s, cmul, 0.0f, kBN, sm, acc);
             __syncthreads();
             buf ^= 1;
           }
@@ -970,7 +970,7 @@ __global__ __launch_bounds__(Cfg<D>::kThreads, Cfg<D>::kWgPerCu) void chunk_atte
           store_own_v<D>(rv, Vs[0]);
           __syncthreads();
           qk_tile<D, true>(Ks[0], qr, s);
-          softmax_pv<D, true>(Vs[0], s, cmul, 0.0f, nval, sm, acc);
+          softmax_pv<D, true, true>(Vs[0], s, cmul, 0.0f, nval, sm, acc);
         }
       }
 

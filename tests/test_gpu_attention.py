@@ -262,3 +262,30 @@ def test_k_smoothing_and_adaptive_v_attention(ops, D):
         model.append(k, v)
         q, ko, vo = (rand_bits(rng, (H, 100, D)) for _ in range(3))
         run_case(ops, cache, model, q, ko, vo, 1.0 / np.sqrt(D), what=f"smooth D{D} tokens {model.n_tokens()}")
+
+
+def test_own_values_beyond_fp16_range(ops):
+    """The chunk's own K/V enter the bf16 matrix cores as given: values far beyond
+    fp16's range (|v| up to ~1e6) and tiny ones.  The bar is scaled by the size of V
+    (max-abs 1e-2 relative to max |V|, relative L2 5e-3)."""
+    from gpu_util import dev, host
+    rng = np.random.default_rng(71)
+    H, D, T_f = 2, 128, 64
+    k1, v1 = rand_bits(rng, (H, 2 * T_f, D)), rand_bits(rng, (H, 2 * T_f, D))
+    cache, model = build_both(ops, H, D, T_f, 1, 3, [(k1, v1)])
+    q, ko = rand_bits(rng, (H, 150, D)), rand_bits(rng, (H, 150, D))
+    vf = rng.standard_normal((H, 150, D)).astype(np.float32)
+    vf[0] *= 1e6
+    vf[1, :, :64] *= 1e-20
+    vo = W.f32_to_bf16_bits(vf)
+    scale = 1.0 / np.sqrt(D)
+    out = host(cache.attention(dev(q), dev(ko), dev(vo), scale))
+    ck, cv = model.dequantized_kv()
+    want = chunk_attention_ref(q, ko, vo, ck, cv, scale)
+    for h in range(H):
+        vmax = max(np.abs(cv[h]).max(), np.abs((vo[h].astype(np.uint32) << 16).view(np.float32)).max())
+        err = np.abs(out[h] - want[h]).max()
+        rel = np.linalg.norm(out[h] - want[h]) / np.linalg.norm(want[h])
+        print(f"[own beyond fp16, head {h}] max_abs/max|V| = {err / vmax:.3e} rel_l2 = {rel:.3e}", flush=True)
+        assert np.all(np.isfinite(out[h]))
+        assert err <= 1e-2 * vmax and rel <= 5e-3
