@@ -289,3 +289,32 @@ def test_own_values_beyond_fp16_range(ops):
         print(f"[own beyond fp16, head {h}] max_abs/max|V| = {err / vmax:.3e} rel_l2 = {rel:.3e}", flush=True)
         assert np.all(np.isfinite(out[h]))
         assert err <= 1e-2 * vmax and rel <= 5e-3
+
+
+@pytest.mark.parametrize("fmt", [dict(), dict(mxfp4=True)])
+def test_largest_frame_count(ops, fmt):
+    """The largest cache the configuration accepts: 4 sink + 60 window frames (64
+    frames, 65,536 tokens of 1024-token frames), filled by single-frame appends and
+    rolled past once; attention over all of it on sampled query rows, and the last
+    chunk's codes bit-exact."""
+    from gpu_util import dev, host, check_attention
+    from oracle import quantize_ref, mx_quantize_ref
+    rng = np.random.default_rng(81)
+    H, D, T_f, sink, window = 2, 128, 1024, 4, 60
+    cache = ops.KVCache(H, D, T_f, sink, window, **fmt)
+    model = CacheModel(H, D, T_f, sink, window, **fmt)
+    for c in range(sink + window + 3):
+        k, v = rand_bits(rng, (H, T_f, D)), rand_bits(rng, (H, T_f, D))
+        cache.append(dev(k), dev(v), 1)
+        model.append(k, v)
+    assert model.n_tokens() == (sink + window) * T_f
+    kc, ks, vc, vs, _, _ = (host(t) for t in cache.export_chunk(sink + window + 2))
+    qz = mx_quantize_ref if fmt else (lambda x: quantize_ref(x)[:2])
+    assert all(np.array_equal(a, b) for a, b in zip((kc, ks, vc, vs), (*qz(k), *qz(v))))
+    n_q = 700
+    q, ko, vo = (rand_bits(rng, (H, n_q, D)) for _ in range(3))
+    rows = np.unique(np.concatenate([np.arange(0, 20), rng.integers(0, n_q, 30), [n_q - 1]]))
+    out = host(cache.attention(dev(q), dev(ko), dev(vo), 1.0 / np.sqrt(D)))
+    ck, cv = model.dequantized_kv()
+    want = chunk_attention_ref(q, ko, vo, ck, cv, 1.0 / np.sqrt(D), rows=rows)
+    check_attention(out[:, rows], want, f"64 frames x 1024 tokens {fmt}")
