@@ -60,7 +60,8 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=36)
     p.add_argument("--warmup", type=int, default=4)
-    p.add_argument("--reps", type=int, default=30, help="launches per kernel microbenchmark")
+    p.add_argument("--reps", type=int, default=100, help="launches per attention microbenchmark")
+    p.add_argument("--quantize-reps", type=int, default=1000, help="appends timed by the quantize leg")
     p.add_argument("--warm-launches", type=int, default=30,
                    help="untimed attention launches enqueued right before the timed ones")
     p.add_argument("--no-cpu-baseline", action="store_true")
@@ -106,27 +107,46 @@ def measured_traffic(leg):
         return None
 
 
-def timed(fn, reps, torch, warm=3, host_us_per_call=None):
+def timed(fn, reps, torch, warm=3, host_us_per_call=None, dist=None):
     """Mean ms per call of fn() over `reps` back-to-back calls, HIP events on
     the current stream (the stream the library launches on).  `warm` untimed
     calls are enqueued right before the timed ones, so the GPU is at its working
     clock when timing starts.  For calls shorter than the host's enqueue time,
     `host_us_per_call` queues a device-side sleep first, long enough for the host
     to enqueue every timed call before the first one starts: the events then time
-    back-to-back GPU execution, not the Python call rate."""
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    fn()
-    torch.cuda.synchronize()
-    for _ in range(warm):
+    back-to-back GPU execution, not the Python call rate.  With a dict `dist`, an
+    event also separates every two calls, and the median, p10 and p90 of the
+    per-call times (µs) are stored in it."""
+    def run(per_call):
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1 if per_call else 2)]
         fn()
-    if host_us_per_call:
-        torch.cuda._sleep(int(2.0e3 * host_us_per_call * reps) + 1_000_000)   # ~cycles at >= 2 GHz
-    e0.record()
-    for _ in range(reps):
-        fn()
-    e1.record()
-    torch.cuda.synchronize()
-    return e0.elapsed_time(e1) / reps
+        torch.cuda.synchronize()
+        for _ in range(warm):
+            fn()
+        if host_us_per_call:
+            torch.cuda._sleep(int(2.0e3 * host_us_per_call * reps) + 1_000_000)   # ~cycles at >= 2 GHz
+        ev[0].record()
+        for i in range(reps):
+            fn()
+            if per_call:
+                ev[i + 1].record()
+        if not per_call:
+            ev[1].record()
+        torch.cuda.synchronize()
+        return ev
+
+    ev = run(False)
+    mean_ms = ev[0].elapsed_time(ev[1]) / reps
+    if dist is not None:
+        # a second pass with an event between every two calls (each event adds a little
+        # to the call it follows, so the mean above is taken without them)
+        import numpy as np
+        ev = run(True)
+        t = np.array([ev[i].elapsed_time(ev[i + 1]) * 1e3 for i in range(reps)])
+        dist.update({"median_us": float(np.median(t)), "p10_us": float(np.percentile(t, 10)),
+                     "p90_us": float(np.percentile(t, 90)), "reps": reps,
+                     "note": "per-call times from a second pass with an event between calls"})
+    return mean_ms
 
 
 def dev_bits(torch, bits, device):
@@ -189,11 +209,12 @@ def attention_roofline(args, torch, ops, W, cache, qkv, out):
     time over `reps` back-to-back launches (HIP events on the launch stream)."""
     wl = W.WORKLOADS["rollout"]
     q, k, v = qkv
+    dist = {}
     ams = timed(lambda: cache.attention(q, k, v, wl.softmax_scale, out=out), args.reps, torch,
-                warm=args.warm_launches)
+                warm=args.warm_launches, dist=dist)
     flops = W.attention_flops(wl.n_heads, wl.n_q, cache.tokens()[0] + cache.tokens()[1] + wl.n_q,
                               wl.head_dim)
-    return {"attn_ms": ams, "attn_flops": flops, "attn_tflops": flops / (ams * 1e-3) / 1e12}
+    return {"attn_ms": ams, "attn_flops": flops, "attn_tflops": flops / (ams * 1e-3) / 1e12, "attn_dist": dist}
 
 
 def roofline_only(args, torch, ops, W, device):
@@ -213,7 +234,7 @@ def roofline_only(args, torch, ops, W, device):
     r = attention_roofline(args, torch, ops, W, cache, qkv, out)
     return {"launch_us": r["attn_ms"] * 1e3, "flops_per_launch": r["attn_flops"],
             "tflops": r["attn_tflops"], "frac_mfma_peak": r["attn_tflops"] / MFMA_BF16_PEAK_TFLOPS,
-            "cache_tokens": sum(cache.tokens())}
+            "cache_tokens": sum(cache.tokens()), "per_launch": r["attn_dist"]}
 
 
 def quantize_leg(args, torch, ops, W, device, k_smooth=False, v_adaptive=False, sets=None, mxfp4=False):
@@ -238,12 +259,13 @@ def quantize_leg(args, torch, ops, W, device, k_smooth=False, v_adaptive=False, 
         it[0] += 1
         cache.append(k, v, wl.chunk_frames)
 
-    reps = max(args.reps, 50)
-    ms = timed(app, reps, torch, warm=10, host_us_per_call=60.0)
+    reps = max(args.quantize_reps, 1)
+    dist = {}
+    ms = timed(app, reps, torch, warm=10, host_us_per_call=60.0, dist=dist)
     elems = wl.n_heads * wl.chunk_tokens * wl.head_dim
     nbytes = 2 * (W.quantize_bytes_mx(elems) if mxfp4 else W.quantize_bytes(elems))
     gbps = nbytes / (ms * 1e-3) / 1e9
-    out = {"us_per_append": ms * 1e3, "bytes_per_append": nbytes, "GB_per_s": gbps,
+    out = {"us_per_append": ms * 1e3, "bytes_per_append": nbytes, "GB_per_s": gbps, "per_append": dist,
            "roofline": {"bound": "hbm", "achieved": gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                         "frac": gbps / HBM_PEAK_GBPS,
                         "traffic": None if (k_smooth or v_adaptive) else
@@ -411,7 +433,8 @@ def main():
                      "achieved": r["attn_tflops"], "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": r["attn_tflops"] / MFMA_BF16_PEAK_TFLOPS,
                      "traffic": measured_traffic("attention"),
-                     "launch_us": r["attn_ms"] * 1e3, "flops_per_launch": r["attn_flops"]},
+                     "launch_us": r["attn_ms"] * 1e3, "flops_per_launch": r["attn_flops"],
+                     "per_launch": r["attn_dist"]},
         "quantize": qz,
         "configs": configs,
         "cpu_baseline": None,
