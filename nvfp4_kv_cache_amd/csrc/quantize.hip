@@ -80,6 +80,18 @@ __device__ __forceinline__ float div_rn(float x, float b, float r) {
   return __builtin_fmaf(-e, r, q);
 }
 
+// The same with ONE correction, for bf16 numerators: then it is already RN(x / b)
+// whenever x, b, the product q0 b and the remainder are normal fp32 numbers.  This
+// was checked exhaustively: every bf16 significand against every fp32 significand
+// (2^7 x 2^23 pairs; a power-of-two change of x or b scales every step exactly, so
+// the pairs cover all exponents in that range).  The encoder keeps the element
+// quotients in it (see extreme_rescale).
+__device__ __forceinline__ float div_rn_bf16(float x, float b, float r) {
+  const float q = x * r;
+  const float e = __builtin_fmaf(q, b, -x);
+  return __builtin_fmaf(-e, r, q);
+}
+
 // Per-tensor constants of the encoder.
 struct TensorConsts {
   float st;       // s_t
@@ -88,10 +100,13 @@ struct TensorConsts {
   float xs;       // 2^K applied to x and eff alike when s_t is extreme, else 1
 };
 
-// Power of two that brings s_t near 2^-10 when s_t leaves [2^-100, 2^100]: x / eff
+// Power of two that brings s_t near 2^-10 when s_t leaves [2^-80, 2^100]: x / eff
 // is unchanged when both are scaled by it, and all the scaled operands stay normal.
+// Inside the range eff >= 2^-9 s_t >= 2^-89, so every quotient that can round to a
+// nonzero code (x / eff > 1/4) has x > 2^-91 and a remainder near x 2^-24, far above
+// the smallest normal; a smaller quotient gives code 0 however it is rounded.
 __device__ __forceinline__ float extreme_rescale(float st) {
-  if (!(st > 0.0f) || (st >= 0x1p-100f && st <= 0x1p100f)) return 1.0f;
+  if (!(st > 0.0f) || (st >= 0x1p-80f && st <= 0x1p100f)) return 1.0f;
   const int e = st < 0x1p-126f ? -127 : int((__float_as_uint(st) >> 23) & 0xFF) - 127;
   return __builtin_ldexpf(1.0f, -10 - e);
 }
@@ -130,9 +145,12 @@ __device__ __forceinline__ float2 divisor_entry(uint32_t sc, float st, float xs)
   return make_float2(eff, eff > 0.0f ? 1.0f / eff : 0.0f);
 }
 
-template <bool SCALED>
+// BF16: x is a bf16 value (8 significant bits); otherwise any fp32 (K minus its
+// channel means).
+template <bool SCALED, bool BF16 = true>
 __device__ __forceinline__ float quot(float x, float eff, float r, float xs) {
-  return div_rn(SCALED ? x * xs : x, eff, r);
+  if constexpr (BF16) return div_rn_bf16(SCALED ? x * xs : x, eff, r);
+  else return div_rn(SCALED ? x * xs : x, eff, r);
 }
 
 // One token's 16 bf16 of a block as fp32 (exact), element order.
@@ -191,16 +209,16 @@ __device__ __forceinline__ uint32_t choose_scale46(const float (&x)[16], float a
 }
 
 // Codec layout: one token's 16 values -> 8 bytes (element 2k in the low nibble).
-template <bool SCALED>
+template <bool SCALED, bool BF16 = true>
 __device__ __forceinline__ uint2 encode_token(const float (&x)[16], float eff, float r, float xs) {
   uint32_t c[2] = {0u, 0u};
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
     const float *y = x + 8 * h;
-    c[h] = cvt_fp4<0>(c[h], quot<SCALED>(y[0], eff, r, xs), quot<SCALED>(y[1], eff, r, xs));
-    c[h] = cvt_fp4<1>(c[h], quot<SCALED>(y[2], eff, r, xs), quot<SCALED>(y[3], eff, r, xs));
-    c[h] = cvt_fp4<2>(c[h], quot<SCALED>(y[4], eff, r, xs), quot<SCALED>(y[5], eff, r, xs));
-    c[h] = cvt_fp4<3>(c[h], quot<SCALED>(y[6], eff, r, xs), quot<SCALED>(y[7], eff, r, xs));
+    c[h] = cvt_fp4<0>(c[h], quot<SCALED, BF16>(y[0], eff, r, xs), quot<SCALED, BF16>(y[1], eff, r, xs));
+    c[h] = cvt_fp4<1>(c[h], quot<SCALED, BF16>(y[2], eff, r, xs), quot<SCALED, BF16>(y[3], eff, r, xs));
+    c[h] = cvt_fp4<2>(c[h], quot<SCALED, BF16>(y[4], eff, r, xs), quot<SCALED, BF16>(y[5], eff, r, xs));
+    c[h] = cvt_fp4<3>(c[h], quot<SCALED, BF16>(y[6], eff, r, xs), quot<SCALED, BF16>(y[7], eff, r, xs));
   }
   return make_uint2(c[0], c[1]);
 }
@@ -252,7 +270,7 @@ __device__ __forceinline__ void item_canonical(const QuantArgs &a, const Octet &
     }
     const uint32_t sc = scale_code(absmax16(x), tc);
     const float2 dv = tab[sc];
-    const uint2 c = encode_token<SCALED>(x, dv.x, dv.y, tc.xs);
+    const uint2 c = encode_token<SCALED, !MEAN>(x, dv.x, dv.y, tc.xs);
     if (j < o.nvalid) {
       const int64_t row = int64_t(o.h) * a.rows + o.row + j;
       *reinterpret_cast<uint2 *>(qt.codes + row * (a.D / 2) + b * 8) = c;

@@ -63,6 +63,25 @@ def test_codec_random(ops, ws, shape, scale):
     assert_codec_equal(codec_gpu(ops, ws, bits), quantize_ref(bits), f"t4 {shape} x{scale}")
 
 
+@pytest.mark.parametrize("e", [-68, -70, -72, -75, -80, -85, -90, -95])
+def test_small_tensor_scales(ops, ws, e):
+    """Tensors whose s_t falls between 2^-102 and 2^-78: around the range limit
+    below which the encoder moves x and eff by a power of two so that every element
+    quotient and its remainder stay normal fp32 numbers.  Codec and cache append
+    (both tensors of one append at different scales) against the oracle."""
+    from gpu_util import dev, host
+    rng = np.random.default_rng(500 - e)
+    a = t4_bits(rng, (3, 120, 128), 2.0 ** e)
+    b = t4_bits(rng, (3, 120, 128), 2.0 ** (e - 3))
+    assert_codec_equal(codec_gpu(ops, ws, a), quantize_ref(a), f"codec 2^{e}")
+    cache = ops.KVCache(3, 128, 40, 1, 3)
+    cache.append(dev(a), dev(b), 3)
+    kc, ks, vc, vs, sk, sv = cache.export_chunk(0)
+    assert_codec_equal((host(kc), host(ks), host(sk)[0]), quantize_ref(a), f"append 2^{e} K")
+    assert_codec_equal((host(vc), host(vs), host(sv)[0]), quantize_ref(b), f"append 2^{e} V")
+    cache.close()
+
+
 def test_codec_special_values(ops, ws):
     """Zeros of both signs, bf16 subnormals, values on E2M1 thresholds after
     scaling, and a block far below the tensor amax (subnormal E4M3 scales)."""
