@@ -81,11 +81,13 @@ __device__ __forceinline__ float div_rn(float x, float b, float r) {
 }
 
 // The same with ONE correction, for bf16 numerators: then it is already RN(x / b)
-// whenever x, b, the product q0 b and the remainder are normal fp32 numbers.  This
-// was checked exhaustively: every bf16 significand against every fp32 significand
-// (2^7 x 2^23 pairs; a power-of-two change of x or b scales every step exactly, so
-// the pairs cover all exponents in that range).  The encoder keeps the element
-// quotients in it (see extreme_rescale).
+// whenever the remainder q0 b - x is computed exactly.  This was checked
+// exhaustively: every bf16 significand against every fp32 significand (2^7 x 2^23
+// pairs; a power-of-two change of x or b scales every step exactly, so the pairs
+// cover every exponent pair with an exact remainder and a normal quotient).  The
+// remainder is a multiple of about 2^-47 x, so it is exact for x >= 2^-102; below
+// that its rounding can move a quotient that lies next to a rounding boundary.  The
+// encoder keeps every quotient that matters in that range (see extreme_rescale).
 __device__ __forceinline__ float div_rn_bf16(float x, float b, float r) {
   const float q = x * r;
   const float e = __builtin_fmaf(q, b, -x);
@@ -103,8 +105,8 @@ struct TensorConsts {
 // Power of two that brings s_t near 2^-10 when s_t leaves [2^-80, 2^100]: x / eff
 // is unchanged when both are scaled by it, and all the scaled operands stay normal.
 // Inside the range eff >= 2^-9 s_t >= 2^-89, so every quotient that can round to a
-// nonzero code (x / eff > 1/4) has x > 2^-91 and a remainder near x 2^-24, far above
-// the smallest normal; a smaller quotient gives code 0 however it is rounded.
+// nonzero code (x / eff > 1/4) has x > 2^-91, where the one-correction quotient is
+// exact; a smaller quotient gives code 0 however it is rounded.
 __device__ __forceinline__ float extreme_rescale(float st) {
   if (!(st > 0.0f) || (st >= 0x1p-80f && st <= 0x1p100f)) return 1.0f;
   const int e = st < 0x1p-126f ? -127 : int((__float_as_uint(st) >> 23) & 0xFF) - 127;
@@ -161,6 +163,20 @@ __device__ __forceinline__ void unpack16(const uint4 (&u)[2], float (&x)[16]) {
     x[2 * k] = __uint_as_float(w[k] << 16);
     x[2 * k + 1] = __uint_as_float(w[k] & 0xFFFF0000u);
   }
+}
+
+// bf16 bits of max |x| over one token's 16 values (finite inputs: the order of the
+// magnitude bits is the order of the values), on packed 16-bit maxima.
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t block_max_bits(const uint4 (&u)[2]) {
+  auto m = [](uint32_t a, uint32_t b) {
+    return __builtin_bit_cast(uint32_t, __builtin_elementwise_max(__builtin_bit_cast(u16x2, a),
+                                                                   __builtin_bit_cast(u16x2, b)));
+  };
+  const uint32_t k = 0x7FFF7FFFu;
+  const uint32_t r = m(m(m(u[0].x & k, u[0].y & k), m(u[0].z & k, u[0].w & k)),
+                       m(m(u[1].x & k, u[1].y & k), m(u[1].z & k, u[1].w & k)));
+  return max(r & 0xFFFFu, r >> 16);
 }
 
 __device__ __forceinline__ float absmax16(const float (&x)[16]) {
@@ -242,10 +258,12 @@ struct Octet {
 
 // Canonical item: per token, block max -> scale byte -> divisor -> 8 code bytes.
 // MEAN: K-smoothing, the block's 16 channel means are subtracted first (fp32).
+// bmax (optional): the tokens' block maxima as bf16 bits, taken before s_t was known.
 template <bool SCALED, bool MEAN = false>
 __device__ __forceinline__ void item_canonical(const QuantArgs &a, const Octet &o, int b,
                                                const uint4 (&u)[kOctet][2],
-                                               const TensorConsts &tc, const float2 *tab) {
+                                               const TensorConsts &tc, const float2 *tab,
+                                               const uint32_t *bmax = nullptr) {
   const QuantTensor &qt = a.t[o.tensor];
   const int nb = a.D >> 4;
   float mu[16];
@@ -268,7 +286,7 @@ __device__ __forceinline__ void item_canonical(const QuantArgs &a, const Octet &
 #pragma unroll
       for (int i = 0; i < 16; ++i) x[i] = x[i] - mu[i];
     }
-    const uint32_t sc = scale_code(absmax16(x), tc);
+    const uint32_t sc = scale_code(bmax ? __uint_as_float(bmax[j] << 16) : absmax16(x), tc);
     const float2 dv = tab[sc];
     const uint2 c = encode_token<SCALED, !MEAN>(x, dv.x, dv.y, tc.xs);
     if (j < o.nvalid) {
@@ -285,7 +303,8 @@ __device__ __forceinline__ void item_canonical(const QuantArgs &a, const Octet &
 template <bool SCALED, bool ADAPT = false>
 __device__ __forceinline__ void item_transposed(const QuantArgs &a, const Octet &o, int b,
                                                 const uint4 (&u)[kOctet][2],
-                                                const TensorConsts &tc, const float2 *tab) {
+                                                const TensorConsts &tc, const float2 *tab,
+                                                const uint32_t *bmax = nullptr) {
   const QuantTensor &qt = a.t[o.tensor];
   const int nb = a.D >> 4;
   uint32_t sc[kOctet];
@@ -297,7 +316,8 @@ __device__ __forceinline__ void item_transposed(const QuantArgs &a, const Octet 
     float xa[16], xb[16];                                                            \
     unpack16(u[2 * SEL], xa);                                                        \
     unpack16(u[2 * SEL + 1], xb);                                                    \
-    const float ma = absmax16(xa), mb = absmax16(xb);                                \
+    const float ma = bmax ? __uint_as_float(bmax[2 * SEL] << 16) : absmax16(xa);     \
+    const float mb = bmax ? __uint_as_float(bmax[2 * SEL + 1] << 16) : absmax16(xb); \
     sc[2 * SEL] = scale_code(ma, tc);                                                \
     sc[2 * SEL + 1] = scale_code(mb, tc);                                            \
     if constexpr (ADAPT) {                                                           \
@@ -527,11 +547,12 @@ __global__ __launch_bounds__(kQuantThreads) void quantize_fused_kernel(QuantArgs
   uint4 u[kOctet][2];
   const Octet oc = locate_octet(a, blockIdx.x, min(o, opt - 1));
   load_octet(a, oc, b, u);
-  uint32_t mx = 0;
+  // the tokens' block maxima (needed by the encode, known before s_t)
+  uint32_t bm[kOctet], mx = 0;
 #pragma unroll
   for (int j = 0; j < kOctet; ++j) {
-    const uint32_t q = vmax4(u[j][0]), r = vmax4(u[j][1]);
-    mx = max(mx, max(max(q & 0xFFFFu, q >> 16), max(r & 0xFFFFu, r >> 16)));
+    bm[j] = block_max_bits(u[j]);
+    mx = max(mx, bm[j]);
   }
   uint32_t mk = wave_max_u32(oc.tensor == 0 ? mx : 0u);
   uint32_t mv = wave_max_u32(oc.tensor == 1 ? mx : 0u);
@@ -616,11 +637,11 @@ __global__ __launch_bounds__(kQuantThreads) void quantize_fused_kernel(QuantArgs
     const float2 *tab = s_tab[oc.tensor];
     const bool tr = a.t[oc.tensor].transposed != 0;
     if (tc.xs == 1.0f) {
-      if (tr) item_transposed<false>(a, oc, b, u, tc, tab);
-      else item_canonical<false>(a, oc, b, u, tc, tab);
+      if (tr) item_transposed<false>(a, oc, b, u, tc, tab, bm);
+      else item_canonical<false>(a, oc, b, u, tc, tab, bm);
     } else {
-      if (tr) item_transposed<true>(a, oc, b, u, tc, tab);
-      else item_canonical<true>(a, oc, b, u, tc, tab);
+      if (tr) item_transposed<true>(a, oc, b, u, tc, tab, bm);
+      else item_canonical<true>(a, oc, b, u, tc, tab, bm);
     }
   }
 }
