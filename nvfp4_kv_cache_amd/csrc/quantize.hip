@@ -278,6 +278,16 @@ __device__ __forceinline__ void item_canonical(const QuantArgs &a, const Octet &
       mu[4 * k + 3] = m4.w;
     }
   }
+  // with the maxima at hand, every scale byte and divisor first (their table reads
+  // overlap), then the codes
+  uint32_t scp[kOctet];
+  float2 dvp[kOctet];
+  if (bmax) {
+#pragma unroll
+    for (int j = 0; j < kOctet; ++j) scp[j] = scale_code(__uint_as_float(bmax[j] << 16), tc);
+#pragma unroll
+    for (int j = 0; j < kOctet; ++j) dvp[j] = tab[scp[j]];
+  }
 #pragma unroll
   for (int j = 0; j < kOctet; ++j) {
     float x[16];
@@ -286,8 +296,8 @@ __device__ __forceinline__ void item_canonical(const QuantArgs &a, const Octet &
 #pragma unroll
       for (int i = 0; i < 16; ++i) x[i] = x[i] - mu[i];
     }
-    const uint32_t sc = scale_code(bmax ? __uint_as_float(bmax[j] << 16) : absmax16(x), tc);
-    const float2 dv = tab[sc];
+    const uint32_t sc = bmax ? scp[j] : scale_code(absmax16(x), tc);
+    const float2 dv = bmax ? dvp[j] : tab[sc];
     const uint2 c = encode_token<SCALED, !MEAN>(x, dv.x, dv.y, tc.xs);
     if (j < o.nvalid) {
       const int64_t row = int64_t(o.h) * a.rows + o.row + j;
@@ -311,21 +321,37 @@ __device__ __forceinline__ void item_transposed(const QuantArgs &a, const Octet 
   uint32_t out[16];
 #pragma unroll
   for (int d = 0; d < 16; ++d) out[d] = 0u;
-#define NVFP4KV_PAIR(SEL)                                                            \
-  {                                                                                  \
-    float xa[16], xb[16];                                                            \
-    unpack16(u[2 * SEL], xa);                                                        \
-    unpack16(u[2 * SEL + 1], xb);                                                    \
-    const float ma = bmax ? __uint_as_float(bmax[2 * SEL] << 16) : absmax16(xa);     \
-    const float mb = bmax ? __uint_as_float(bmax[2 * SEL + 1] << 16) : absmax16(xb); \
-    sc[2 * SEL] = scale_code(ma, tc);                                                \
-    sc[2 * SEL + 1] = scale_code(mb, tc);                                            \
-    if constexpr (ADAPT) {                                                           \
-      sc[2 * SEL] = choose_scale46<SCALED>(xa, ma, sc[2 * SEL], tc, tab);            \
-      sc[2 * SEL + 1] = choose_scale46<SCALED>(xb, mb, sc[2 * SEL + 1], tc, tab);    \
-    }                                                                                \
-    const float2 da = tab[sc[2 * SEL]], db = tab[sc[2 * SEL + 1]];                   \
-    encode_pair_transposed<SEL, SCALED>(xa, xb, da.x, da.y, db.x, db.y, tc.xs, out); \
+  // with the maxima at hand (no adaptive choice), every scale byte and divisor first
+  float2 dvp[kOctet];
+  const bool pre = bmax && !ADAPT;
+  if (pre) {
+#pragma unroll
+    for (int j = 0; j < kOctet; ++j) sc[j] = scale_code(__uint_as_float(bmax[j] << 16), tc);
+#pragma unroll
+    for (int j = 0; j < kOctet; ++j) dvp[j] = tab[sc[j]];
+  }
+#define NVFP4KV_PAIR(SEL)                                                             \
+  {                                                                                   \
+    float xa[16], xb[16];                                                             \
+    unpack16(u[2 * SEL], xa);                                                         \
+    unpack16(u[2 * SEL + 1], xb);                                                     \
+    float2 da, db;                                                                    \
+    if (pre) {                                                                        \
+      da = dvp[2 * SEL];                                                              \
+      db = dvp[2 * SEL + 1];                                                          \
+    } else {                                                                          \
+      const float ma = bmax ? __uint_as_float(bmax[2 * SEL] << 16) : absmax16(xa);    \
+      const float mb = bmax ? __uint_as_float(bmax[2 * SEL + 1] << 16) : absmax16(xb); \
+      sc[2 * SEL] = scale_code(ma, tc);                                               \
+      sc[2 * SEL + 1] = scale_code(mb, tc);                                           \
+      if constexpr (ADAPT) {                                                          \
+        sc[2 * SEL] = choose_scale46<SCALED>(xa, ma, sc[2 * SEL], tc, tab);           \
+        sc[2 * SEL + 1] = choose_scale46<SCALED>(xb, mb, sc[2 * SEL + 1], tc, tab);   \
+      }                                                                               \
+      da = tab[sc[2 * SEL]];                                                          \
+      db = tab[sc[2 * SEL + 1]];                                                      \
+    }                                                                                 \
+    encode_pair_transposed<SEL, SCALED>(xa, xb, da.x, da.y, db.x, db.y, tc.xs, out);  \
   }
   NVFP4KV_PAIR(0)
   NVFP4KV_PAIR(1)
