@@ -1,0 +1,65 @@
+"""The encoder's element quotient, checked on the host (no GPU): RN(x / eff) from
+r = RN(1 / eff) with one Markstein correction equals the IEEE quotient for bf16
+numerators whenever the remainder is exact.  The C program in host_checks/ runs the
+fp32 steps with the host's fused multiply-add; here it covers every bf16 significand
+against a strided sample of the 2^23 divisor significands (the full sweep takes
+minutes: `one_correction 0 1`).  At exponents whose remainder underflows, the same
+steps can miss by one ulp, which is why the encoder rescales such tensors."""
+
+import os
+import subprocess
+
+import pytest
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+SRC = os.path.join(HERE, "host_checks", "one_correction.c")
+
+
+@pytest.fixture(scope="module")
+def prog(tmp_path_factory):
+    exe = str(tmp_path_factory.mktemp("div") / "one_correction")
+    subprocess.run(["gcc", "-O2", "-std=c99", "-ffp-contract=off", "-o", exe, SRC, "-lm"], check=True)
+    return exe
+
+
+def run(prog, start, step):
+    out = subprocess.run([prog, str(start), str(step)], capture_output=True, text=True)
+    print(out.stdout)
+    return out
+
+
+def test_one_correction_exact_for_bf16_numerators(prog):
+    out = run(prog, 5, 1021)   # 8217 divisor significands x 128 numerators x 7 placements
+    assert out.returncode == 0, out.stdout
+    assert "0 mismatches" in out.stdout
+
+
+def test_divisors_with_all_ones_significand(prog):
+    # the significand 1.11...1 is the classic hard case for reciprocal-based division
+    out = run(prog, (1 << 23) - 1, 1)
+    assert out.returncode == 0, out.stdout
+
+
+def test_underflowing_remainder_can_miss():
+    # a case found by the full sweep: x = 2^-104, eff = (2 - 2^-23) 2^-103.  The
+    # exact quotient is just above 1/4 (code 1); the one-correction steps with a
+    # remainder below 2^-126 return exactly 1/4 (code 0 by ties-to-even).  Shown
+    # with exact rational arithmetic of the same steps.
+    from fractions import Fraction as F
+    import numpy as np
+    x = np.float32(2.0 ** -104)
+    b = np.float32((2 - 2.0 ** -23) * 2.0 ** -103)
+    r = np.float32(1) / b                          # RN(1/b)
+    q0 = np.float32(x * r)                         # RN(x r)
+
+    def rn32(v):                                   # round an exact rational to fp32 (subnormals kept)
+        f = np.float32(float(v))
+        # float(v) rounds to fp64 first; fix a possible double rounding by comparing neighbours
+        cands = [np.nextafter(f, np.float32(-np.inf)), f, np.nextafter(f, np.float32(np.inf))]
+        best = min(cands, key=lambda c: (abs(F(float(c)) - v), int(np.frombuffer(c.tobytes(), np.uint32)[0]) & 1))
+        return best
+
+    e = rn32(F(float(q0)) * F(float(b)) - F(float(x)))
+    q1 = rn32(F(float(q0)) - F(float(e)) * F(float(r)))
+    want = rn32(F(float(x)) / F(float(b)))
+    assert float(want) > 0.25 and float(q1) == 0.25
