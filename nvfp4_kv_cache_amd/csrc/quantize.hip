@@ -7,30 +7,32 @@
 // E4M3 (nearest, ties to even, saturating at 448); eff = E4M3(bs) * s_t;
 // code = E2M1(|x| / eff) (nearest, ties to even, saturating at 6) with x's sign.
 //
-// Two kernels.  The tensor scale needs the amax of the whole chunk tensor (all
-// heads) before any block can be encoded; a grid-wide barrier inside one kernel
-// would need a cooperative launch, which costs far more on this GPU than the whole
-// quantization, so:
-//   1. quantize_amax_kernel streams K and V once and writes one partial maximum
-//      per workgroup (no atomics);
-//   2. quantize_encode_kernel reduces the partials, then re-reads its tiles (the
-//      chunk, 28.8 MB for the 1.3B shape, is still in the 256 MB Infinity Cache)
-//      and writes codes and scales.
+// Two schedules.  The tensor scale needs the amax of the whole chunk tensor (all
+// heads) before any block can be encoded.
+//   * Cache appends (quantize_fused_kernel, one pass): every workgroup of a grid
+//     that is resident all at once (the launcher checks the occupancy) loads its
+//     tile into registers, publishes its maxima in an epoch-tagged workspace slot,
+//     waits (bounded) for every slot of the launch and encodes from the registers,
+//     so the chunk is read once.  No cooperative launch is needed.
+//   * The standalone codec, and appends with K-smoothing or adaptive V scales,
+//     whose workspace cannot carry epochs or which need the channel means first:
+//     quantize_amax_kernel streams K and V once and writes one partial maximum per
+//     workgroup (no atomics); quantize_encode_kernel reduces the partials, then
+//     re-reads its tiles (the chunk, 28.8 MB for the 1.3B shape, is still in the
+//     256 MB Infinity Cache) and writes codes and scales.
 //
 // Exact encoding without an IEEE division per element.  The gfx950 converts
 // v_cvt_scalef32_pk_fp4_f32 / _fp8_f32 (scale 1.0) round to nearest-even and
 // saturate exactly like the recipe for every finite fp32 input (fp8 needs a clamp
 // at 448, above which it returns NaN), so the code is hw_fp4(RN(x / eff)).  The
-// quotient RN(x / b) is obtained from r = RN(1 / b) (one IEEE division per block)
-// by Markstein's method: q0 = RN(x r) is within 1.5 ulp of x / b; one correction
-// q1 = RN(q0 + (x - q0 b) r) makes it faithful; a second one, with the now exact
-// remainder, q2 = RN(q1 + (x - q1 b) r), is the correctly rounded quotient
-// (Markstein's theorem: y = RN(1/b) and a faithful q give RN(a/b) in one step).
-// Five fp32 operations and no branches per element; the block scale's two
-// divisions use the same scheme.  Quotients below 2^-126 fall out of the theorem's
-// range but are far below the first E2M1 threshold (0.25), so their code is exact
-// regardless; blocks whose eff leaves [2^-120, 2^110] divide each element with
-// IEEE division instead.
+// quotient RN(x / eff) is obtained from r = RN(1 / eff) (one IEEE division per
+// scale code and tensor, in an LDS table) by Markstein's method: q0 = RN(x r), then
+// corrections q' = RN(q - (q eff - x) r) with the remainder from one fused
+// multiply-add.  For a bf16 x one correction already gives RN(x / eff) whenever the
+// remainder is exact (div_rn_bf16: three fp32 operations per element); K minus its
+// channel means takes two (div_rn), as do the block scale's two divisions.  Tensors
+// whose s_t leaves [2^-80, 2^100] move x and eff by one power of two first, which
+// keeps every quotient that can give a nonzero code in that exact range.
 //
 // Work unit: an item is one octet of consecutive tokens x one 16-element block
 // (8 x 32 bytes of bf16), one item per thread; a workgroup tile is 256 / (D/16)
