@@ -344,7 +344,7 @@ def main():
     args = parse()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
-              "(this path is single-GPU; see DESIGN.md for how it would shard)", file=sys.stderr)
+              "(this path is single-GPU)", file=sys.stderr)
         sys.exit(2)
     if args.warmup < 4:
         log("note: warmup < 4 chunks, so the timed steps do not all see the full cache")

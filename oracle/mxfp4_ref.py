@@ -8,7 +8,7 @@ and a tensor-level scale on top; so MXFP4 has coarser blocks, a block scale that
 is not E4M3 and no tensor-level scale.  For the format itself the appendix cites
 the OCP Microscaling Formats (MX) specification, version 1.0.
 
-Readings (the cited specification's MXFP4, restated; also listed in the design doc)
+Readings (the cited specification's MXFP4, restated)
 -----------------------------------------------------------------------------
 * Block: 32 consecutive elements along the last (head_dim) axis.
 * Block scale: a power of two X = 2^E, stored as an E8M0 byte E + 127 (E in

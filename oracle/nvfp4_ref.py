@@ -16,7 +16,7 @@ What the pages fix
   frame chunk; the packed form costs 9/16 byte per element (4 bits of code plus
   one byte of scale per 16 elements), i.e. 9/8 T_c H d bytes for K and V.
 
-Readings taken where the pages are silent (each is also listed in the design doc)
+Readings taken where the pages are silent
 ---------------------------------------------------------------------------
 * Tensor scale  s_t = amax_t / (6 * 448) = amax_t / 2688, one fp32 division,
   where amax_t is the largest |x| of one chunk tensor (all heads).
