@@ -35,7 +35,7 @@ def draw_bits(rng, shape):
     return W.f32_to_bf16_bits(x.astype(np.float32))
 
 
-@pytest.mark.parametrize("seed", range(12))
+@pytest.mark.parametrize("seed", range(24))
 def test_random_config(ops, seed):
     from gpu_util import dev, host, check_attention
     rng = np.random.default_rng(1000 + seed)
@@ -79,5 +79,11 @@ def test_random_config(ops, seed):
         ck, cv = model.dequantized_kv()
         qc = mxfp8_dequantize_ref(*mxfp8_quantize_ref(q)) if fmt.get("mx_scaled_qk") else None
         want = chunk_attention_ref(q, ko, vo, ck, cv, scale, q_cache64=qc)
-        check_attention(out, want, f"seed {seed} step {step} n_q={n_q} cache={model.n_tokens()}")
+        # draws go up to ~3x unit scale (and heavy tails): the max-abs bar is taken in
+        # units of the RMS of V (cache and own), never below the plain bar
+        from oracle.nvfp4_ref import bf16_bits_to_f32
+        v_all = np.concatenate([cv.reshape(-1), bf16_bits_to_f32(vo).astype(np.float64).reshape(-1)])
+        v_rms = float(np.sqrt(np.mean(v_all ** 2)))
+        check_attention(out, want, f"seed {seed} step {step} n_q={n_q} cache={model.n_tokens()} v_rms={v_rms:.2f}",
+                        v_scale=v_rms)
     cache.close()
