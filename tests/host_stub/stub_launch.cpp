@@ -68,6 +68,8 @@ int stub_last_quant_options(void) {
   return (g_q.t[0].mean ? 1 : 0) | (g_q.n_tensors > 1 && g_q.t[1].adaptive ? 2 : 0);
 }
 int64_t stub_last_attn_k_mean(void) { return reinterpret_cast<int64_t>(g_a.k_mean); }
+// epoch of the last quantize launch: > 0 lets the launcher take the single-pass kernel
+int64_t stub_last_quant_epoch(void) { return int64_t(g_q.epoch); }
 void stub_fail_next(int rc) { g_fail_next = rc; }
 // segments of the last attention launch: out[3i..3i+2] = tok0, ntok, scale_slot
 int stub_last_segments(int32_t *out, int max) {

@@ -240,3 +240,27 @@ def test_append_k_smoothing_and_adaptive_v(ops, D, T_f, frames):
         print(f"chunk {c}: {np.count_nonzero(want_v[1] != plain_v[1])} of {want_v[1].size} V blocks take the 4-scale",
               flush=True)
         assert_codec_equal((host(vc), host(vs), host(sv)[0]), want_v, f"chunk {c} V")
+
+
+@pytest.mark.parametrize("D,T_f,frames", [(128, 1560, [3]), (64, 40, [2, 1]), (128, 8, [4, 2])])
+def test_append_adaptive_v_single_pass(ops, D, T_f, frames):
+    """Adaptive 4/6 V scales without K-smoothing take the single-pass append (the
+    maxima need no channel means): K and V codes, scale bytes and tensor scales equal
+    the oracle's bit for bit."""
+    from gpu_util import dev, host
+    rng = np.random.default_rng(3 * D + T_f)
+    H = 3
+    cache = ops.KVCache(H, D, T_f, 1, 6, v_adaptive=True)
+    chunks = []
+    for nf in frames:
+        k = t4_bits(rng, (H, nf * T_f, D), 1.5)
+        v = t4_bits(rng, (H, nf * T_f, D), 2.0)
+        cache.append(dev(k), dev(v), nf)
+        chunks.append((k, v))
+    for c, (k, v) in enumerate(chunks):
+        kc, ks, vc, vs, sk, sv = cache.export_chunk(c)
+        assert_codec_equal((host(kc), host(ks), host(sk)[0]), quantize_ref(k), f"chunk {c} K")
+        want_v = quantize_ref(v, adaptive=True)
+        print(f"chunk {c}: {np.count_nonzero(want_v[1] != quantize_ref(v)[1])} V blocks take the 4-scale", flush=True)
+        assert_codec_equal((host(vc), host(vs), host(sv)[0]), want_v, f"chunk {c} V")
+    cache.close()

@@ -287,10 +287,12 @@ def test_cache_errors_and_rollback(stub):
 
 def test_cache_options_route_to_their_kernels(stub):
     """Each cache option reaches the launches it changes: K-smoothing runs the mean
-    reduction and hands its means to the quantizer and to attention; adaptive V
-    scales mark V; MXFP4 appends go to the single-pass MXFP4 quantizer (never the
-    NVFP4 one), and its attention and export launches carry the format."""
+    reduction and hands its means to the quantizer (two passes) and to attention;
+    adaptive V scales mark V (single pass allowed); MXFP4 appends go to the
+    single-pass MXFP4 quantizer (never the NVFP4 one), and its attention and export
+    launches carry the format."""
     stub.stub_last_attn_k_mean.restype = ctypes.c_int64
+    stub.stub_last_quant_epoch.restype = ctypes.c_int64
     d = ctypes.c_void_p(0x1000)
     for opts in (0, 1, 2, 3, 4, 12):
         before = [stub.stub_calls(k) for k in range(5)]
@@ -304,6 +306,7 @@ def test_cache_options_route_to_their_kernels(stub):
             assert calls[0] == 1 and calls[4] == 0
             assert calls[3] == (1 if opts & 1 else 0)
             assert stub.stub_last_quant_options() == opts
+            assert (stub.stub_last_quant_epoch() > 0) == (not opts & 1)
         assert stub.chunk_attention(c.h, d, d, d, 8, 0.125, d, None) == OK
         assert stub.stub_last_attn_mx() == (2 if opts & 8 else 1 if opts & 4 else 0)
         assert (stub.stub_last_attn_k_mean() != 0) == bool(opts & 1)
