@@ -388,7 +388,7 @@ def main():
         log(f"quantize, K-smoothing + adaptive V: {qo['us_per_append']:.2f} us/append")
         qa, _ = quantize_leg(args, torch, ops, W, device, v_adaptive=True, sets=qsets)
         configs["quantize_v_adaptive"] = {k: qa[k] for k in ("us_per_append", "GB_per_s")}
-        log(f"quantize, adaptive V (single pass): {qa['us_per_append']:.2f} us/append")
+        log(f"quantize, adaptive V: {qa['us_per_append']:.2f} us/append")
         configs["wan13b_k_smooth_v_adaptive"] = attention_config("wan13b", args, torch, ops, W, device,
                                                                  k_smooth=True, v_adaptive=True)
         log(f"wan13b, K-smoothing + adaptive V: {configs['wan13b_k_smooth_v_adaptive']['us']:.1f} us")

@@ -380,7 +380,7 @@ int kvcache_append(kvcache *c, const uint16_t *k, const uint16_t *v, int32_t n_f
   a.ws = c->ws();
   a.epoch = ++c->epoch;   // never reused, even if the launch fails
   a.spin_limit = g_spin_limit.load(std::memory_order_relaxed);
-  if (c->k_smooth()) a.epoch = 0;   // K minus its channel means: the two-pass kernels
+  if (cfg.options) a.epoch = 0;   // smoothing / adaptive scales: the two-pass kernels
   if (c->k_smooth()) {
     const int rm = launch_channel_mean(k, cfg.n_heads, a.T, cfg.head_dim, c->kmean(sslot), c->kmean_ws(), stream);
     if (rm != NVFP4KV_OK) return rm;

@@ -664,14 +664,11 @@ __global__ __launch_bounds__(kQuantThreads) void quantize_fused_kernel(QuantArgs
     const TensorConsts &tc = oc.tensor ? tc1 : tc0;
     const float2 *tab = s_tab[oc.tensor];
     const bool tr = a.t[oc.tensor].transposed != 0;
-    const bool adapt = a.t[oc.tensor].adaptive != 0;
     if (tc.xs == 1.0f) {
-      if (tr && adapt) item_transposed<false, true>(a, oc, b, u, tc, tab, bm);
-      else if (tr) item_transposed<false>(a, oc, b, u, tc, tab, bm);
+      if (tr) item_transposed<false>(a, oc, b, u, tc, tab, bm);
       else item_canonical<false>(a, oc, b, u, tc, tab, bm);
     } else {
-      if (tr && adapt) item_transposed<true, true>(a, oc, b, u, tc, tab, bm);
-      else if (tr) item_transposed<true>(a, oc, b, u, tc, tab, bm);
+      if (tr) item_transposed<true>(a, oc, b, u, tc, tab, bm);
       else item_canonical<true>(a, oc, b, u, tc, tab, bm);
     }
   }

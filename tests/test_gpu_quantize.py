@@ -243,10 +243,10 @@ def test_append_k_smoothing_and_adaptive_v(ops, D, T_f, frames):
 
 
 @pytest.mark.parametrize("D,T_f,frames", [(128, 1560, [3]), (64, 40, [2, 1]), (128, 8, [4, 2])])
-def test_append_adaptive_v_single_pass(ops, D, T_f, frames):
-    """Adaptive 4/6 V scales without K-smoothing take the single-pass append (the
-    maxima need no channel means): K and V codes, scale bytes and tensor scales equal
-    the oracle's bit for bit."""
+def test_append_adaptive_v_only(ops, D, T_f, frames):
+    """Adaptive 4/6 V scales without K-smoothing: K codes by the plain recipe, V with
+    the per-block choice; codes, scale bytes and tensor scales equal the oracle's bit
+    for bit."""
     from gpu_util import dev, host
     rng = np.random.default_rng(3 * D + T_f)
     H = 3
@@ -264,3 +264,35 @@ def test_append_adaptive_v_single_pass(ops, D, T_f, frames):
         print(f"chunk {c}: {np.count_nonzero(want_v[1] != quantize_ref(v)[1])} V blocks take the 4-scale", flush=True)
         assert_codec_equal((host(vc), host(vs), host(sv)[0]), want_v, f"chunk {c} V")
     cache.close()
+
+
+def test_append_k_smoothing_extreme_scales(ops):
+    """K-smoothing and adaptive V appends of chunks at extreme scales (1e-20, 3e5,
+    with per-channel offsets in K), under either poll limit (these appends take the
+    two-pass quantizer, which has no wait): codes, scale bytes and tensor scales
+    equal the oracle's."""
+    from gpu_util import dev, host
+    from oracle import channel_mean_ref
+    H, D, T_f = 3, 128, 256
+    rng = np.random.default_rng(12)
+    chunks = []
+    for s in (1.0, 1e-20, 3e5):
+        kx = (rng.standard_normal((H, 2 * T_f, D)) + rng.standard_normal((H, 1, D)) * 8) * s
+        chunks.append((W.f32_to_bf16_bits(kx.astype(np.float32)), t4_bits(rng, (H, 2 * T_f, D), 1.0 / s)))
+    results = []
+    for limit in (0, 1 << 16):
+        ops.set_wait_limit(limit)
+        try:
+            cache = ops.KVCache(H, D, T_f, 2, 4, k_smooth=True, v_adaptive=True)
+            for k, v in chunks:
+                cache.append(dev(k), dev(v), 2)
+            results.append([tuple(host(t) for t in cache.export_chunk(c)) for c in range(3)])
+        finally:
+            ops.set_wait_limit(1 << 16)
+    for c, (k, v) in enumerate(chunks):
+        wk = quantize_ref(k, mean=channel_mean_ref(k))
+        wv = quantize_ref(v, adaptive=True)
+        for r in results:
+            kc, ks, vc, vs, sk, sv = r[c]
+            assert_codec_equal((kc, ks, sk[0]), wk, f"chunk {c} K")
+            assert_codec_equal((vc, vs, sv[0]), wv, f"chunk {c} V")

@@ -287,8 +287,9 @@ def test_cache_errors_and_rollback(stub):
 
 def test_cache_options_route_to_their_kernels(stub):
     """Each cache option reaches the launches it changes: K-smoothing runs the mean
-    reduction and hands its means to the quantizer (two passes) and to attention;
-    adaptive V scales mark V (single pass allowed); MXFP4 appends go to the
+    reduction and hands its means to the quantizer and to attention; adaptive V
+    scales mark V; appends with either option take the two-pass quantizer (epoch 0),
+    plain ones may take the single pass; MXFP4 appends go to the
     single-pass MXFP4 quantizer (never the NVFP4 one), and its attention and export
     launches carry the format."""
     stub.stub_last_attn_k_mean.restype = ctypes.c_int64
@@ -306,7 +307,7 @@ def test_cache_options_route_to_their_kernels(stub):
             assert calls[0] == 1 and calls[4] == 0
             assert calls[3] == (1 if opts & 1 else 0)
             assert stub.stub_last_quant_options() == opts
-            assert (stub.stub_last_quant_epoch() > 0) == (not opts & 1)
+            assert (stub.stub_last_quant_epoch() > 0) == (opts == 0)
         assert stub.chunk_attention(c.h, d, d, d, 8, 0.125, d, None) == OK
         assert stub.stub_last_attn_mx() == (2 if opts & 8 else 1 if opts & 4 else 0)
         assert (stub.stub_last_attn_k_mean() != 0) == bool(opts & 1)
