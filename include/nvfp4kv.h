@@ -62,8 +62,10 @@ const char *nvfp4kv_version(void);
  * maxima through the cache's workspace and each waits for the others for at most
  * `limit` polls before computing the tensor maxima itself by scanning the whole chunk.
  * chunk_attention: a query block cut between workgroups is finished by the one that
- * holds its first key tiles, which waits for the others' partial results for at most
- * `limit` polls per partial before processing the block's remaining tiles itself.
+ * holds its LAST key tiles: the workgroups holding its earlier tiles each publish the
+ * partial result of their part, and the last one waits for them for at most `limit`
+ * polls per partial, merges them in workgroup order, or, when one is still missing,
+ * processes the block's earlier tiles itself.
  * Default 65536; a small limit exercises the fallbacks.  Process-wide, read at each
  * call.  Errors: EINVAL (limit < 0). */
 int nvfp4kv_set_wait_limit(int32_t limit);

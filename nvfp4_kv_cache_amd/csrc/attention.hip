@@ -798,9 +798,10 @@ __global__ __launch_bounds__(Cfg<D>::kThreads, Cfg<D>::kWgPerCu) void chunk_atte
     u32x4 qr[D / 16];
 
     // Tiles [r0, r1) of block b.  Normally r0 = t0, r1 = t1, once.  The workgroup
-    // that holds a cut block's first tiles waits (bounded) for the partials of the
-    // other workgroups; if one is still missing it processes the block's remaining
-    // tiles itself (a second pass of this loop) instead of merging.
+    // that holds a cut block's last tiles waits (bounded) for the partials of the
+    // workgroups holding its earlier tiles; if one is still missing it processes the
+    // block's earlier tiles [0, r0) itself (a second pass of this loop) instead of
+    // merging.
     int r0 = t0, r1 = t1;
     while (true) {
       // ---- cache tiles (NVFP4)

@@ -59,9 +59,4 @@ int zero_device_bytes_blocking(void *ptr, size_t bytes) {
   return NVFP4KV_HIP_OK(hipMemset(ptr, 0, bytes));
 }
 
-int zero_device_bytes_async(void *ptr, size_t bytes, void *stream) {
-  if (bytes == 0) return NVFP4KV_OK;
-  return NVFP4KV_HIP_OK(hipMemsetAsync(ptr, 0, bytes, reinterpret_cast<hipStream_t>(stream)));
-}
-
 }  // namespace nvfp4kv

@@ -77,11 +77,14 @@ struct Segment {
 
 // Attention load balancing.  The key tiles of all (head, query block) pairs form one
 // list of work units that is cut into equal ranges, one per workgroup.  A query block
-// cut between workgroups g < g+1 < ... is finished by g, which holds its first tiles
-// and processes them last: every later workgroup holds a later part as its first
-// range, publishes the partial result in its slot and tags its flag with the
-// launch's epoch.  Scratch (in the cache's storage): one slot and one flag per
-// workgroup (flags start zeroed; epochs never repeat).
+// cut between workgroups gf < gf+1 < ... < g is finished by g, which holds its LAST
+// tiles and processes them last (each workgroup walks its share from the end): every
+// earlier workgroup holds an earlier part of the block as the first range it
+// processes, publishes that partial result in its slot and tags its flag with the
+// launch's epoch; g waits for those flags (bounded), merges the partials in
+// workgroup order, and on a timeout processes the block's earlier tiles itself.
+// Scratch (in the cache's storage): one slot and one flag per workgroup (flags
+// start zeroed; epochs never repeat).
 constexpr int kAttnMaxCus = 256;
 constexpr int attn_wg_per_cu(int D) { return D >= 128 ? 1 : 2; }
 constexpr int attn_max_grid(int D) { return kAttnMaxCus * attn_wg_per_cu(D); }
@@ -147,6 +150,5 @@ inline size_t channel_mean_ws_floats(int H, int T, int D) {
 int launch_channel_mean(const uint16_t *k, int H, int T, int D, float *mean, float *ws, void *stream);
 int copy_device_floats(float *dst, const float *src, size_t n, void *stream);
 int zero_device_bytes_blocking(void *ptr, size_t bytes);
-int zero_device_bytes_async(void *ptr, size_t bytes, void *stream);
 
 }  // namespace nvfp4kv

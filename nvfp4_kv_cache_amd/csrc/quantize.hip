@@ -960,7 +960,9 @@ int launch_quantize(const QuantArgs &in, void *stream) {
   const int64_t vecs = int64_t(a.H) * a.T * a.D / 8;
   int64_t g1 = (vecs + kAmaxThreads * 2 - 1) / (kAmaxThreads * 2);
   if (g1 > cus) g1 = cus;
-  if (g1 > kMaxQuantGrid) g1 = kMaxQuantGrid;
+  // the encode kernel reduces one partial per thread of its workgroup
+  static_assert(kQuantThreads <= kMaxQuantGrid, "partials array holds every amax workgroup");
+  if (g1 > kQuantThreads) g1 = kQuantThreads;
   if (g1 < 1) g1 = 1;
   hipLaunchKernelGGL(quantize_amax_kernel, dim3(unsigned(g1)), dim3(kAmaxThreads), 0, s, a);
   if (hipGetLastError() != hipSuccess) return NVFP4KV_EHIP;

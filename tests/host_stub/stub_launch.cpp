@@ -53,7 +53,6 @@ int launch_channel_mean(const uint16_t *, int, int, int, float *, float *, void 
 }
 int copy_device_floats(float *, const float *, size_t, void *) { return take_fail(); }
 int zero_device_bytes_blocking(void *, size_t) { return 0; }
-int zero_device_bytes_async(void *, size_t, void *) { return 0; }
 }  // namespace nvfp4kv
 
 using namespace nvfp4kv;

@@ -18,6 +18,13 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "nvfp4kv.h")
 LIB = os.path.join(ROOT, "nvfp4_kv_cache_amd", "libnvfp4kv.so")
 STUB = os.path.join(ROOT, "nvfp4_kv_cache_amd", "libnvfp4kv_hoststub.so")
+# NVFP4KV_STUB_SANITIZE=1: the stub build of the host code is instrumented with
+# AddressSanitizer and UndefinedBehaviorSanitizer (the process must preload the ASan
+# runtime; test_metadata_under_sanitizers below does this in a child process)
+SANITIZE = os.environ.get("NVFP4KV_STUB_SANITIZE") == "1"
+if SANITIZE:
+    STUB = STUB.replace(".so", "_asan.so")
+SAN_FLAGS = ["-fsanitize=address,undefined", "-fno-sanitize-recover=all", "-fno-omit-frame-pointer", "-g"]
 
 OK, EINVAL, ESHAPE, ECAPACITY, ESTATE, EHIP = 0, -1, -2, -3, -4, -5
 
@@ -139,7 +146,8 @@ def test_storage_bytes_budget(real):
 def stub():
     src = [os.path.join(ROOT, "nvfp4_kv_cache_amd", "csrc", "api.cpp"),
            os.path.join(ROOT, "tests", "host_stub", "stub_launch.cpp")]
-    subprocess.run(["g++", "-O1", "-std=c++17", "-fPIC", "-shared", "-o", STUB] + src, check=True)
+    flags = SAN_FLAGS if SANITIZE else []
+    subprocess.run(["g++", "-O1", "-std=c++17", "-fPIC", "-shared", *flags, "-o", STUB] + src, check=True)
     L = ctypes.CDLL(STUB)
     P = ctypes.c_void_p
     L.kvcache_storage_bytes.restype = ctypes.c_size_t
@@ -314,3 +322,23 @@ def test_cache_options_route_to_their_kernels(stub):
         assert stub.kvcache_export_chunk(c.h, 0, d, d, d, d, d, d, None) == OK
         assert stub.stub_last_export_block() == (32 if opts & 4 else 16)
         stub.kvcache_destroy(c.h)
+
+
+@pytest.mark.skipif(SANITIZE, reason="this test starts the sanitized run itself")
+def test_metadata_under_sanitizers():
+    """The host code (api.cpp: slot map, FIFO eviction, segment lists, argument checks)
+    built with AddressSanitizer and UndefinedBehaviorSanitizer runs every stub test of
+    this file in a child process; any report aborts it."""
+    asan = subprocess.run(["g++", "-print-file-name=libasan.so"], capture_output=True, text=True).stdout.strip()
+    if not os.path.isabs(asan) or not os.path.exists(asan):
+        pytest.skip("no ASan runtime for g++")
+    env = dict(os.environ, NVFP4KV_STUB_SANITIZE="1", LD_PRELOAD=asan,
+               ASAN_OPTIONS="detect_leaks=0:abort_on_error=1",
+               UBSAN_OPTIONS="halt_on_error=1:print_stacktrace=1")
+    r = subprocess.run(["python", "-m", "pytest", "-q", "-p", "no:cacheprovider", __file__,
+                        "-k", "metadata_matches or errors_and_rollback or options_route"],
+                       cwd=ROOT, env=env, capture_output=True, text=True, timeout=600)
+    tail = (r.stdout + r.stderr)[-3000:]
+    assert r.returncode == 0, tail
+    assert "ERROR: AddressSanitizer" not in tail and "runtime error" not in tail, tail
+    assert " passed" in r.stdout, tail
