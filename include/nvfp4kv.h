@@ -95,6 +95,26 @@ int nvfp4_quantize_kv(const uint16_t *x, int64_t H, int64_t T, int64_t D, uint8_
                       size_t workspace_bytes, void *stream);
 
 /* ------------------------------------------------------------------------------
+ * The same codec for callers that cannot allocate device memory or pass a workspace:
+ * code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc.  Arguments, results and errors are those of nvfp4_quantize_kv (minus
+ * the workspace); the result is bit-identical to it.
+ * Scratch: a file-scope device array of nvfp4_quantize_noalloc_scratch_bytes()
+ * (32 KiB) inside the library, one per GPU, held until the process ends; its address
+ * is resolved on the first call on each device.  The codec's scratch need does not
+ * grow with the input (one partial maximum per workgroup of its first pass, at most
+ * 256), so every input nvfp4_quantize_kv accepts fits; a need beyond the array would
+ * return NVFP4KV_ECAPACITY.  The call allocates nothing (no hipMalloc, no allocating
+ * library routine).  Every call on a GPU shares that GPU's array: calls that may
+ * overlap on one GPU (two streams, two threads) race and must be serialized by the
+ * caller.  Errors: as nvfp4_quantize_kv; EHIP also if the array's device address
+ * cannot be resolved.
+ * ------------------------------------------------------------------------------ */
+size_t nvfp4_quantize_noalloc_scratch_bytes(void);
+int nvfp4_quantize_kv_noalloc(const uint16_t *x, int64_t H, int64_t T, int64_t D, uint8_t *codes,
+                              uint8_t *scales, float *tensor_scale, void *stream);
+
+/* ------------------------------------------------------------------------------
  * Standalone MXFP4 codec of one tensor: the block-scaled FP4 format the paper text's
  * appendix A.2 ("FP4 Quantization") sets against NVFP4, as defined by the OCP
  * Microscaling Formats (MX) specification v1.0 it cites.

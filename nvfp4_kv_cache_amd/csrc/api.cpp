@@ -223,33 +223,51 @@ const char *nvfp4kv_version(void) { return "0.1.0"; }
 
 size_t nvfp4_quantize_workspace_bytes(void) { return sizeof(QuantWorkspace); }
 
-int nvfp4_quantize_kv(const uint16_t *x, int64_t H, int64_t T, int64_t D, uint8_t *codes,
-                      uint8_t *scales, float *tensor_scale, void *workspace,
-                      size_t workspace_bytes, void *stream) {
-  if (!x || !codes || !scales || !tensor_scale || !workspace) return NVFP4KV_EINVAL;
-  if (!aligned(x, 16) || !aligned(codes, 8) || !aligned(tensor_scale, 4) || !aligned(workspace, 4))
-    return NVFP4KV_EINVAL;
+namespace {
+// Argument checks and launch arguments of the standalone codec (workspace apart).
+int codec_args(const uint16_t *x, int64_t H, int64_t T, int64_t D, uint8_t *codes, uint8_t *scales,
+               float *tensor_scale, QuantArgs *a) {
+  if (!x || !codes || !scales || !tensor_scale) return NVFP4KV_EINVAL;
+  if (!aligned(x, 16) || !aligned(codes, 8) || !aligned(tensor_scale, 4)) return NVFP4KV_EINVAL;
   if (H < 1 || T < 1 || D < 16 || D % 16 != 0 || D > 4096) return NVFP4KV_EINVAL;
   if (H * T * D >= (int64_t(1) << 40) || T > (int64_t(1) << 30) || H > (1 << 20))
     return NVFP4KV_EINVAL;
-  if (workspace_bytes < sizeof(QuantWorkspace)) return NVFP4KV_ECAPACITY;
+  memset(a, 0, sizeof(*a));
+  a->t[0].src = x;
+  a->t[0].codes = codes;
+  a->t[0].scales = scales;
+  a->t[0].tensor_scale = tensor_scale;
+  a->t[0].transposed = 0;
+  a->n_tensors = 1;
+  a->H = int32_t(H);
+  a->T = int32_t(T);
+  a->D = int32_t(D);
+  a->tokens_per_frame = int32_t(T);
+  a->n_frames = 1;
+  a->rows = T;
+  a->frame_slot[0] = 0;
+  return NVFP4KV_OK;
+}
+}  // namespace
+
+int nvfp4_quantize_kv(const uint16_t *x, int64_t H, int64_t T, int64_t D, uint8_t *codes,
+                      uint8_t *scales, float *tensor_scale, void *workspace,
+                      size_t workspace_bytes, void *stream) {
+  if (!workspace || !aligned(workspace, 4)) return NVFP4KV_EINVAL;
   QuantArgs a;
-  memset(&a, 0, sizeof(a));
-  a.t[0].src = x;
-  a.t[0].codes = codes;
-  a.t[0].scales = scales;
-  a.t[0].tensor_scale = tensor_scale;
-  a.t[0].transposed = 0;
-  a.n_tensors = 1;
-  a.H = int32_t(H);
-  a.T = int32_t(T);
-  a.D = int32_t(D);
-  a.tokens_per_frame = int32_t(T);
-  a.n_frames = 1;
-  a.rows = T;
-  a.frame_slot[0] = 0;
+  if (int rc = codec_args(x, H, T, D, codes, scales, tensor_scale, &a)) return rc;
+  if (workspace_bytes < sizeof(QuantWorkspace)) return NVFP4KV_ECAPACITY;
   a.ws = reinterpret_cast<QuantWorkspace *>(workspace);
   return launch_quantize(a, stream);
+}
+
+size_t nvfp4_quantize_noalloc_scratch_bytes(void) { return kNoAllocScratchBytes; }
+
+int nvfp4_quantize_kv_noalloc(const uint16_t *x, int64_t H, int64_t T, int64_t D, uint8_t *codes,
+                              uint8_t *scales, float *tensor_scale, void *stream) {
+  QuantArgs a;
+  if (int rc = codec_args(x, H, T, D, codes, scales, tensor_scale, &a)) return rc;
+  return launch_quantize_noalloc(a, stream);
 }
 
 int mxfp4_quantize_kv(const uint16_t *x, int64_t H, int64_t T, int64_t D, uint8_t *codes,

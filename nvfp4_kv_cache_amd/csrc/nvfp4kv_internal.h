@@ -135,6 +135,10 @@ struct ExportArgs {
 
 // Launchers: return 0 or a negative nvfp4kv_status (EHIP).  `stream` is hipStream_t.
 int launch_quantize(const QuantArgs &a, void *stream);
+// The standalone codec with its workspace in the library's per-device scratch array
+// (a.ws is ignored): no allocation.  EHIP if the array's address cannot be resolved.
+constexpr size_t kNoAllocScratchBytes = sizeof(QuantWorkspace);
+int launch_quantize_noalloc(const QuantArgs &a, void *stream);
 // MXFP4 (32-element blocks, E8M0 scales, no tensor scale): one pass
 int launch_quantize_mx(const QuantArgs &a, void *stream);
 int launch_attention(const AttnArgs &a, void *stream);

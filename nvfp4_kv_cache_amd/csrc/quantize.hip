@@ -48,6 +48,8 @@
 // fp4 convert is fed.  Tokens are processed pair by pair in load order, so a wave
 // starts encoding as soon as its first loads arrive.
 
+#include <atomic>
+
 #include "device_common.h"
 
 namespace nvfp4kv {
@@ -563,7 +565,6 @@ __device__ __forceinline__ void tensor_max_scan(const QuantArgs &a, uint32_t &mk
 __global__ __launch_bounds__(kQuantThreads) void quantize_fused_kernel(QuantArgs a) {
   __shared__ uint32_t s_red[2][kQuantThreads / 64];
   __shared__ int s_ok[kQuantThreads / 64];
-  __shared__ float s_st[2];
   __shared__ float2 s_tab[2][kScaleCodes];
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int nb = a.D >> 4;
@@ -972,6 +973,42 @@ int launch_quantize(const QuantArgs &in, void *stream) {
   hipLaunchKernelGGL(quantize_encode_kernel, dim3(unsigned(g2)), dim3(kQuantThreads), 0, s, a,
                      int(g1));
   return NVFP4KV_HIP_OK(hipGetLastError());
+}
+
+// ---- the codec without a caller workspace
+// File-scope device array standing in for the workspace: one copy per GPU, at its
+// own address on each, resolved once per device with hipGetSymbolAddress (in host
+// code the array's name is only a host-side stand-in, never a device address).  The
+// two-pass codec writes every partial maximum it reads within the same call, so
+// nothing in it has to start zeroed; calls that overlap on one GPU share it and race.
+static __device__ __align__(256) uint8_t scratch[kNoAllocScratchBytes];
+
+namespace {
+std::atomic<void *> g_scratch_ptr[kMaxDevices];
+
+void *scratch_for_current_device() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  void *p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (!p) {
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return nullptr;
+    g_scratch_ptr[dev].store(p, std::memory_order_release);
+  }
+  return p;
+}
+}  // namespace
+
+int launch_quantize_noalloc(const QuantArgs &in, void *stream) {
+  // the codec's workspace need does not grow with the input (one partial maximum per
+  // workgroup of the first pass, at most kQuantThreads of them), so the fixed array
+  // always suffices; the check keeps that true if the launch shape ever changes
+  static_assert(sizeof(QuantWorkspace) <= kNoAllocScratchBytes, "codec workspace fits the scratch array");
+  if (in.epoch != 0) return NVFP4KV_EINVAL;   // the single-pass append needs zeroed epoch slots
+  void *p = scratch_for_current_device();
+  if (!p) return NVFP4KV_EHIP;
+  QuantArgs a = in;
+  a.ws = reinterpret_cast<QuantWorkspace *>(p);
+  return launch_quantize(a, stream);
 }
 
 }  // namespace nvfp4kv

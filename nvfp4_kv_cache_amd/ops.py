@@ -50,6 +50,8 @@ def lib():
             "nvfp4kv_set_wait_limit": (I, [ctypes.c_int32]),
             "nvfp4_quantize_workspace_bytes": (SZ, []),
             "nvfp4_quantize_kv": (I, [P, I64, I64, I64, P, P, P, P, SZ, P]),
+            "nvfp4_quantize_noalloc_scratch_bytes": (SZ, []),
+            "nvfp4_quantize_kv_noalloc": (I, [P, I64, I64, I64, P, P, P, P]),
             "mxfp4_quantize_kv": (I, [P, I64, I64, I64, P, P, P]),
             "kvcache_storage_bytes": (SZ, [ctypes.POINTER(KVCacheConfig)]),
             "kvcache_create": (I, [ctypes.POINTER(KVCacheConfig), P, SZ, ctypes.POINTER(P)]),
@@ -126,6 +128,30 @@ def quantize_kv(x, workspace=None):
                                  ctypes.c_void_p(scales.data_ptr()), ctypes.c_void_p(ts.data_ptr()),
                                  ctypes.c_void_p(workspace.data_ptr()), workspace.numel(), _stream())
     _check(rc, "nvfp4_quantize_kv")
+    return codes, scales, ts
+
+
+def quantize_kv_noalloc(x, out=None):
+    """The same codec through the entry point that allocates nothing (its scratch is
+    the library's per-device array).  ``out`` optionally gives preallocated (codes,
+    scales, tensor_scale) tensors of the shapes quantize_kv returns, so that the call
+    itself allocates nothing either; returns them."""
+    H, T, D = x.shape
+    dev = x.device
+    if out is None:
+        out = (torch.empty((H, T, D // 2), dtype=torch.uint8, device=dev),
+               torch.empty((H, T, D // 16), dtype=torch.uint8, device=dev),
+               torch.empty(1, dtype=torch.float32, device=dev))
+    codes, scales, ts = out
+    for t, shape, dt, name in ((codes, (H, T, D // 2), torch.uint8, "codes"),
+                               (scales, (H, T, D // 16), torch.uint8, "scales"),
+                               (ts, (1,), torch.float32, "tensor_scale")):
+        if tuple(t.shape) != shape or t.dtype != dt or not t.is_contiguous() or t.device != dev:
+            raise ValueError(f"{name}: expected a contiguous {dt} tensor of shape {shape} on {dev}")
+    rc = lib().nvfp4_quantize_kv_noalloc(_bf16_ptr(x, "x"), H, T, D, ctypes.c_void_p(codes.data_ptr()),
+                                         ctypes.c_void_p(scales.data_ptr()), ctypes.c_void_p(ts.data_ptr()),
+                                         _stream())
+    _check(rc, "nvfp4_quantize_kv_noalloc")
     return codes, scales, ts
 
 
