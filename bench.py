@@ -19,7 +19,9 @@ Prints progress on stderr and ONE JSON line on stdout:
                  workload, cache-cold inputs: algorithmic GB/s vs 8 TB/s HBM
   configs        the other workloads (tiny, 1.3B-shaped, 5B-shaped), and the append and
                  the 1.3B-shaped attention with K-smoothing + adaptive V scales
-  cpu_baseline   the CPU oracle on a bounded sample of the same attention
+  rollout_full_loop  the whole 40-chunk streaming rollout from an empty cache
+                 (ramp included): latent frames/s = 120 / loop time
+  cpu_baseline   the CPU oracle on a bounded sample of every workload
 """
 
 import argparse
@@ -65,8 +67,6 @@ def parse():
     p.add_argument("--warm-launches", type=int, default=30,
                    help="untimed attention launches enqueued right before the timed ones")
     p.add_argument("--no-cpu-baseline", action="store_true")
-    p.add_argument("--cpu-calls", type=int, default=2,
-                   help="full 1.3B-shaped attention calls the CPU oracle runs as its baseline sample")
     p.add_argument("--skip-configs", action="store_true", help="rollout + roofline legs only")
     p.add_argument("--only", choices=["attention", "quantize", "copy"],
                    help="run one kernel leg only (for profiler runs): the attention kernel on the "
@@ -204,6 +204,54 @@ def rollout(args, torch, ops, W, device):
     return res
 
 
+def rollout_full_loop(torch, ops, W, device):
+    """The whole streaming rollout as the workload defines it: 40 chunks from an
+    empty cache (the ramp through 0, 3, 6, 9 cached frames included), each 4
+    attention calls then the clean chunk's append.  One untimed pass on a fresh
+    cache brings the GPU to its working clock; a second pass on another fresh cache
+    is timed with HIP events: latent frames/s = 120 / loop time."""
+    wl = W.WORKLOADS["rollout"]
+    S = wl.steps_per_chunk
+    log(f"rollout (full loop): drawing {wl.n_chunks} chunks on device")
+    inputs = []
+    for c in range(wl.n_chunks):
+        noisy = [tuple(W.draw_device_normal(wl, c, s, t, device) for t in (W.Q_ID, W.K_ID, W.V_ID))
+                 for s in range(S)]
+        clean = tuple(W.draw_device_normal(wl, c, W.APPEND_STEP, t, device) for t in (W.K_ID, W.V_ID))
+        inputs.append((noisy, clean))
+    out = torch.empty((wl.n_heads, wl.n_q, wl.head_dim), dtype=torch.float32, device=device)
+
+    def loop(cache):
+        for noisy, (kc, vc) in inputs:
+            for q, k, v in noisy:
+                cache.attention(q, k, v, wl.softmax_scale, out=out)
+            cache.append(kc, vc, wl.chunk_frames)
+
+    caches = [ops.KVCache(wl.n_heads, wl.head_dim, wl.tokens_per_frame, wl.sink_frames, wl.window_frames,
+                          device=device) for _ in range(2)]
+    loop(caches[0])
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    loop(caches[1])
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1)
+    flops = sum(S * W.attention_flops(wl.n_heads, wl.n_q, wl.cache_frames_for_chunk(c) * wl.tokens_per_frame
+                                      + wl.n_q, wl.head_dim) for c in range(wl.n_chunks))
+    elems = wl.n_heads * wl.chunk_tokens * wl.head_dim
+    nbytes = wl.n_chunks * 2 * W.quantize_bytes(elems)
+    ideal_s = flops / (MFMA_BF16_PEAK_TFLOPS * 1e12) + nbytes / (HBM_PEAK_GBPS * 1e9)
+    frames = wl.n_chunks * wl.chunk_frames
+    for c in caches:
+        c.close()
+    return {"chunks": wl.n_chunks, "attention_calls": wl.n_chunks * S, "appends": wl.n_chunks,
+            "loop_ms": ms, "latent_frames_per_s": frames / (ms * 1e-3),
+            "ideal_latent_frames_per_s": frames / ideal_s, "frac_of_ideal": ideal_s / (ms * 1e-3),
+            "attention_flops": flops, "append_bytes": nbytes,
+            "note": "ideal = attention FLOPs at the dense bf16/fp16 MFMA peak + append bytes at the HBM peak"}
+
+
 def attention_roofline(args, torch, ops, W, cache, qkv, out):
     """The attention kernel alone on the steady-state rollout cache: mean launch
     time over `reps` back-to-back launches (HIP events on the launch stream)."""
@@ -296,29 +344,85 @@ def attention_config(name, args, torch, ops, W, device, k_smooth=False, v_adapti
             "frac_mfma_peak": tf / MFMA_BF16_PEAK_TFLOPS}
 
 
-def cpu_baseline(args, W):
-    """The oracle, untuned, on a bounded sample: `cpu_calls` full chunk-attention
-    calls of the 1.3B-shaped workload (same shape as the steady-state rollout
-    step: 12 heads x 4680 queries x 23400 keys), on consecutive query chunks over
-    the same cache; plus the oracle codec on one K tensor [12, 4680, 128]."""
+def _median_time(fn, reps):
     import numpy as np
+    t = []
+    for _ in range(reps):
+        t0 = time.perf_counter()
+        fn()
+        t.append(time.perf_counter() - t0)
+    return float(np.median(t))
+
+
+def cpu_baseline(args, W):
+    """The oracle, untuned, timed on the host on a bounded sample of every workload:
+    tiny and quantize-only x10 (median), one full chunk-attention call of the 1.3B- and
+    5B-shaped workloads, and one steady-state chunk of the streaming rollout (one of
+    its 4 attention calls and its append) extrapolated to the 40-chunk loop.  Inputs
+    are drawn and the oracle caches built before each timed call.  The headline value
+    is the 1.3B-shaped call (the steady-state rollout step's attention shape)."""
     from oracle import CacheModel, chunk_attention_ref, quantize_ref
-    wl = W.WORKLOADS["wan13b"]
-    model = CacheModel(wl.n_heads, wl.head_dim, wl.tokens_per_frame, wl.sink_frames, wl.window_frames)
-    for c in range(wl.n_cache_chunks):
-        model.append(*W.clean_chunk(wl, c))
-    ck, cv = model.dequantized_kv()
-    calls = [W.noisy_chunk(wl, wl.n_cache_chunks, step=s) for s in range(max(1, args.cpu_calls))]
-    t0 = time.perf_counter()
-    for q, ko, vo in calls:
+
+    def cache_of(wl, n_chunks, draw):
+        model = CacheModel(wl.n_heads, wl.head_dim, wl.tokens_per_frame, wl.sink_frames, wl.window_frames)
+        for c in range(n_chunks):
+            model.append(*draw(c))
+        return model.dequantized_kv()
+
+    per = {}
+    # tiny: quantize the 4-frame chunk (K and V) + attention, x10
+    wl = W.WORKLOADS["tiny"]
+    k, v = W.clean_chunk(wl, 0)
+    q, ko, vo = W.noisy_chunk(wl, 1)
+
+    def tiny():
+        model = CacheModel(wl.n_heads, wl.head_dim, wl.tokens_per_frame, wl.sink_frames, wl.window_frames)
+        model.append(k, v)
+        ck, cv = model.dequantized_kv()
         chunk_attention_ref(q, ko, vo, ck, cv, wl.softmax_scale)
-    dt = time.perf_counter() - t0
-    n_k = ck.shape[1] + wl.n_q
-    flops = len(calls) * W.attention_flops(wl.n_heads, wl.n_q, n_k, wl.head_dim)
-    k, _ = W.clean_chunk(W.WORKLOADS["quantize"], 0)
-    t1 = time.perf_counter()
-    quantize_ref(k)
-    dq = time.perf_counter() - t1
+    t = _median_time(tiny, 10)
+    f = W.attention_flops(wl.n_heads, wl.n_q, 256 + wl.n_q, wl.head_dim)
+    per["tiny"] = {"seconds_median": t, "reps": 10, "GFLOP_per_s": f / t / 1e9,
+                   "what": "quantize K and V of the cache chunk, dequantize, attention"}
+    # quantize-only: K and V [12, 4680, 128], x10
+    wl = W.WORKLOADS["quantize"]
+    k, v = W.clean_chunk(wl, 0)
+    t = _median_time(lambda: (quantize_ref(k), quantize_ref(v)), 10)
+    nbytes = 2 * W.quantize_bytes(k.size)
+    per["quantize"] = {"seconds_median": t, "reps": 10, "GB_per_s": nbytes / t / 1e9,
+                       "what": "oracle codec of K and V"}
+    # 1.3B- and 5B-shaped: one full call each
+    for name in ("wan13b", "wan5b"):
+        wl = W.WORKLOADS[name]
+        ck, cv = cache_of(wl, wl.n_cache_chunks, lambda c, wl=wl: W.clean_chunk(wl, c))
+        q, ko, vo = W.noisy_chunk(wl, wl.n_cache_chunks)
+        t0 = time.perf_counter()
+        chunk_attention_ref(q, ko, vo, ck, cv, wl.softmax_scale)
+        t = time.perf_counter() - t0
+        f = W.attention_flops(wl.n_heads, wl.n_q, ck.shape[1] + wl.n_q, wl.head_dim)
+        per[name] = {"seconds": t, "reps": 1, "TFLOP_per_s": f / t / 1e12, "flops": f}
+    # streaming rollout: one steady-state chunk (cache of chunks 0..3 = 3 sink + 9 window
+    # frames), one attention call and the append timed, extrapolated to the 40 chunks
+    wl = W.WORKLOADS["rollout"]
+    rng_draw = lambda c: tuple(W.draw_bf16(wl, c, W.APPEND_STEP, t) for t in (W.K_ID, W.V_ID))
+    ck, cv = cache_of(wl, 4, rng_draw)
+    q, ko, vo = W.noisy_chunk(wl, 4, step=0)
+    t0 = time.perf_counter()
+    chunk_attention_ref(q, ko, vo, ck, cv, wl.softmax_scale)
+    t_attn = time.perf_counter() - t0
+    k, v = rng_draw(4)
+    t0 = time.perf_counter()
+    quantize_ref(k), quantize_ref(v)
+    t_app = time.perf_counter() - t0
+    n_full = ck.shape[1] + wl.n_q
+    # attention time scales with the key count of each chunk (0, 3, 6, 9, 12, 12, ... frames)
+    t_loop = sum(wl.steps_per_chunk * t_attn * (wl.cache_frames_for_chunk(c) * wl.tokens_per_frame + wl.n_q)
+                 / n_full + t_app for c in range(wl.n_chunks))
+    per["rollout"] = {"seconds_attention_call": t_attn, "seconds_append": t_app,
+                      "extrapolated_loop_seconds": t_loop,
+                      "latent_frames_per_s": wl.n_chunks * wl.chunk_frames / t_loop,
+                      "what": f"1 steady-state attention call + 1 append timed, extrapolated to "
+                              f"{wl.n_chunks} chunks x ({wl.steps_per_chunk} calls scaled by key count + 1 append)"}
     try:
         from threadpoolctl import threadpool_info
         cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [os.cpu_count()])
@@ -332,12 +436,13 @@ def cpu_baseline(args, W):
                 break
     except OSError:
         pass
-    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
-            "sample": f"{len(calls)} float64 chunk-attention calls of the 1.3B-shaped workload (12 heads x "
-                      f"{wl.n_q} queries x {n_k} keys x D128), {dt:.1f} s; numpy BLAS threads={cores}; "
+    h = per["wan13b"]
+    return {"value": h["TFLOP_per_s"], "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+            "sample": f"float64 oracle: one 1.3B-shaped chunk-attention call (12 heads x 4680 queries x 23400 "
+                      f"keys x D128) for the value; per_config: tiny and quantize-only x10 (median), one "
+                      f"5B-shaped call, one steady-state rollout chunk extrapolated; numpy BLAS threads={cores}; "
                       f"{cpu_model}",
-            "seconds": dt, "host_cpus": os.cpu_count(),
-            "quantize_GB_per_s": W.quantize_bytes(k.size) / dq / 1e9, "quantize_seconds": dq}
+            "seconds": h["seconds"], "host_cpus": os.cpu_count(), "per_config": per}
 
 
 def main():
@@ -375,6 +480,11 @@ def main():
     log(f"rollout: {r['ms_per_step']:.3f} ms/step, {r['tflops']:.1f} TFLOP/s, "
         f"{r['frames_per_s']:.1f} frames/s; attention kernel {r['attn_ms']*1e3:.1f} us "
         f"= {r['attn_tflops']:.1f} TFLOP/s")
+    full = None
+    if not args.skip_configs:
+        full = rollout_full_loop(torch, ops, W, device)
+        log(f"rollout, full 40-chunk loop: {full['loop_ms']:.1f} ms = {full['latent_frames_per_s']:.1f} frames/s "
+            f"({100 * full['frac_of_ideal']:.1f}% of the {full['ideal_latent_frames_per_s']:.0f} frames/s ideal)")
     qz, qsets = quantize_leg(args, torch, ops, W, device)
     log(f"quantize: {qz['us_per_append']:.2f} us/append = {qz['GB_per_s']:.1f} GB/s")
     configs = {}
@@ -419,7 +529,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": "fp16/bf16 MFMA, fp32 accumulate",
         "data": "synthetic",
         "config": {
             "workload": "streaming rollout, steady state: 12 heads, head_dim 128, 1560 tokens/frame, "
@@ -431,6 +541,7 @@ def main():
             "cache_tokens": r["cache_tokens"], "steady_state": r["steady_state"],
         },
         "latent_frames_per_s": r["frames_per_s"],
+        "rollout_full_loop": full,
         "wall_ms_per_step": r["wall_ms_per_step"],
         "roofline": {"bound": "mfma", "kernel": "chunk_attention_kernel<128, false, false> (NVFP4 cache)",
                      "achieved": r["attn_tflops"], "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",

@@ -59,8 +59,10 @@ const char *nvfp4kv_version(void);
 
 /* Testing hook for the two bounded waits between workgroups; either way the results
  * are the same.  kvcache_append's single-pass quantizer: workgroups exchange their
- * maxima through the cache's workspace and each waits for the others for at most
- * `limit` polls before computing the tensor maxima itself by scanning the whole chunk.
+ * maxima through the cache's workspace; a workgroup that has polled `limit` times
+ * without finding every other workgroup's maxima helps instead, computing one missing
+ * workgroup's tile maxima per further poll and publishing them in its place (bounded
+ * extra work: about one more read of the chunk in all).
  * chunk_attention: a query block cut between workgroups is finished by the one that
  * holds its LAST key tiles: the workgroups holding its earlier tiles each publish the
  * partial result of their part, and the last one waits for them for at most `limit`
@@ -223,6 +225,13 @@ int kvcache_destroy(kvcache *c);
  * this chunk would enter the window), EHIP. */
 int kvcache_append(kvcache *c, const uint16_t *k, const uint16_t *v, int32_t n_frames,
                    void *stream);
+
+/* The kernel schedule an append of n_frames frames takes on the current device (host
+ * output): 1 = the single-pass quantizer (one kernel, each chunk element read once),
+ * 2 = the two-pass quantizer (caches with K-smoothing or adaptive V scales, or a grid
+ * that would not fit on the GPU at once), 3 = the MXFP4 quantizer (one kernel, no
+ * exchange between workgroups).  Errors: EINVAL, EHIP. */
+int kvcache_append_schedule(const kvcache *c, int32_t n_frames, int32_t *schedule);
 
 /* Drops the oldest n_frames window frames (never sinks); metadata only.
  * Errors: EINVAL (n_frames < 0), ESTATE (fewer than n_frames window frames). */

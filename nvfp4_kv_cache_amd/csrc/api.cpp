@@ -409,6 +409,29 @@ int kvcache_append(kvcache *c, const uint16_t *k, const uint16_t *v, int32_t n_f
   return NVFP4KV_OK;
 }
 
+int kvcache_append_schedule(const kvcache *c, int32_t n_frames, int32_t *schedule) {
+  if (!c || !schedule || n_frames < 1 || n_frames > kMaxFrames) return NVFP4KV_EINVAL;
+  const kvcache_config &cfg = c->cfg;
+  if (int64_t(n_frames) * cfg.tokens_per_frame > (int64_t(1) << 30)) return NVFP4KV_EINVAL;
+  if (c->mx()) {
+    *schedule = 3;
+    return NVFP4KV_OK;
+  }
+  QuantArgs a;
+  memset(&a, 0, sizeof(a));
+  a.n_tensors = 2;
+  a.H = cfg.n_heads;
+  a.T = n_frames * cfg.tokens_per_frame;
+  a.D = cfg.head_dim;
+  a.tokens_per_frame = cfg.tokens_per_frame;
+  a.n_frames = n_frames;
+  a.epoch = cfg.options ? 0 : 1;   // as kvcache_append: options take the two passes
+  const int rc = quantize_single_pass(a);
+  if (rc < 0) return rc;
+  *schedule = rc ? 1 : 2;
+  return NVFP4KV_OK;
+}
+
 int kvcache_evict(kvcache *c, int32_t n_frames) {
   if (!c || n_frames < 0) return NVFP4KV_EINVAL;
   if (n_frames > c->st.win_count) return NVFP4KV_ESTATE;

@@ -135,6 +135,9 @@ struct ExportArgs {
 
 // Launchers: return 0 or a negative nvfp4kv_status (EHIP).  `stream` is hipStream_t.
 int launch_quantize(const QuantArgs &a, void *stream);
+// 1 if launch_quantize would take the single-pass kernel for these arguments on the
+// current device, 0 for the two passes, or a negative status.
+int quantize_single_pass(const QuantArgs &a);
 // The standalone codec with its workspace in the library's per-device scratch array
 // (a.ws is ignored): no allocation.  EHIP if the array's address cannot be resolved.
 constexpr size_t kNoAllocScratchBytes = sizeof(QuantWorkspace);

@@ -545,26 +545,39 @@ __global__ __launch_bounds__(kQuantThreads) void quantize_encode_kernel(QuantArg
 // Single pass (cache appends): every workgroup loads its tile into registers,
 // publishes its maxima of |x| in its workspace slot tagged with the launch's epoch,
 // waits until every workgroup's slot carries that epoch, and encodes from the
-// registers, so the chunk is read once.  All workgroups of the grid must be
-// resident at the same time (the launcher checks the grid against the occupancy).
-// The wait is bounded (a.spin_limit polls): a workgroup that gives up scans the whole
-// tensors for their maxima itself, which gives the same result, so no workgroup can
-// wait forever.
+// registers, so the chunk is read once.  The launcher only takes this path when the
+// grid fits on the GPU at once (occupancy), but co-residency is not guaranteed (other
+// streams' kernels may hold CUs), so the wait is bounded (a.spin_limit polls): past
+// it, a waiting workgroup helps instead of waiting.  Each polling round it takes one
+// tile whose slot is still missing (the k-th missing one, k from its own number, so
+// that helpers spread over the missing tiles), computes that tile's maxima exactly
+// as its owner would, and publishes them in the owner's slot (the owner, when it
+// runs, writes the same word).  A helper thus reads one tile per round; all helpers
+// together read each missing tile about once (at most one extra read of the chunk),
+// and every slot is filled even if its owner never becomes resident first.
 
-__device__ __forceinline__ void tensor_max_scan(const QuantArgs &a, uint32_t &mk, uint32_t &mv) {
-  const int64_t n16 = int64_t(a.H) * a.T * a.D / 8;
-  const uint4 *pk = reinterpret_cast<const uint4 *>(a.t[0].src);
-  const uint4 *pv = reinterpret_cast<const uint4 *>(a.n_tensors > 1 ? a.t[1].src : a.t[0].src);
-  for (int64_t i = threadIdx.x; i < n16; i += kQuantThreads) {
-    const uint32_t q = vmax4(pk[i]), w = vmax4(pv[i]);
-    mk = max(mk, max(q & 0xFFFFu, q >> 16));
-    mv = max(mv, max(w & 0xFFFFu, w >> 16));
+// Packed maxima word of one tile: |bf16| bits of K in bits 15-29, of V in bits 0-14
+// (a tile belongs to one tensor; the other field is 0).
+__device__ __forceinline__ void tile_maxima(const QuantArgs &a, int tile, uint32_t &mk, uint32_t &mv) {
+  const int nb = a.D >> 4;
+  const int opt = kQuantThreads / nb;
+  const int b = threadIdx.x % nb, o = threadIdx.x / nb;
+  const Octet oc = locate_octet(a, tile, min(o, opt - 1));
+  const uint4 *src = reinterpret_cast<const uint4 *>(a.t[oc.tensor].src + int64_t(oc.h) * a.T * a.D + 16 * b);
+  uint32_t mx = 0;
+  for (int j = 0; j < kOctet; ++j) {
+    const int64_t tok = min(oc.tok + j, a.T - 1);
+    const uint4 u[2] = {src[tok * (a.D / 8)], src[tok * (a.D / 8) + 1]};
+    mx = max(mx, block_max_bits(u));
   }
+  mk = oc.tensor == 0 ? mx : 0u;
+  mv = oc.tensor == 1 ? mx : 0u;
 }
 
 __global__ __launch_bounds__(kQuantThreads) void quantize_fused_kernel(QuantArgs a) {
   __shared__ uint32_t s_red[2][kQuantThreads / 64];
   __shared__ int s_ok[kQuantThreads / 64];
+  __shared__ int s_help;
   __shared__ float2 s_tab[2][kScaleCodes];
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int nb = a.D >> 4;
@@ -601,53 +614,79 @@ __global__ __launch_bounds__(kQuantThreads) void quantize_fused_kernel(QuantArgs
   }
   __syncthreads();
 
-  // wait for the slots of every workgroup of this launch
+  // wait for the slots of every workgroup of this launch (bounded; then help)
+  constexpr int kSlotsPerThread = kMaxQuantGrid / kQuantThreads;
   uint32_t gk = 0, gv = 0;
   for (int spin = 0;; ++spin) {
-    bool ok = true;
-    uint32_t k = 0, v = 0;
-    for (int j = tid; j < int(gridDim.x); j += kQuantThreads) {
-      const uint64_t w = __hip_atomic_load(&a.ws->slot[j], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      ok = ok && (w >> 30) == a.epoch;
-      k = max(k, uint32_t(w >> 15) & 0x7FFFu);
-      v = max(v, uint32_t(w) & 0x7FFFu);
+    uint32_t k = 0, v = 0, miss = 0;
+#pragma unroll
+    for (int i = 0; i < kSlotsPerThread; ++i) {
+      const int j = tid + i * kQuantThreads;
+      if (j < int(gridDim.x)) {
+        const uint64_t w = __hip_atomic_load(&a.ws->slot[j], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if ((w >> 30) != a.epoch) miss |= 1u << i;
+        k = max(k, uint32_t(w >> 15) & 0x7FFFu);
+        v = max(v, uint32_t(w) & 0x7FFFu);
+      }
     }
-    const int wave_ok = __all(ok);
+    // missing slots: per-thread counts, scanned over the workgroup
+    const int cnt = __builtin_popcount(miss);
+    int incl = cnt;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int y = __shfl_up(incl, off, 64);
+      if (lane >= off) incl += y;
+    }
     k = wave_max_u32(k);
     v = wave_max_u32(v);
+    if (lane == 63) s_ok[wv] = incl;
     if (lane == 0) {
-      s_ok[wv] = wave_ok;
       s_red[0][wv] = k;
       s_red[1][wv] = v;
     }
     __syncthreads();
-    bool all_ok = true;
+    int n_miss = 0, before = 0;
     gk = gv = 0;
     for (int i = 0; i < kQuantThreads / 64; ++i) {
-      all_ok = all_ok && s_ok[i];
+      n_miss += s_ok[i];
+      before += i < wv ? s_ok[i] : 0;
       gk = max(gk, s_red[0][i]);
       gv = max(gv, s_red[1][i]);
     }
-    __syncthreads();
-    if (all_ok) break;
-    if (spin >= a.spin_limit) {   // give up waiting: scan the tensors
-      uint32_t fk = 0, fv = 0;
-      tensor_max_scan(a, fk, fv);
-      fk = wave_max_u32(fk);
-      fv = wave_max_u32(fv);
-      if (lane == 0) {
-        s_red[0][wv] = fk;
-        s_red[1][wv] = fv;
+    if (n_miss == 0) break;
+    if (spin >= a.spin_limit) {
+      // help: the k-th missing slot of this round, k from this workgroup's number
+      const int kth = int((blockIdx.x + uint32_t(spin - a.spin_limit)) % uint32_t(n_miss));
+      const int excl = before + incl - cnt;
+      if (kth >= excl && kth < excl + cnt) {
+        uint32_t m = miss;
+        for (int r = kth - excl; r > 0; --r) m &= m - 1;   // drop the lower set bits
+        s_help = tid + (__builtin_ctz(m)) * kQuantThreads;
       }
       __syncthreads();
-      gk = gv = 0;
-      for (int i = 0; i < kQuantThreads / 64; ++i) {
-        gk = max(gk, s_red[0][i]);
-        gv = max(gv, s_red[1][i]);
+      const int tile = s_help;
+      uint32_t hk, hv;
+      tile_maxima(a, tile, hk, hv);
+      hk = wave_max_u32(hk);
+      hv = wave_max_u32(hv);
+      if (lane == 0) {
+        s_red[0][wv] = hk;
+        s_red[1][wv] = hv;
       }
-      break;
+      __syncthreads();
+      if (tid == 0) {
+        uint32_t rk = 0, rv = 0;
+        for (int i = 0; i < kQuantThreads / 64; ++i) {
+          rk = max(rk, s_red[0][i]);
+          rv = max(rv, s_red[1][i]);
+        }
+        const uint64_t word = (a.epoch << 30) | (uint64_t(rk) << 15) | uint64_t(rv);
+        __hip_atomic_store(&a.ws->slot[tile], word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+    } else {
+      __builtin_amdgcn_s_sleep(2);
     }
-    __builtin_amdgcn_s_sleep(2);
+    __syncthreads();
   }
 
   const float st0 = bf16_bits_to_float(gk) / 2688.0f, st1 = bf16_bits_to_float(gv) / 2688.0f;
@@ -930,8 +969,9 @@ int launch_quantize_mx(const QuantArgs &in, void *stream) {
   return NVFP4KV_HIP_OK(hipGetLastError());
 }
 
-int launch_quantize(const QuantArgs &in, void *stream) {
-  QuantArgs a = in;
+namespace {
+// Tile shape of the quantize kernels (sets a.tile_tokens, tiles_per_head, total_tiles).
+int quantize_tiles(QuantArgs &a) {
   const int nb = a.D / 16;
   if (nb < 1 || nb > kQuantThreads || a.tokens_per_frame < 1 || a.n_frames < 1) return NVFP4KV_EINVAL;
   a.tile_tokens = kOctet * (kQuantThreads / nb);
@@ -939,23 +979,44 @@ int launch_quantize(const QuantArgs &in, void *stream) {
   const int64_t total = int64_t(a.n_tensors) * a.H * a.tiles_per_head;
   if (total >= (int64_t(1) << 31)) return NVFP4KV_EINVAL;
   a.total_tiles = int32_t(total);
+  return NVFP4KV_OK;
+}
+
+// 1 when the single-pass kernel takes this launch: an epoch is given and the grid (one
+// workgroup per tile) fits on the current device at once by the occupancy API.
+int fused_fits(const QuantArgs &a, int dev) {
+  if (a.epoch == 0 || a.total_tiles > kMaxQuantGrid || dev < 0 || dev >= kMaxDevices) return 0;
+  if (g_fused_per_cu[dev] == 0) {
+    int per = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, quantize_fused_kernel, kQuantThreads, 0) != hipSuccess)
+      return NVFP4KV_EHIP;
+    g_fused_per_cu[dev] = per > 0 ? per : -1;
+  }
+  return g_fused_per_cu[dev] > 0 && a.total_tiles <= int64_t(cu_count(dev)) * g_fused_per_cu[dev] ? 1 : 0;
+}
+}  // namespace
+
+int quantize_single_pass(const QuantArgs &in) {
+  QuantArgs a = in;
+  if (int rc = quantize_tiles(a)) return rc;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return NVFP4KV_EHIP;
+  return fused_fits(a, dev);
+}
+
+int launch_quantize(const QuantArgs &in, void *stream) {
+  QuantArgs a = in;
+  if (int rc = quantize_tiles(a)) return rc;
+  const int64_t total = a.total_tiles;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return NVFP4KV_EHIP;
   const int cus = cu_count(dev);
-  if (a.epoch > 0 && a.total_tiles <= kMaxQuantGrid && dev >= 0 && dev < kMaxDevices) {
-    if (g_fused_per_cu[dev] == 0) {
-      int per = 0;
-      if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, quantize_fused_kernel, kQuantThreads, 0) !=
-          hipSuccess)
-        return NVFP4KV_EHIP;
-      g_fused_per_cu[dev] = per > 0 ? per : -1;
-    }
-    if (g_fused_per_cu[dev] > 0 && a.total_tiles <= int64_t(cus) * g_fused_per_cu[dev]) {
-      hipLaunchKernelGGL(quantize_fused_kernel, dim3(unsigned(a.total_tiles)), dim3(kQuantThreads), 0, s,
-                         a);
-      return NVFP4KV_HIP_OK(hipGetLastError());
-    }
+  const int fits = fused_fits(a, dev);
+  if (fits < 0) return fits;
+  if (fits) {
+    hipLaunchKernelGGL(quantize_fused_kernel, dim3(unsigned(a.total_tiles)), dim3(kQuantThreads), 0, s, a);
+    return NVFP4KV_HIP_OK(hipGetLastError());
   }
   // pass 1: one 1024-thread workgroup per CU (fewer for small inputs)
   const int64_t vecs = int64_t(a.H) * a.T * a.D / 8;

@@ -58,6 +58,7 @@ def lib():
             "kvcache_destroy": (I, [P]),
             "kvcache_append": (I, [P, P, P, ctypes.c_int32, P]),
             "kvcache_evict": (I, [P, ctypes.c_int32]),
+            "kvcache_append_schedule": (I, [P, ctypes.c_int32, ctypes.POINTER(ctypes.c_int32)]),
             "kvcache_tokens": (I, [P, ctypes.POINTER(I64), ctypes.POINTER(I64)]),
             "kvcache_begin_shot": (I, [P]),
             "kvcache_export_k_mean": (I, [P, ctypes.c_int32, P, P]),
@@ -213,6 +214,12 @@ class KVCache:
         rc = lib().kvcache_append(self._h, _bf16_ptr(k, "k", shape), _bf16_ptr(v, "v", shape),
                                   n_frames, _stream())
         _check(rc, "kvcache_append")
+
+    def append_schedule(self, n_frames):
+        """1: single-pass quantizer, 2: two passes, 3: MXFP4 quantizer (see the header)."""
+        r = ctypes.c_int32()
+        _check(lib().kvcache_append_schedule(self._h, n_frames, ctypes.byref(r)), "kvcache_append_schedule")
+        return r.value
 
     def evict(self, n_frames):
         _check(lib().kvcache_evict(self._h, n_frames), "kvcache_evict")

@@ -131,6 +131,8 @@ def test_append_quantize_workload_steady_state(ops):
     for c, (k, v) in enumerate(chunks):
         cache.append(dev(k), dev(v), wl.chunk_frames)
     assert cache.tokens() == (3 * 1560, 9 * 1560)
+    # the headline append path: one single-pass kernel (456 workgroups resident at once)
+    assert cache.append_schedule(wl.chunk_frames) == 1
     for c in (0, 4):
         kc, ks, vc, vs, sk, sv = cache.export_chunk(c)
         k, v = chunks[c]
@@ -178,30 +180,40 @@ def test_append_extreme_and_special_chunks(ops, D):
         assert_codec_equal((host(vc), host(vs), host(sv)[0]), quantize_ref(v), f"D{D} chunk {c} V")
 
 
-def test_append_wait_fallback_scan(ops):
-    """With a zero poll limit, workgroups of the single-pass append quantizer that do
-    not find every maximum published on their first look compute the tensor maxima by
-    scanning the chunk themselves; codes, scale bytes and tensor scales must not change."""
+def test_append_wait_fallback_help(ops):
+    """With a zero poll limit, every workgroup of the single-pass append quantizer that
+    does not find all maxima published on its first look helps: it computes missing
+    workgroups' tile maxima and publishes them in their place; with limits 1 and 2 it
+    first waits a little.  Codes, scale bytes and tensor scales must not change, for a
+    small grid and for the quantize workload's 456 workgroups."""
     from gpu_util import dev, host
-    H, D, T_f = 4, 128, 256         # 16 workgroups per append
     rng = np.random.default_rng(11)
-    chunks = [(t4_bits(rng, (H, 2 * T_f, D), s), t4_bits(rng, (H, 2 * T_f, D), 1.0 / s))
-              for s in (1.0, 1e-20, 3e5)]
-    results = []
-    for limit in (0, 1 << 16):
-        ops.set_wait_limit(limit)
-        try:
-            cache = ops.KVCache(H, D, T_f, 2, 4)
-            for k, v in chunks:
-                cache.append(dev(k), dev(v), 2)
-            results.append([tuple(host(t) for t in cache.export_chunk(c)) for c in range(3)])
-        finally:
-            ops.set_wait_limit(1 << 16)
-    for c, (k, v) in enumerate(chunks):
-        for r in results:
-            kc, ks, vc, vs, sk, sv = r[c]
-            assert_codec_equal((kc, ks, sk[0]), quantize_ref(k), f"chunk {c} K")
-            assert_codec_equal((vc, vs, sv[0]), quantize_ref(v), f"chunk {c} V")
+    cases = []
+    H, D, T_f = 4, 128, 256         # 16 workgroups per append
+    cases.append((H, D, T_f, 2, [(t4_bits(rng, (H, 2 * T_f, D), s), t4_bits(rng, (H, 2 * T_f, D), 1.0 / s))
+                                 for s in (1.0, 1e-20, 3e5)]))
+    wl = W.WORKLOADS["quantize"]
+    cases.append((wl.n_heads, wl.head_dim, wl.tokens_per_frame, wl.chunk_frames,
+                  [W.clean_chunk(wl, c) for c in range(2)]))
+    for H, D, T_f, nf, chunks in cases:
+        results = []
+        for limit in (0, 1, 2, 1 << 16):
+            print(f"[append help] H={H} T_f={T_f} wait limit {limit}", flush=True)
+            ops.set_wait_limit(limit)
+            try:
+                cache = ops.KVCache(H, D, T_f, 2, 4 * nf)
+                assert cache.append_schedule(nf) == 1
+                for k, v in chunks:
+                    cache.append(dev(k), dev(v), nf)
+                results.append([tuple(host(t) for t in cache.export_chunk(c)) for c in range(len(chunks))])
+            finally:
+                ops.set_wait_limit(1 << 16)
+        for c, (k, v) in enumerate(chunks):
+            wk, wv = quantize_ref(k), quantize_ref(v)
+            for r in results:
+                kc, ks, vc, vs, sk, sv = r[c]
+                assert_codec_equal((kc, ks, sk[0]), wk, f"chunk {c} K")
+                assert_codec_equal((vc, vs, sv[0]), wv, f"chunk {c} V")
     with pytest.raises(ops.NVFP4KVError):
         ops.set_wait_limit(-1)
 

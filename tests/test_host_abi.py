@@ -162,6 +162,7 @@ def stub():
     L.kvcache_shot_sink.argtypes = [P, ctypes.POINTER(ctypes.c_int64), ctypes.POINTER(ctypes.c_int32),
                                     ctypes.POINTER(ctypes.c_int64)]
     L.kvcache_export_chunk.argtypes = [P, ctypes.c_int32] + [P] * 7
+    L.kvcache_append_schedule.argtypes = [P, ctypes.c_int32, ctypes.POINTER(ctypes.c_int32)]
     L.stub_last_segments.argtypes = [ctypes.POINTER(ctypes.c_int32), ctypes.c_int]
     L.stub_last_quant_slots.argtypes = [ctypes.POINTER(ctypes.c_int32), ctypes.c_int,
                                         ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_int64)]
@@ -299,7 +300,7 @@ def test_cache_options_route_to_their_kernels(stub):
     scales mark V; appends with either option take the two-pass quantizer (epoch 0),
     plain ones may take the single pass; MXFP4 appends go to the
     single-pass MXFP4 quantizer (never the NVFP4 one), and its attention and export
-    launches carry the format."""
+    launches carry the format; kvcache_append_schedule reports the same routing."""
     stub.stub_last_attn_k_mean.restype = ctypes.c_int64
     stub.stub_last_quant_epoch.restype = ctypes.c_int64
     d = ctypes.c_void_p(0x1000)
@@ -316,6 +317,10 @@ def test_cache_options_route_to_their_kernels(stub):
             assert calls[3] == (1 if opts & 1 else 0)
             assert stub.stub_last_quant_options() == opts
             assert (stub.stub_last_quant_epoch() > 0) == (opts == 0)
+        sched = ctypes.c_int32()
+        assert stub.kvcache_append_schedule(c.h, 2, ctypes.byref(sched)) == OK
+        assert sched.value == (3 if opts & 4 else 2 if opts else 1)
+        assert stub.kvcache_append_schedule(c.h, 0, ctypes.byref(sched)) == EINVAL
         assert stub.chunk_attention(c.h, d, d, d, 8, 0.125, d, None) == OK
         assert stub.stub_last_attn_mx() == (2 if opts & 8 else 1 if opts & 4 else 0)
         assert (stub.stub_last_attn_k_mean() != 0) == bool(opts & 1)
