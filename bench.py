@@ -68,11 +68,11 @@ def parse():
                    help="untimed attention launches enqueued right before the timed ones")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--skip-configs", action="store_true", help="rollout + roofline legs only")
-    p.add_argument("--only", choices=["attention", "quantize", "copy"],
+    p.add_argument("--only", choices=["attention", "quantize", "copy", "stream"],
                    help="run one kernel leg only (for profiler runs): the attention kernel on the "
                         "steady-state rollout cache (the roofline leg), the append of the "
                         "quantize-only workload, or a plain 256 MiB device copy (reference for "
-                        "the HBM byte counters)")
+                        "the HBM byte counters), or the same-size streaming reference of the append")
     p.add_argument("--mxfp4", action="store_true",
                    help="with --only attention / quantize: the cache holds MXFP4 instead of NVFP4")
     p.add_argument("--mx-scaled-qk", action="store_true",
@@ -321,6 +321,31 @@ def quantize_leg(args, torch, ops, W, device, k_smooth=False, v_adaptive=False, 
     return out, sets
 
 
+def stream_leg(args, torch, ops, W, device, sets):
+    """The same-size streaming reference: the bytes of one K+V append of the quantize
+    workload (2 B read, 1/2 + 1/16 B written per element) moved with the quantizer's
+    tiling and no exchange between workgroups, cycling the same 10 cache-cold input
+    sets: the time this transfer size allows."""
+    wl = W.WORKLOADS["quantize"]
+    H, T, D = wl.n_heads, wl.chunk_tokens, wl.head_dim
+    out = [torch.empty(s, dtype=torch.uint8, device=device)
+           for s in ((H, T, D // 2), (H, T, D // 16), (H, T, D // 2), (H, T, D // 16))]
+    it = [0]
+
+    def run():
+        k, v = sets[it[0] % len(sets)]
+        it[0] += 1
+        ops.stream_reference(k, v, out)
+
+    reps = max(args.quantize_reps, 1)
+    dist = {}
+    ms = timed(run, reps, torch, warm=10, host_us_per_call=60.0, dist=dist)
+    nbytes = 2 * W.quantize_bytes(H * T * D)
+    gbps = nbytes / (ms * 1e-3) / 1e9
+    return {"us_per_call": ms * 1e3, "bytes_per_call": nbytes, "GB_per_s": gbps, "frac_hbm_peak": gbps / HBM_PEAK_GBPS,
+            "per_call": dist}
+
+
 def attention_config(name, args, torch, ops, W, device, k_smooth=False, v_adaptive=False, mxfp4=False,
                      mx_scaled_qk=False):
     wl = W.WORKLOADS[name]
@@ -471,6 +496,12 @@ def main():
         print(json.dumps({"leg": "copy", "bytes_read": src.numel() * 4, "bytes_written": dst.numel() * 4,
                           "ms": ms, "GB_per_s": 2 * src.numel() * 4 / (ms * 1e-3) / 1e9}), flush=True)
         return
+    if args.only == "stream":
+        wl = W.WORKLOADS["quantize"]
+        sets = [tuple(dev_bits(torch, b, device) for b in W.clean_chunk(wl, c)) for c in range(10)]
+        r = stream_leg(args, torch, ops, W, device, sets)
+        print(json.dumps({"leg": "stream", "workload": "quantize", **r}), flush=True)
+        return
     if args.only == "quantize":
         qz, _ = quantize_leg(args, torch, ops, W, device, mxfp4=args.mxfp4)
         print(json.dumps({"leg": "quantize", "workload": "quantize", "mxfp4": args.mxfp4, **qz}), flush=True)
@@ -514,6 +545,9 @@ def main():
                                                              mx_scaled_qk=True)
         log(f"wan13b, MXFP4 cache, MX-scaled QK^T with MXFP8 queries: "
             f"{configs['wan13b_mxfp4_scaled_qk']['us']:.1f} us")
+    sr = stream_leg(args, torch, ops, W, device, qsets)
+    configs["quantize_stream_reference"] = sr
+    log(f"stream reference (same bytes, no exchange): {sr['us_per_call']:.2f} us = {sr['GB_per_s']:.1f} GB/s")
     configs["quantize"] = {k: qz[k] for k in ("us_per_append", "GB_per_s", "bytes_per_append")}
     configs["quantize"]["frac_hbm_peak"] = qz["roofline"]["frac"]
 

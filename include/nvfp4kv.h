@@ -116,6 +116,16 @@ size_t nvfp4_quantize_noalloc_scratch_bytes(void);
 int nvfp4_quantize_kv_noalloc(const uint16_t *x, int64_t H, int64_t T, int64_t D, uint8_t *codes,
                               uint8_t *scales, float *tensor_scale, void *stream);
 
+/* Measurement hook: the bytes of a two-tensor NVFP4 codec call (2 bytes read, 1/2 + 1/16
+ * byte written per element) moved with the quantizer's tiling, no exchange between
+ * workgroups and almost no arithmetic -- the time this transfer size allows on the GPU.
+ * x0, x1 bf16 [H, T, D]; codes0/1 uint8 [H, T, D/2] and scales0/1 uint8 [H, T, D/16]
+ * receive bytes derived from the inputs that are NOT an NVFP4 encoding.
+ * Errors: EINVAL (null or misaligned pointer, sizes as for nvfp4_quantize_kv), EHIP. */
+int nvfp4kv_stream_reference(const uint16_t *x0, const uint16_t *x1, int64_t H, int64_t T, int64_t D,
+                             uint8_t *codes0, uint8_t *scales0, uint8_t *codes1, uint8_t *scales1,
+                             void *stream);
+
 /* ------------------------------------------------------------------------------
  * Standalone MXFP4 codec of one tensor: the block-scaled FP4 format the paper text's
  * appendix A.2 ("FP4 Quantization") sets against NVFP4, as defined by the OCP

@@ -261,6 +261,27 @@ int nvfp4_quantize_kv(const uint16_t *x, int64_t H, int64_t T, int64_t D, uint8_
   return launch_quantize(a, stream);
 }
 
+int nvfp4kv_stream_reference(const uint16_t *x0, const uint16_t *x1, int64_t H, int64_t T, int64_t D,
+                             uint8_t *codes0, uint8_t *scales0, uint8_t *codes1, uint8_t *scales1,
+                             void *stream) {
+  if (!x0 || !x1 || !codes0 || !scales0 || !codes1 || !scales1) return NVFP4KV_EINVAL;
+  if (!aligned(x0, 16) || !aligned(x1, 16) || !aligned(codes0, 8) || !aligned(codes1, 8)) return NVFP4KV_EINVAL;
+  if (H < 1 || T < 1 || D < 16 || D % 16 != 0 || D > 4096) return NVFP4KV_EINVAL;
+  if (H * T * D >= (int64_t(1) << 40) || T > (int64_t(1) << 30) || H > (1 << 20)) return NVFP4KV_EINVAL;
+  QuantArgs a;
+  memset(&a, 0, sizeof(a));
+  a.t[0] = QuantTensor{x0, codes0, scales0, nullptr, 0, 0, nullptr};
+  a.t[1] = QuantTensor{x1, codes1, scales1, nullptr, 0, 0, nullptr};
+  a.n_tensors = 2;
+  a.H = int32_t(H);
+  a.T = int32_t(T);
+  a.D = int32_t(D);
+  a.tokens_per_frame = int32_t(T);
+  a.n_frames = 1;
+  a.rows = T;
+  return launch_stream_reference(a, stream);
+}
+
 size_t nvfp4_quantize_noalloc_scratch_bytes(void) { return kNoAllocScratchBytes; }
 
 int nvfp4_quantize_kv_noalloc(const uint16_t *x, int64_t H, int64_t T, int64_t D, uint8_t *codes,

@@ -138,6 +138,8 @@ int launch_quantize(const QuantArgs &a, void *stream);
 // 1 if launch_quantize would take the single-pass kernel for these arguments on the
 // current device, 0 for the two passes, or a negative status.
 int quantize_single_pass(const QuantArgs &a);
+// Same-size streaming reference of a two-tensor codec launch (measurement hook).
+int launch_stream_reference(const QuantArgs &a, void *stream);
 // The standalone codec with its workspace in the library's per-device scratch array
 // (a.ws is ignored): no allocation.  EHIP if the array's address cannot be resolved.
 constexpr size_t kNoAllocScratchBytes = sizeof(QuantWorkspace);

@@ -1036,6 +1036,50 @@ int launch_quantize(const QuantArgs &in, void *stream) {
   return NVFP4KV_HIP_OK(hipGetLastError());
 }
 
+// ---- same-size streaming reference (a measurement hook, not part of the method)
+// Reads two bf16 tensors of n elements and writes, per tensor, n/2 code bytes and
+// n/16 scale bytes in the codec layout, with the quantizer's tiling (one octet of
+// tokens x one 16-element block per thread, one 256-token x D tile per workgroup, one
+// workgroup per tile) and a trivial per-element operation: the same bytes moved with
+// no exchange between workgroups and almost no arithmetic, i.e. the time this
+// transfer size allows.
+__global__ __launch_bounds__(kQuantThreads) void stream_reference_kernel(QuantArgs a) {
+  const int tid = threadIdx.x;
+  const int nb = a.D >> 4;
+  const int opt = kQuantThreads / nb;
+  const int b = tid % nb, o = tid / nb;
+  const Octet oc = locate_octet(a, blockIdx.x, min(o, opt - 1));
+  uint4 u[kOctet][2];
+  load_octet(a, oc, b, u);
+  if (o >= opt) return;
+  const QuantTensor &qt = a.t[oc.tensor];
+#pragma unroll
+  for (int j = 0; j < kOctet; ++j) {
+    // code nibble = the top 4 bits of each bf16 (sign and 3 exponent bits); scale
+    // byte = the block's largest exponent byte
+    uint32_t c[2] = {0u, 0u}, e = 0u;
+    const uint32_t w[8] = {u[j][0].x, u[j][0].y, u[j][0].z, u[j][0].w, u[j][1].x, u[j][1].y, u[j][1].z, u[j][1].w};
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      c[k >> 2] |= (((w[k] >> 12) & 0xFu) | ((w[k] >> 24) & 0xF0u)) << (8 * (k & 3));
+      e = max(e, (w[k] >> 7) & 0xFFu);
+    }
+    if (j < oc.nvalid) {
+      const int64_t row = int64_t(oc.h) * a.rows + oc.row + j;
+      *reinterpret_cast<uint2 *>(qt.codes + row * (a.D / 2) + b * 8) = make_uint2(c[0], c[1]);
+      qt.scales[row * nb + b] = uint8_t(e);
+    }
+  }
+}
+
+int launch_stream_reference(const QuantArgs &in, void *stream) {
+  QuantArgs a = in;
+  if (int rc = quantize_tiles(a)) return rc;
+  hipLaunchKernelGGL(stream_reference_kernel, dim3(unsigned(a.total_tiles)), dim3(kQuantThreads), 0,
+                     reinterpret_cast<hipStream_t>(stream), a);
+  return NVFP4KV_HIP_OK(hipGetLastError());
+}
+
 // ---- the codec without a caller workspace
 // File-scope device array standing in for the workspace: one copy per GPU, at its
 // own address on each, resolved once per device with hipGetSymbolAddress (in host

@@ -51,6 +51,7 @@ def lib():
             "nvfp4_quantize_workspace_bytes": (SZ, []),
             "nvfp4_quantize_kv": (I, [P, I64, I64, I64, P, P, P, P, SZ, P]),
             "nvfp4_quantize_noalloc_scratch_bytes": (SZ, []),
+            "nvfp4kv_stream_reference": (I, [P, P, I64, I64, I64, P, P, P, P, P]),
             "nvfp4_quantize_kv_noalloc": (I, [P, I64, I64, I64, P, P, P, P]),
             "mxfp4_quantize_kv": (I, [P, I64, I64, I64, P, P, P]),
             "kvcache_storage_bytes": (SZ, [ctypes.POINTER(KVCacheConfig)]),
@@ -154,6 +155,16 @@ def quantize_kv_noalloc(x, out=None):
                                          _stream())
     _check(rc, "nvfp4_quantize_kv_noalloc")
     return codes, scales, ts
+
+
+def stream_reference(x0, x1, out):
+    """Measurement hook: moves the bytes of a two-tensor codec call with the quantizer's
+    tiling and no exchange between workgroups (outputs are not an encoding).  out =
+    (codes0, scales0, codes1, scales1), preallocated uint8 tensors."""
+    H, T, D = x0.shape
+    ptrs = [ctypes.c_void_p(t.data_ptr()) for t in out]
+    _check(lib().nvfp4kv_stream_reference(_bf16_ptr(x0, "x0"), _bf16_ptr(x1, "x1", (H, T, D)), H, T, D, *ptrs,
+                                          _stream()), "nvfp4kv_stream_reference")
 
 
 def mxfp4_quantize_kv(x):

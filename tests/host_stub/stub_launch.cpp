@@ -33,6 +33,7 @@ int launch_quantize_noalloc(const QuantArgs &a, void *) {
   return 0;
 }
 int quantize_single_pass(const QuantArgs &a) { return a.epoch > 0 ? 1 : 0; }
+int launch_stream_reference(const QuantArgs &, void *) { return take_fail(); }
 int g_mx_calls = 0;
 int launch_quantize_mx(const QuantArgs &a, void *) {
   if (int rc = take_fail()) return rc;
