@@ -77,6 +77,10 @@ def parse():
                    help="with --only attention / quantize: the cache holds MXFP4 instead of NVFP4")
     p.add_argument("--mx-scaled-qk", action="store_true",
                    help="with --only attention --mxfp4: QK^T on the MX-scaled matrix cores (MXFP8 queries)")
+    p.add_argument("--k-smooth", action="store_true",
+                   help="with --only quantize: the cache applies K-smoothing")
+    p.add_argument("--v-adaptive", action="store_true",
+                   help="with --only quantize: the cache applies adaptive 4/6 V block scales")
     return p.parse_args()
 
 
@@ -503,8 +507,10 @@ def main():
         print(json.dumps({"leg": "stream", "workload": "quantize", **r}), flush=True)
         return
     if args.only == "quantize":
-        qz, _ = quantize_leg(args, torch, ops, W, device, mxfp4=args.mxfp4)
-        print(json.dumps({"leg": "quantize", "workload": "quantize", "mxfp4": args.mxfp4, **qz}), flush=True)
+        qz, _ = quantize_leg(args, torch, ops, W, device, mxfp4=args.mxfp4, k_smooth=args.k_smooth,
+                             v_adaptive=args.v_adaptive)
+        print(json.dumps({"leg": "quantize", "workload": "quantize", "mxfp4": args.mxfp4,
+                          "k_smooth": args.k_smooth, "v_adaptive": args.v_adaptive, **qz}), flush=True)
         return
 
     r = rollout(args, torch, ops, W, device)

@@ -62,7 +62,10 @@ const char *nvfp4kv_version(void);
  * maxima through the cache's workspace; a workgroup that has polled `limit` times
  * without finding every other workgroup's maxima helps instead, computing one missing
  * workgroup's tile maxima per further poll and publishing them in its place (bounded
- * extra work: about one more read of the chunk in all).
+ * extra work: about one more read of the chunk in all).  With K-smoothing the K
+ * workgroups also exchange their tiles' channel sums and their max |K - mean| the same
+ * way (a helper computes a missing tile's sums, or its maximum after the means of its
+ * head: at most about two more reads of K).
  * chunk_attention: a query block cut between workgroups is finished by the one that
  * holds its LAST key tiles: the workgroups holding its earlier tiles each publish the
  * partial result of their part, and the last one waits for them for at most `limit`
@@ -170,7 +173,9 @@ int mxfp4_quantize_kv(const uint16_t *x, int64_t H, int64_t T, int64_t D, uint8_
  *   NVFP4KV_V_ADAPTIVE  each V block is encoded with its maximum mapped to 6 and to 4
  *                       (same tensor scale) and keeps the encoding with the smaller
  *                       fp32 squared error (ties: 6).  Decoding is unchanged.
- * Appends with options run the two-pass quantizer (plus the mean reduction).
+ * Appends with options run their own single-pass quantizer when its grid fits on the
+ *                       GPU at once (kvcache_append_schedule), else the channel-mean
+ *                       reduction and the two-pass quantizer; the results are the same.
  *   NVFP4KV_MXFP4       the cache holds MXFP4 instead (see mxfp4_quantize_kv: 32-element
  *                       blocks, E8M0 scales, no tensor scale; the paper text's appendix
  *                       A.2 contrasts the two formats).  Appends run one single-pass
@@ -238,9 +243,11 @@ int kvcache_append(kvcache *c, const uint16_t *k, const uint16_t *v, int32_t n_f
 
 /* The kernel schedule an append of n_frames frames takes on the current device (host
  * output): 1 = the single-pass quantizer (one kernel, each chunk element read once),
- * 2 = the two-pass quantizer (caches with K-smoothing or adaptive V scales, or a grid
- * that would not fit on the GPU at once), 3 = the MXFP4 quantizer (one kernel, no
- * exchange between workgroups).  Errors: EINVAL, EHIP. */
+ * 2 = the two-pass quantizer (a grid that would not fit on the GPU at once; with
+ * K-smoothing, after the channel-mean reduction), 3 = the MXFP4 quantizer (one kernel,
+ * no exchange between workgroups), 4 = the single-pass quantizer with the cache's
+ * K-smoothing and/or adaptive V scales (one kernel; K workgroups also exchange their
+ * tiles' channel sums and their max |K - mean|).  Errors: EINVAL, EHIP. */
 int kvcache_append_schedule(const kvcache *c, int32_t n_frames, int32_t *schedule);
 
 /* Drops the oldest n_frames window frames (never sinks); metadata only.

@@ -30,7 +30,7 @@ bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p
 
 struct Layout {
   int64_t rows;   // token capacity per head
-  size_t kcodes, kscales, vcodes, vscales, table, ws, attn_flags, attn_part, kmean, kmean_ws, total;
+  size_t kcodes, kscales, vcodes, vscales, table, ws, opt_slots, attn_flags, attn_part, kmean, kmean_ws, total;
 };
 
 bool config_ok(const kvcache_config *c) {
@@ -66,6 +66,10 @@ bool make_layout(const kvcache_config *c, Layout *L) {
   L->vscales = off; off = round_up(off + size_t(H * L->rows * D / block));
   L->table = off;   off = round_up(off + sizeof(float) * 2 * kScaleSlots);
   L->ws = off;      off = round_up(off + sizeof(QuantWorkspace));
+  const int64_t t_max = int64_t(c->sink_frames + c->window_frames) * c->tokens_per_frame;
+  L->opt_slots = off;
+  if (c->options & NVFP4KV_K_SMOOTH)   // the smoothing single pass's exchange words (zeroed)
+    off = round_up(off + sizeof(uint64_t) * option_slot_words(int(H), t_max, int(D)));
   L->attn_flags = off; off = round_up(off + sizeof(uint64_t) * attn_max_grid(int(D)));
   L->attn_part = off; off = round_up(off + attn_max_grid(int(D)) * attn_slot_bytes(int(D)));
   L->kmean = off;
@@ -75,7 +79,6 @@ bool make_layout(const kvcache_config *c, Layout *L) {
     // for the longest chunk an append accepts (sink + window frames)
     off = round_up(off + sizeof(float) * kScaleSlots * H * D);
     L->kmean_ws = off;
-    const int64_t t_max = int64_t(c->sink_frames + c->window_frames) * c->tokens_per_frame;
     off = round_up(off + sizeof(float) * channel_mean_ws_floats(int(H), int(t_max), int(D)));
   }
   L->total = off;
@@ -138,6 +141,8 @@ struct kvcache {
     return reinterpret_cast<float *>(base + L.kmean) + int64_t(scale_slot) * cfg.n_heads * cfg.head_dim;
   }
   float *kmean_ws() const { return reinterpret_cast<float *>(base + L.kmean_ws); }
+  uint64_t *cmax_slots() const { return reinterpret_cast<uint64_t *>(base + L.opt_slots); }
+  uint64_t *sum_slots() const { return cmax_slots() + 16 * kMaxQuantGrid; }
   int32_t window_slot(const State &s, int32_t i) const { return s.win[(s.win_head + i) % kMaxFrames]; }
   bool in_shot_sink(const State &s, int64_t frame) const {
     return frame >= s.shot_start && frame < s.shot_start + cfg.shot_frames;
@@ -418,13 +423,20 @@ int kvcache_append(kvcache *c, const uint16_t *k, const uint16_t *v, int32_t n_f
   a.rows = c->L.rows;
   a.ws = c->ws();
   a.epoch = ++c->epoch;   // never reused, even if the launch fails
+  if (uint32_t(a.epoch) == 0) a.epoch = ++c->epoch;   // tagged words use the low half; 0 = never written
   a.spin_limit = g_spin_limit.load(std::memory_order_relaxed);
-  if (cfg.options) a.epoch = 0;   // smoothing / adaptive scales: the two-pass kernels
-  if (c->k_smooth()) {
-    const int rm = launch_channel_mean(k, cfg.n_heads, a.T, cfg.head_dim, c->kmean(sslot), c->kmean_ws(), stream);
-    if (rm != NVFP4KV_OK) return rm;
+  int rc;
+  if (c->mx()) {
+    rc = launch_quantize_mx(a, stream);
+  } else if (cfg.options) {
+    if (c->k_smooth()) {
+      a.sum_slots = c->sum_slots();
+      a.cmax_slots = c->cmax_slots();
+    }
+    rc = launch_quantize_options(a, c->k_smooth() ? c->kmean(sslot) : nullptr, c->kmean_ws(), stream);
+  } else {
+    rc = launch_quantize(a, stream);
   }
-  const int rc = c->mx() ? launch_quantize_mx(a, stream) : launch_quantize(a, stream);
   if (rc != NVFP4KV_OK) return rc;
   c->st = s;
   return NVFP4KV_OK;
@@ -446,7 +458,13 @@ int kvcache_append_schedule(const kvcache *c, int32_t n_frames, int32_t *schedul
   a.D = cfg.head_dim;
   a.tokens_per_frame = cfg.tokens_per_frame;
   a.n_frames = n_frames;
-  a.epoch = cfg.options ? 0 : 1;   // as kvcache_append: options take the two passes
+  a.epoch = 1;
+  if (cfg.options) {   // the slots are part of every K-smoothing cache
+    const int rc = quantize_options_single_pass(a, c->k_smooth(), (cfg.options & NVFP4KV_V_ADAPTIVE) != 0);
+    if (rc < 0) return rc;
+    *schedule = rc ? 4 : 2;
+    return NVFP4KV_OK;
+  }
   const int rc = quantize_single_pass(a);
   if (rc < 0) return rc;
   *schedule = rc ? 1 : 2;

@@ -51,8 +51,28 @@ struct QuantArgs {
   int32_t spin_limit;         // polls of the single-pass wait before its fallback scan
   uint64_t epoch;             // > 0: the single-pass kernel may be used with this epoch
   QuantWorkspace *ws;
+  // Single pass with K-smoothing (null: the options take the two passes).  Words
+  // (low 32 bits of the epoch) << 32 | fp32 bits, current only when the tag matches
+  // the launch's epoch, so they start zeroed and the low half of an epoch is never 0.
+  uint64_t *sum_slots;        // [2][H][tiles_per_head][D]: each K tile's channel sums, then
+                              // its channel extremes (bf16 bits of the largest << 16 | smallest)
+  uint64_t *cmax_slots;       // [16 x kMaxQuantGrid]: each head's max |K - mean|, one word
+                              // per 128-byte line (every K workgroup of the head writes it)
+  float *k_mean_out;          // receives the channel means [H][D]
   int32_t frame_slot[kMaxFrames];   // destination slot of each source frame
 };
+
+// Tokens of one quantizer tile for the cache's head_dim (one octet of tokens per
+// thread, 256 threads, D/16 threads per octet).
+inline int64_t quant_tile_tokens(int D) { return int64_t(8) * kQuantThreads / (D / 16); }
+// Words of the K-smoothing single pass's slots for chunks of up to t_max tokens: the
+// head words, the tile statistics, and slack for the reads of the statistics past a
+// head's last tile (at most max(tiles_per_head, 16) nodes of 64 words).
+inline size_t option_slot_words(int H, int64_t t_max, int D) {
+  const int64_t tt = quant_tile_tokens(D);
+  const int64_t tiles = (t_max + tt - 1) / tt;
+  return size_t(16 * kMaxQuantGrid + 2 * int64_t(H) * tiles * D + (tiles + 16) * 64);
+}
 
 // One level of the K-smoothing channel sums: a pairwise tree over each channel's
 // tokens (padded with +0.0 to a power of two), `group` leaves per workgroup.
@@ -138,6 +158,13 @@ int launch_quantize(const QuantArgs &a, void *stream);
 // 1 if launch_quantize would take the single-pass kernel for these arguments on the
 // current device, 0 for the two passes, or a negative status.
 int quantize_single_pass(const QuantArgs &a);
+// Appends with K-smoothing (k_mean: the chunk's means [H][D], written) and/or adaptive
+// V scales (a.t[1].adaptive): the single pass with the options when it fits on the
+// device at once (a.epoch > 0, and the slots given for K-smoothing), else the channel
+// means (kmean_ws: channel_mean_ws_floats(H, T, D) floats) and the two passes.
+int launch_quantize_options(const QuantArgs &a, float *k_mean, float *kmean_ws, void *stream);
+// 1 if launch_quantize_options would take its single pass, 0 if not, or a negative status.
+int quantize_options_single_pass(const QuantArgs &a, bool k_smooth, bool v_adaptive);
 // Same-size streaming reference of a two-tensor codec launch (measurement hook).
 int launch_stream_reference(const QuantArgs &a, void *stream);
 // The standalone codec with its workspace in the library's per-device scratch array

@@ -169,6 +169,14 @@ __device__ __forceinline__ void unpack16(const uint4 (&u)[2], float (&x)[16]) {
   }
 }
 
+// Element i (0..15) of one token's block as fp32 (exact), extracted where it is used.
+__device__ __forceinline__ float elem16(const uint4 (&u)[2], int i) {
+  const uint4 q = u[i >> 3];
+  const int c = (i >> 1) & 3;
+  const uint32_t w = c == 0 ? q.x : c == 1 ? q.y : c == 2 ? q.z : q.w;
+  return __uint_as_float((i & 1) ? (w & 0xFFFF0000u) : (w << 16));
+}
+
 // bf16 bits of max |x| over one token's 16 values (finite inputs: the order of the
 // magnitude bits is the order of the values), on packed 16-bit maxima.
 typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
@@ -325,10 +333,21 @@ __device__ __forceinline__ void item_transposed(const QuantArgs &a, const Octet 
   uint32_t out[16];
 #pragma unroll
   for (int d = 0; d < 16; ++d) out[d] = 0u;
-  // with the maxima at hand (no adaptive choice), every scale byte and divisor first
+  // every scale byte and divisor first when the maxima are at hand, or (adaptive
+  // scales) after choosing each token's byte on its own, one token at a time
   float2 dvp[kOctet];
-  const bool pre = bmax && !ADAPT;
-  if (pre) {
+  const bool pre = bmax || ADAPT;
+  if (ADAPT) {
+#pragma unroll
+    for (int j = 0; j < kOctet; ++j) {
+      float x[16];
+      unpack16(u[j], x);
+      const float m = bmax ? __uint_as_float(bmax[j] << 16) : absmax16(x);
+      sc[j] = choose_scale46<SCALED>(x, m, scale_code(m, tc), tc, tab);
+    }
+#pragma unroll
+    for (int j = 0; j < kOctet; ++j) dvp[j] = tab[sc[j]];
+  } else if (bmax) {
 #pragma unroll
     for (int j = 0; j < kOctet; ++j) sc[j] = scale_code(__uint_as_float(bmax[j] << 16), tc);
 #pragma unroll
@@ -348,10 +367,6 @@ __device__ __forceinline__ void item_transposed(const QuantArgs &a, const Octet 
       const float mb = bmax ? __uint_as_float(bmax[2 * SEL + 1] << 16) : absmax16(xb); \
       sc[2 * SEL] = scale_code(ma, tc);                                               \
       sc[2 * SEL + 1] = scale_code(mb, tc);                                           \
-      if constexpr (ADAPT) {                                                          \
-        sc[2 * SEL] = choose_scale46<SCALED>(xa, ma, sc[2 * SEL], tc, tab);           \
-        sc[2 * SEL + 1] = choose_scale46<SCALED>(xb, mb, sc[2 * SEL + 1], tc, tab);   \
-      }                                                                               \
       da = tab[sc[2 * SEL]];                                                          \
       db = tab[sc[2 * SEL + 1]];                                                      \
     }                                                                                 \
@@ -370,6 +385,19 @@ __device__ __forceinline__ void item_transposed(const QuantArgs &a, const Octet 
         make_uint2(sc[0] | (sc[1] << 8) | (sc[2] << 16) | (sc[3] << 24),
                    sc[4] | (sc[5] << 8) | (sc[6] << 16) | (sc[7] << 24));
   }
+}
+
+// The octet's source only (tensor, head, first token, tokens inside the chunk): what a
+// helper needs, without the destination rows' frame table.
+__device__ __forceinline__ Octet locate_source(const QuantArgs &a, int tile, int o) {
+  Octet r;
+  r.tensor = tile / (a.H * a.tiles_per_head);
+  const int rem = tile - r.tensor * a.H * a.tiles_per_head;
+  r.h = rem / a.tiles_per_head;
+  r.tok = (rem - r.h * a.tiles_per_head) * a.tile_tokens + kOctet * o;
+  r.nvalid = min(max(a.T - r.tok, 0), kOctet);
+  r.row = 0;
+  return r;
 }
 
 __device__ __forceinline__ Octet locate_octet(const QuantArgs &a, int tile, int o) {
@@ -562,7 +590,7 @@ __device__ __forceinline__ void tile_maxima(const QuantArgs &a, int tile, uint32
   const int nb = a.D >> 4;
   const int opt = kQuantThreads / nb;
   const int b = threadIdx.x % nb, o = threadIdx.x / nb;
-  const Octet oc = locate_octet(a, tile, min(o, opt - 1));
+  const Octet oc = locate_source(a, tile, min(o, opt - 1));
   const uint4 *src = reinterpret_cast<const uint4 *>(a.t[oc.tensor].src + int64_t(oc.h) * a.T * a.D + 16 * b);
   uint32_t mx = 0;
   for (int j = 0; j < kOctet; ++j) {
@@ -711,6 +739,637 @@ __global__ __launch_bounds__(kQuantThreads) void quantize_fused_kernel(QuantArgs
       if (tr) item_transposed<true>(a, oc, b, u, tc, tab, bm);
       else item_canonical<true>(a, oc, b, u, tc, tab, bm);
     }
+  }
+}
+
+// ---- single pass with the cache options (K-smoothing, adaptive V block scales)
+// Its own kernel with its own occupancy check, so that the plain single pass keeps
+// its registers.  The structure is the plain single pass's, with the options' extra
+// exchanges:
+//  * V workgroups (and K workgroups without smoothing) publish their tile maxima and
+//    wait for the slots of their own tensor only, then encode (V with the adaptive
+//    block scale when asked).
+//  * K workgroups with smoothing need the channel means before the tensor maximum.
+//    The means' pairwise tree runs over the +0.0-padded power-of-two token count
+//    n_in; a tile of tile_tokens tokens starting at a multiple of tile_tokens is one
+//    aligned subtree of it (all of it when n_in < tile_tokens: the chunk is then one
+//    tile).  Each workgroup publishes, per channel, its tile's node sum and the
+//    largest and smallest value of its tokens; waits for the nodes of its head;
+//    finishes the top of the tree (nodes past the last tile are +0.0) and divides by
+//    T: the same fp32 operations as the tree taken level by level.  Rounding is
+//    monotone, so over a channel's values x the largest |RN(x - mean)| is that of its
+//    largest or of its smallest value: the head's max |K - mean| follows from the
+//    published extremes, exactly.  Every workgroup of the head publishes that head
+//    word (all alike), waits for every head's word, and encodes K - mean from its
+//    registers.
+// The exchanged words carry the low half of the launch's epoch in their upper half,
+// so a reader that sees the tag sees the value (no fences).  Every wait is bounded:
+// past a.spin_limit polls a workgroup helps, one missing tile or head per round (the
+// k-th missing one, k from its own number), computing exactly what its owner would
+// publish; a missing head word is computed from that head's published tiles (helping
+// with them first if some are missing).
+namespace {
+
+struct OptShared {
+  uint32_t red[2][kQuantThreads / 64];
+  int cnt[kQuantThreads / 64];
+  int pick;
+  uint32_t mask;
+  float2 tab[kScaleCodes];
+  float mu[128];
+  float mu_help[128];
+  float part[kQuantThreads * 16];      // [octets per tile][D]: each octet's channel sums
+  uint32_t ext[kQuantThreads * 16];    // [octets per tile][D]: its largest | smallest value (bf16 bits)
+};
+
+__device__ __forceinline__ uint64_t tagged(const QuantArgs &a, uint32_t bits) {
+  return (uint64_t(uint32_t(a.epoch)) << 32) | bits;
+}
+__device__ __forceinline__ bool tag_ok(const QuantArgs &a, uint64_t w) {
+  return uint32_t(w >> 32) == uint32_t(a.epoch);
+}
+
+// Leaves of the means tree under one node: min(n_in, tile_tokens), n_in the power of
+// two >= T; and the nodes of the tree's top.
+__device__ __forceinline__ int node_leaves(const QuantArgs &a) {
+  const int n_in = a.T <= 1 ? 1 : 1 << (32 - __builtin_clz(uint32_t(a.T - 1)));
+  return min(n_in, a.tile_tokens);
+}
+__device__ __forceinline__ int top_nodes(const QuantArgs &a) {
+  const int n_in = a.T <= 1 ? 1 : 1 << (32 - __builtin_clz(uint32_t(a.T - 1)));
+  return n_in / node_leaves(a);
+}
+
+// Pairwise sum of v[0..n), n a power of two <= 32: neighbours first, level by level.
+__device__ __forceinline__ float tree32(const float (&v)[32], int n) {
+  float l1[16], l2[8], l3[4], l4[2];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) l1[i] = v[2 * i] + v[2 * i + 1];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) l2[i] = l1[2 * i] + l1[2 * i + 1];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) l3[i] = l2[2 * i] + l2[2 * i + 1];
+  l4[0] = l3[0] + l3[1];
+  l4[1] = l3[2] + l3[3];
+  const float l5 = l4[0] + l4[1];
+  return n >= 32 ? l5 : n == 16 ? l4[0] : n == 8 ? l3[0] : n == 4 ? l2[0] : n == 2 ? l1[0] : v[0];
+}
+
+// Pairwise sum in push order: after 2^m pushes of aligned subtree sums, st[m] holds
+// their pairwise sum (a pushed value meets its left neighbours level by level).
+template <int N>
+__device__ __forceinline__ void pairwise_push(float (&st)[N], int i, float v) {
+#pragma unroll
+  for (int k = 0; k < N; ++k) {
+    if ((i >> k) & 1) {
+      v = st[k] + v;
+    } else {
+      st[k] = v;
+      return;
+    }
+  }
+}
+template <int N>
+__device__ __forceinline__ float pairwise_total(const float (&st)[N], int levels) {
+  float r = st[0];
+#pragma unroll
+  for (int k = 1; k < N; ++k) r = k == levels ? st[k] : r;
+  return r;
+}
+
+// Word of tile statistic (head h, channel c, tile of the head `node`): channels in
+// groups of 64, the tiles of a head consecutive within a group, so that a wave's 64
+// channels of one node are one 512-byte run and the nodes of a channel are 512 bytes
+// apart (immediate offsets from one address).
+__device__ __forceinline__ int64_t stat_index(const QuantArgs &a, int h, int c, int node) {
+  return ((int64_t(h) * (a.D >> 6) + (c >> 6)) * a.tiles_per_head + node) * 64 + (c & 63);
+}
+
+// Packed extremes of bf16 values: largest value's bits << 16 | smallest value's bits.
+__device__ __forceinline__ uint32_t ext_pack(float hi, float lo) {
+  return (__float_as_uint(hi) & 0xFFFF0000u) | (__float_as_uint(lo) >> 16);
+}
+__device__ __forceinline__ float ext_hi(uint32_t e) { return __uint_as_float(e & 0xFFFF0000u); }
+__device__ __forceinline__ float ext_lo(uint32_t e) { return __uint_as_float(e << 16); }
+
+// Workgroup-wide count of missing slots (bit i of `miss`: slot tid + i * kQuantThreads
+// of the polled range) and maxima of k, v.  With `help` and some missing, the k-th
+// missing slot (k = seed mod the count) is left in sh.pick.  Every thread calls it;
+// it ends with a barrier.
+__device__ int poll_reduce(uint32_t miss, uint32_t &k, uint32_t &v, bool help, uint32_t seed,
+                           OptShared &sh) {
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int cnt = __builtin_popcount(miss);
+  int incl = cnt;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int y = __shfl_up(incl, off, 64);
+    if (lane >= off) incl += y;
+  }
+  k = wave_max_u32(k);
+  v = wave_max_u32(v);
+  if (lane == 63) sh.cnt[wv] = incl;
+  if (lane == 0) {
+    sh.red[0][wv] = k;
+    sh.red[1][wv] = v;
+  }
+  __syncthreads();
+  int n = 0, before = 0;
+  k = v = 0;
+  for (int i = 0; i < kQuantThreads / 64; ++i) {
+    n += sh.cnt[i];
+    before += i < wv ? sh.cnt[i] : 0;
+    k = max(k, sh.red[0][i]);
+    v = max(v, sh.red[1][i]);
+  }
+  if (help && n > 0) {
+    const int kth = int(seed % uint32_t(n));
+    const int excl = before + incl - cnt;
+    if (kth >= excl && kth < excl + cnt) {
+      uint32_t m = miss;
+      for (int r = kth - excl; r > 0; --r) m &= m - 1;   // drop the lower set bits
+      sh.pick = tid + __builtin_ctz(m) * kQuantThreads;
+    }
+  }
+  __syncthreads();
+  return n;
+}
+
+// Bounded wait for the maxima slots [lo, hi) (helping past the limit); K and V maxima
+// over them.
+__device__ void wait_maxima(const QuantArgs &a, int lo, int hi, uint32_t &gk, uint32_t &gv, OptShared &sh) {
+  constexpr int kSlotsPerThread = kMaxQuantGrid / kQuantThreads;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  for (int spin = 0;; ++spin) {
+    uint32_t k = 0, v = 0, miss = 0;
+#pragma unroll
+    for (int i = 0; i < kSlotsPerThread; ++i) {
+      const int j = lo + tid + i * kQuantThreads;
+      if (j < hi) {
+        const uint64_t w = __hip_atomic_load(&a.ws->slot[j], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if ((w >> 30) != a.epoch) miss |= 1u << i;
+        k = max(k, uint32_t(w >> 15) & 0x7FFFu);
+        v = max(v, uint32_t(w) & 0x7FFFu);
+      }
+    }
+    const bool help = spin >= a.spin_limit;
+    const int n = poll_reduce(miss, k, v, help, blockIdx.x + uint32_t(spin), sh);
+    if (n == 0) {
+      gk = k;
+      gv = v;
+      return;
+    }
+    if (help) {
+      const int tile = lo + sh.pick;
+      uint32_t hk, hv;
+      tile_maxima(a, tile, hk, hv);
+      hk = wave_max_u32(hk);
+      hv = wave_max_u32(hv);
+      if (lane == 0) {
+        sh.red[0][wv] = hk;
+        sh.red[1][wv] = hv;
+      }
+      __syncthreads();
+      if (tid == 0) {
+        uint32_t rk = 0, rv = 0;
+        for (int i = 0; i < kQuantThreads / 64; ++i) {
+          rk = max(rk, sh.red[0][i]);
+          rv = max(rv, sh.red[1][i]);
+        }
+        const uint64_t word = (a.epoch << 30) | (uint64_t(rk) << 15) | uint64_t(rv);
+        __hip_atomic_store(&a.ws->slot[tile], word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+      __syncthreads();
+    } else {
+      __builtin_amdgcn_s_sleep(2);
+    }
+  }
+}
+
+// Order-preserving 16-bit keys of two packed bf16 values (negative values have all
+// bits flipped, others only the sign), so that unsigned 16-bit maxima and minima of
+// keys are those of the values; key_to_bf16 undoes it.
+typedef unsigned short u16x2_t __attribute__((ext_vector_type(2)));
+typedef short i16x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t bf16_keys(uint32_t w) {
+  const uint32_t neg = __builtin_bit_cast(uint32_t, __builtin_bit_cast(i16x2_t, w) >> (i16x2_t){15, 15});
+  return w ^ (neg | 0x80008000u);
+}
+__device__ __forceinline__ uint32_t keys_to_bf16(uint32_t k) {
+  // a key with the top bit clear came from a negative value
+  const uint32_t pos = __builtin_bit_cast(uint32_t, __builtin_bit_cast(i16x2_t, k) >> (i16x2_t){15, 15});
+  return k ^ (~pos | 0x80008000u);
+}
+__device__ __forceinline__ uint32_t pk_max_u16(uint32_t x, uint32_t y) {
+  return __builtin_bit_cast(uint32_t, __builtin_elementwise_max(__builtin_bit_cast(u16x2_t, x), __builtin_bit_cast(u16x2_t, y)));
+}
+__device__ __forceinline__ uint32_t pk_min_u16(uint32_t x, uint32_t y) {
+  return __builtin_bit_cast(uint32_t, __builtin_elementwise_min(__builtin_bit_cast(u16x2_t, x), __builtin_bit_cast(u16x2_t, y)));
+}
+
+// One half (8 channels) of the thread's octet into the LDS tables: the channel sums
+// of its 8 leaves, pairwise (tokens past T are +0.0; a node of fewer than 8 leaves,
+// L < 8, i.e. T <= 4, is the left part of octet 0), and the channel extremes (tokens
+// past T re-read the last token, a value of the channel), as bf16 bits.
+__device__ __forceinline__ void octet_half(const uint4 (&uh)[kOctet], int nvalid, int L, float *sums,
+                                           uint32_t *ext) {
+  // extremes: per word (two channels) the packed key maxima / minima over the tokens
+  uint32_t kmax[4], kmin[4];
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    uint32_t k = bf16_keys(c == 0 ? uh[0].x : c == 1 ? uh[0].y : c == 2 ? uh[0].z : uh[0].w);
+    kmax[c] = kmin[c] = k;
+#pragma unroll
+    for (int j = 1; j < kOctet; ++j) {
+      k = bf16_keys(c == 0 ? uh[j].x : c == 1 ? uh[j].y : c == 2 ? uh[j].z : uh[j].w);
+      kmax[c] = pk_max_u16(kmax[c], k);
+      kmin[c] = pk_min_u16(kmin[c], k);
+    }
+    kmax[c] = keys_to_bf16(kmax[c]);
+    kmin[c] = keys_to_bf16(kmin[c]);
+  }
+  uint32_t e[8];
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    e[2 * c] = (kmax[c] << 16) | (kmin[c] & 0xFFFFu);
+    e[2 * c + 1] = (kmax[c] & 0xFFFF0000u) | (kmin[c] >> 16);
+  }
+  // sums
+  float s[8];
+  const bool full = nvalid == kOctet;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    float x[kOctet];
+#pragma unroll
+    for (int j = 0; j < kOctet; ++j) {
+      const uint4 q = uh[j];
+      const int c = i >> 1;
+      const uint32_t w = c == 0 ? q.x : c == 1 ? q.y : c == 2 ? q.z : q.w;
+      x[j] = __uint_as_float((i & 1) ? (w & 0xFFFF0000u) : (w << 16));
+      if (!full) x[j] = j < nvalid ? x[j] : 0.0f;
+    }
+    const float p0 = x[0] + x[1], p1 = x[2] + x[3], p2 = x[4] + x[5], p3 = x[6] + x[7];
+    const float q0 = p0 + p1, q1 = p2 + p3;
+    s[i] = L >= 8 ? q0 + q1 : L == 4 ? q0 : L == 2 ? p0 : x[0];
+  }
+  float4 *s4 = reinterpret_cast<float4 *>(sums);
+  s4[0] = make_float4(s[0], s[1], s[2], s[3]);
+  s4[1] = make_float4(s[4], s[5], s[6], s[7]);
+  uint4 *e4 = reinterpret_cast<uint4 *>(ext);
+  e4[0] = make_uint4(e[0], e[1], e[2], e[3]);
+  e4[1] = make_uint4(e[4], e[5], e[6], e[7]);
+}
+
+// The octets' tables -> the tile's node sum and extremes per channel, published as
+// tagged words sums[h][tile of the head][c] and ext[h][tile of the head][c] (ext after
+// the H x tiles_per_head x D sums).  Threads [0, D) take the sums, threads [D, 2D) the
+// extremes.  Every thread calls it.
+__device__ void publish_tile_stats(const QuantArgs &a, int tile, int h, OptShared &sh) {
+  __syncthreads();
+  const int tid = threadIdx.x;
+  const int L = node_leaves(a);
+  const int n_oct = L >= 8 ? L / 8 : 1;                 // octets under the node (at most 64)
+  const int n_all = kQuantThreads / (a.D >> 4);         // octets of the tile
+  const int64_t n_sums = int64_t(a.H) * a.tiles_per_head * a.D;
+  if (tid < a.D) {
+    float v[32];
+#pragma unroll
+    for (int i = 0; i < 32; ++i) v[i] = i < n_oct ? sh.part[i * a.D + tid] : 0.0f;
+    float node = tree32(v, min(n_oct, 32));
+    if (n_oct > 32) {   // two aligned halves of 32 octets
+#pragma unroll
+      for (int i = 0; i < 32; ++i) v[i] = sh.part[(32 + i) * a.D + tid];
+      node = node + tree32(v, 32);
+    }
+    __hip_atomic_store(a.sum_slots + stat_index(a, h, tid, tile % a.tiles_per_head),
+                       tagged(a, __float_as_uint(node)), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  } else if (tid < 2 * a.D) {
+    const int c = tid - a.D;
+    float hi = -__builtin_inff(), lo = __builtin_inff();
+    for (int i0 = 0; i0 < n_all; i0 += 32) {   // 32 or 64 octets: independent reads
+      uint32_t e[32];
+#pragma unroll
+      for (int i = 0; i < 32; ++i) e[i] = sh.ext[(i0 + i) * a.D + c];
+#pragma unroll
+      for (int i = 0; i < 32; ++i) {
+        hi = fmaxf(hi, ext_hi(e[i]));
+        lo = fminf(lo, ext_lo(e[i]));
+      }
+    }
+    __hip_atomic_store(a.sum_slots + n_sums + stat_index(a, h, c, tile % a.tiles_per_head),
+                       tagged(a, ext_pack(hi, lo)), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  __syncthreads();
+}
+
+// The owner: its tile's statistics from the registers.
+__device__ void own_tile_stats(const QuantArgs &a, int tile, const Octet &oc, int o, int b,
+                               const uint4 (&u)[kOctet][2], OptShared &sh) {
+  const int L = node_leaves(a);
+#pragma unroll
+  for (int hh = 0; hh < 2; ++hh) {
+    uint4 uh[kOctet];
+#pragma unroll
+    for (int j = 0; j < kOctet; ++j) uh[j] = u[j][hh];
+    octet_half(uh, oc.nvalid, L, sh.part + o * a.D + 16 * b + 8 * hh, sh.ext + o * a.D + 16 * b + 8 * hh);
+  }
+  publish_tile_stats(a, tile, oc.h, sh);
+}
+
+// A helper: loads K tile `tile` half a block at a time and publishes its statistics.
+__device__ void help_tile_stats(const QuantArgs &a, int tile, OptShared &sh) {
+  const int nb = a.D >> 4;
+  const int opt = kQuantThreads / nb;
+  const int b = threadIdx.x % nb, o = threadIdx.x / nb;
+  const Octet oc = locate_source(a, tile, min(o, opt - 1));
+  const int L = node_leaves(a);
+  const uint4 *src = reinterpret_cast<const uint4 *>(a.t[0].src + int64_t(oc.h) * a.T * a.D + 16 * b);
+#pragma unroll
+  for (int hh = 0; hh < 2; ++hh) {
+    uint4 uh[kOctet];
+#pragma unroll
+    for (int j = 0; j < kOctet; ++j) uh[j] = src[int64_t(min(oc.tok + j, a.T - 1)) * (a.D / 8) + hh];
+    octet_half(uh, oc.nvalid, L, sh.part + o * a.D + 16 * b + 8 * hh, sh.ext + o * a.D + 16 * b + 8 * hh);
+  }
+  publish_tile_stats(a, tile, oc.h, sh);
+}
+
+// Means of head h into mu[0..D) and the head's max |K - mean| (fp32 bits, returned to
+// every thread): waits until every tile of the head has published its statistics
+// (bounded; then helps), finishes the top of the means tree with the nodes past the
+// last tile as +0.0 and divides by T; per channel max(|RN(hi - mean)|, |RN(lo - mean)|)
+// over the head's extremes.  The nodes go in batches of 32 (aligned subtrees when
+// there are more); P = 256 / D threads share a channel, each taking 32 / P consecutive
+// nodes of the batch.  Every thread calls it.
+__device__ uint32_t head_stats(const QuantArgs &a, int h, float *mu, OptShared &sh) {
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int tph = a.tiles_per_head;
+  const int n_top = top_nodes(a);           // a power of two, >= tph, <= 2^11
+  const int P = kQuantThreads / a.D;        // 2 (D = 128) or 4 (D = 64)
+  const int npp = 32 / P;                   // nodes per thread and batch: 16 or 8
+  const int c = tid % a.D, part = tid / a.D;
+  const int n_batch = min(n_top, 32);       // nodes per batch (all batches alike)
+  const int n_parts = max(1, n_batch / npp);   // parts holding nodes of a batch
+  const int n_mine = min(npp, n_batch);     // nodes per part
+  const int64_t n_sums = int64_t(a.H) * tph * a.D;
+  float st[7];                              // pairwise stack over the batches
+  float hi = -__builtin_inff(), lo = __builtin_inff();
+  // First a light wait on one word per tile of the head (its channel-0 extremes), so
+  // that the full statistics are normally read once; the full read below still checks
+  // every word's tag (another lane's words may become visible later) and polls again.
+  for (int spin = 0;; ++spin) {
+    uint32_t miss = 0, k = 0, v = 0;
+    for (int i = 0; i < (tph + kQuantThreads - 1) / kQuantThreads; ++i) {
+      const int node = tid + i * kQuantThreads;
+      if (node < tph && !tag_ok(a, __hip_atomic_load(a.sum_slots + n_sums + stat_index(a, h, 0, node),
+                                                    __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)))
+        miss |= 1u << i;
+    }
+    const bool help = spin >= a.spin_limit;
+    if (poll_reduce(miss, k, v, help, blockIdx.x + uint32_t(spin), sh) == 0) break;
+    if (help) help_tile_stats(a, h * tph + sh.pick, sh);   // barriers inside
+    else __builtin_amdgcn_s_sleep(2);
+  }
+  if (tid == 0) sh.mask = 0u;
+  __syncthreads();
+  for (int base = 0, spin = 0; base < n_top; base += 32) {
+    float half = 0.0f;
+    while (true) {
+      uint32_t miss = 0;
+      float bh = -__builtin_inff(), bl = __builtin_inff();
+      if (part < n_parts) {
+        uint64_t w[16], x[16];
+        const int first = base + part * npp;
+        // unconditional loads from one address: nodes past the head's last tile (at
+        // most max(tiles_per_head, 16) of them) read the next rows' words or the slack
+        // after the arrays, and are not used
+        const uint64_t *ps = a.sum_slots + stat_index(a, h, c, first), *px = ps + n_sums;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          w[i] = __hip_atomic_load(ps + 64 * i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          x[i] = __hip_atomic_load(px + 64 * i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+        float v[32];
+#pragma unroll
+        for (int i = 0; i < 32; ++i) {
+          v[i] = 0.0f;
+          if (i < 16) {
+            const bool real = i < n_mine && first + i < tph;   // past the last tile: +0.0
+            if (real && !(tag_ok(a, w[i]) && tag_ok(a, x[i]))) miss |= 1u << (part * npp + i);
+            v[i] = real ? __uint_as_float(uint32_t(w[i])) : 0.0f;
+            if (real) {
+              bh = fmaxf(bh, ext_hi(uint32_t(x[i])));
+              bl = fminf(bl, ext_lo(uint32_t(x[i])));
+            }
+          }
+        }
+        half = tree32(v, n_mine);
+      }
+      if (miss) atomicOr(&sh.mask, miss);
+      __syncthreads();
+      const uint32_t all = sh.mask;
+      if (all == 0u) {
+        if (part > 0 && part < n_parts) sh.part[part * a.D + c] = half;
+        hi = fmaxf(hi, bh);
+        lo = fminf(lo, bl);
+        __syncthreads();
+        break;
+      }
+      __syncthreads();
+      if (tid == 0) sh.mask = 0u;   // everyone has read it; the next writes follow a barrier
+      if (spin >= a.spin_limit) {
+        uint32_t m = all;
+        for (int r = int((blockIdx.x + uint32_t(spin)) % uint32_t(__builtin_popcount(all))); r > 0; --r) m &= m - 1;
+        help_tile_stats(a, h * tph + base + __builtin_ctz(m), sh);   // barriers inside
+      } else {
+        __builtin_amdgcn_s_sleep(2);
+        __syncthreads();
+      }
+      ++spin;
+    }
+    if (part == 0) {
+      float sub = half;   // the batch's subtree: its parts pairwise (1, 2 or 4 of them)
+      if (n_parts == 2) sub = half + sh.part[a.D + c];
+      if (n_parts == 4) sub = (half + sh.part[a.D + c]) + (sh.part[2 * a.D + c] + sh.part[3 * a.D + c]);
+      pairwise_push(st, base / 32, sub);
+    }
+    __syncthreads();   // sh.part is read before the next batch or a helper writes it
+  }
+  // the parts' extremes of each channel meet in LDS; then the channel's maximum
+  if (part > 0) {
+    sh.ext[part * a.D + c] = ext_pack(hi, lo);
+  }
+  __syncthreads();
+  uint32_t m = 0;
+  if (part == 0) {
+    for (int p = 1; p < P; ++p) {
+      hi = fmaxf(hi, ext_hi(sh.ext[p * a.D + c]));
+      lo = fminf(lo, ext_lo(sh.ext[p * a.D + c]));
+    }
+    const int levels = n_top > 32 ? __builtin_ctz(uint32_t(n_top / 32)) : 0;
+    const float mean = pairwise_total(st, levels) / float(a.T);
+    mu[c] = mean;
+    m = max(__float_as_uint(hi - mean) & 0x7FFFFFFFu, __float_as_uint(lo - mean) & 0x7FFFFFFFu);
+  }
+  m = wave_max_u32(m);
+  if (lane == 0) sh.red[0][wv] = m;
+  __syncthreads();
+  uint32_t r = 0;
+  for (int i = 0; i < kQuantThreads / 64; ++i) r = max(r, sh.red[0][i]);
+  __syncthreads();
+  return r;
+}
+
+// One poll of the H head words: returns the number missing (the k-th missing one,
+// k = seed mod the count, left in sh.pick when `help`) and their maximum in kmax.
+__device__ int poll_heads(const QuantArgs &a, bool help, uint32_t seed, uint32_t &kmax, OptShared &sh) {
+  constexpr int kSlotsPerThread = kMaxQuantGrid / kQuantThreads;
+  const int tid = threadIdx.x;
+  uint32_t k = 0, v = 0, miss = 0;
+#pragma unroll
+  for (int i = 0; i < kSlotsPerThread; ++i) {
+    const int j = tid + i * kQuantThreads;
+    if (j < a.H) {
+      const uint64_t w = __hip_atomic_load(a.cmax_slots + 16 * j, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (!tag_ok(a, w)) miss |= 1u << i;
+      k = max(k, uint32_t(w));
+    }
+  }
+  const int n = poll_reduce(miss, k, v, help, seed, sh);
+  kmax = k;
+  return n;
+}
+
+// max |x - mu| (fp32 bits) of the thread's 8 tokens of one block, per token.
+__device__ __forceinline__ void centered_maxima(const uint4 (&u)[kOctet][2], const float (&mu)[16],
+                                                uint32_t (&bmf)[kOctet]) {
+#pragma unroll
+  for (int j = 0; j < kOctet; ++j) {
+    uint32_t m = 0;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) m = max(m, __float_as_uint(elem16(u[j], i) - mu[i]) & 0x7FFFFFFFu);
+    bmf[j] = m;
+  }
+}
+
+// K - mean in the codec layout: per token the block's scale byte from its max
+// |x - mean| (taken before s_t was known), then the codes with two-correction
+// quotients (x - mean is not a bf16 value).
+template <bool SCALED>
+__device__ __forceinline__ void item_centered(const QuantArgs &a, const Octet &o, int b,
+                                              const uint4 (&u)[kOctet][2], const float (&mu)[16],
+                                              const uint32_t (&bmf)[kOctet], const TensorConsts &tc,
+                                              const float2 *tab) {
+  const QuantTensor &qt = a.t[o.tensor];
+  const int nb = a.D >> 4;
+  uint32_t scp[kOctet];
+  float2 dvp[kOctet];
+#pragma unroll
+  for (int j = 0; j < kOctet; ++j) scp[j] = scale_code(__uint_as_float(bmf[j]), tc);
+#pragma unroll
+  for (int j = 0; j < kOctet; ++j) dvp[j] = tab[scp[j]];
+#pragma unroll
+  for (int j = 0; j < kOctet; ++j) {
+    float x[16];
+    unpack16(u[j], x);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) x[i] = x[i] - mu[i];
+    const uint2 c = encode_token<SCALED, false>(x, dvp[j].x, dvp[j].y, tc.xs);
+    if (j < o.nvalid) {
+      const int64_t row = int64_t(o.h) * a.rows + o.row + j;
+      *reinterpret_cast<uint2 *>(qt.codes + row * (a.D / 2) + b * 8) = c;
+      qt.scales[row * nb + b] = uint8_t(scp[j]);
+    }
+  }
+}
+
+}  // namespace
+
+template <bool KS, bool VA>
+__global__ __launch_bounds__(kQuantThreads, 2) void quantize_options_kernel(QuantArgs a) {
+  __shared__ OptShared sh;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int nb = a.D >> 4;
+  const int opt = kQuantThreads / nb;         // octets per tile
+  const int b = tid % nb, o = tid / nb;
+  const int nk = a.H * a.tiles_per_head;      // K tiles come first
+  const int tile = blockIdx.x;
+  const bool is_k = tile < nk;
+
+  uint4 u[kOctet][2];
+  const Octet oc = locate_octet(a, tile, min(o, opt - 1));
+  load_octet(a, oc, b, u);
+
+  float st;
+  float mu[16];
+  uint32_t bm[kOctet];    // per token: the block's max |x| (bf16 bits) or max |x - mean| (fp32 bits)
+  if (KS && is_k) {
+    own_tile_stats(a, tile, oc, o, b, u, sh);
+    // The tile is read again for the encode (from the caches) once the tensor maximum
+    // is known: holding it in registers through the statistics exchange would spill.
+    // First the own head's statistics; then, while head words are missing, wait or
+    // (past the limit) compute a missing head's word (one call site of head_stats).
+    int head = oc.h;
+    uint32_t kmax = 0;
+    for (int spin = -1;; ++spin) {
+      if (head >= 0) {
+        const uint32_t m = head_stats(a, head, spin < 0 ? sh.mu : sh.mu_help, sh);
+        if (tid == 0) __hip_atomic_store(a.cmax_slots + 16 * head, tagged(a, m), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+      if (spin < 0 && tile % a.tiles_per_head == 0 && tid < a.D) a.k_mean_out[int64_t(oc.h) * a.D + tid] = sh.mu[tid];
+      const bool help = spin >= a.spin_limit;
+      if (poll_heads(a, help, blockIdx.x + uint32_t(spin), kmax, sh) == 0) break;
+      head = help ? sh.pick : -1;
+      if (!help) __builtin_amdgcn_s_sleep(2);
+    }
+    st = __uint_as_float(kmax) / 2688.0f;
+    load_octet(a, oc, b, u);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) mu[i] = sh.mu[16 * b + i];
+    centered_maxima(u, mu, bm);
+  } else {
+    uint32_t mx = 0;
+#pragma unroll
+    for (int j = 0; j < kOctet; ++j) {
+      bm[j] = block_max_bits(u[j]);
+      mx = max(mx, bm[j]);
+    }
+    const uint32_t mk = wave_max_u32(is_k ? mx : 0u), mv = wave_max_u32(is_k ? 0u : mx);
+    if (lane == 0) {
+      sh.red[0][wv] = mk;
+      sh.red[1][wv] = mv;
+    }
+    __syncthreads();
+    if (tid == 0) {
+      uint32_t rk = 0, rv = 0;
+      for (int i = 0; i < kQuantThreads / 64; ++i) {
+        rk = max(rk, sh.red[0][i]);
+        rv = max(rv, sh.red[1][i]);
+      }
+      const uint64_t word = (a.epoch << 30) | (uint64_t(rk) << 15) | uint64_t(rv);
+      __hip_atomic_store(&a.ws->slot[tile], word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    __syncthreads();
+    uint32_t gk, gv;
+    wait_maxima(a, is_k ? 0 : nk, is_k ? nk : 2 * nk, gk, gv, sh);
+    st = bf16_bits_to_float(is_k ? gk : gv) / 2688.0f;
+  }
+
+  if ((tile == 0 || tile == nk) && tid == 0) *a.t[is_k ? 0 : 1].tensor_scale = st;
+  const TensorConsts tc = tensor_consts(st);
+  for (int e = tid; e < kScaleCodes; e += kQuantThreads) sh.tab[e] = divisor_entry(e, st, tc.xs);
+  __syncthreads();
+  if (is_k) {
+    if constexpr (KS) {
+      if (tc.xs == 1.0f) item_centered<false>(a, oc, b, u, mu, bm, tc, sh.tab);
+      else item_centered<true>(a, oc, b, u, mu, bm, tc, sh.tab);
+    } else {
+      if (tc.xs == 1.0f) item_canonical<false>(a, oc, b, u, tc, sh.tab, bm);
+      else item_canonical<true>(a, oc, b, u, tc, sh.tab, bm);
+    }
+  } else {
+    if (tc.xs == 1.0f) item_transposed<false, VA>(a, oc, b, u, tc, sh.tab, bm);
+    else item_transposed<true, VA>(a, oc, b, u, tc, sh.tab, bm);
   }
 }
 
@@ -1034,6 +1693,85 @@ int launch_quantize(const QuantArgs &in, void *stream) {
   hipLaunchKernelGGL(quantize_encode_kernel, dim3(unsigned(g2)), dim3(kQuantThreads), 0, s, a,
                      int(g1));
   return NVFP4KV_HIP_OK(hipGetLastError());
+}
+
+namespace {
+// Co-resident workgroups per CU of each options instantiation (0: not yet asked, -1: none).
+int g_opt_per_cu[kMaxDevices][3];
+
+template <bool KS, bool VA>
+int options_per_cu(int dev) {
+  int &slot = g_opt_per_cu[dev][(KS ? 1 : 0) + (VA ? 2 : 0) - 1];
+  if (slot == 0) {
+    int per = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, quantize_options_kernel<KS, VA>, kQuantThreads, 0) !=
+        hipSuccess)
+      return NVFP4KV_EHIP;
+    slot = per > 0 ? per : -1;
+  }
+  return slot;
+}
+
+// 1 when the options single pass takes this launch (a.tile_tokens etc. already set).
+int options_fits(const QuantArgs &a, bool ks, bool va, int dev) {
+  if (!ks && !va) return 0;
+  if (a.epoch == 0 || uint32_t(a.epoch) == 0 || a.n_tensors != 2 || a.total_tiles > kMaxQuantGrid) return 0;
+  if (dev < 0 || dev >= kMaxDevices) return 0;
+  if (ks) {
+    if (!a.sum_slots || !a.cmax_slots || !a.k_mean_out || a.D > 128) return 0;
+    // the top of the means tree: at most 2^11 nodes per head
+    int64_t n_in = 1;
+    while (n_in < a.T) n_in *= 2;
+    const int64_t leaves = n_in < a.tile_tokens ? n_in : a.tile_tokens;
+    if (n_in / leaves > 2048) return 0;
+  }
+  const int per = ks ? (va ? options_per_cu<true, true>(dev) : options_per_cu<true, false>(dev))
+                     : options_per_cu<false, true>(dev);
+  if (per < 0 && per != -1) return per;
+  return per > 0 && a.total_tiles <= int64_t(cu_count(dev)) * per ? 1 : 0;
+}
+}  // namespace
+
+int quantize_options_single_pass(const QuantArgs &in, bool k_smooth, bool v_adaptive) {
+  QuantArgs a = in;
+  if (int rc = quantize_tiles(a)) return rc;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return NVFP4KV_EHIP;
+  // the cache gives the slots to every K-smoothing append; stand-ins for the check
+  static uint64_t probe;
+  static float probe_mean;
+  if (k_smooth) {
+    a.sum_slots = a.cmax_slots = &probe;
+    a.k_mean_out = &probe_mean;
+  }
+  return options_fits(a, k_smooth, v_adaptive, dev);
+}
+
+int launch_quantize_options(const QuantArgs &in, float *k_mean, float *kmean_ws, void *stream) {
+  QuantArgs a = in;
+  if (int rc = quantize_tiles(a)) return rc;
+  const bool ks = k_mean != nullptr, va = a.n_tensors > 1 && a.t[1].adaptive != 0;
+  a.k_mean_out = k_mean;
+  a.t[0].mean = k_mean;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return NVFP4KV_EHIP;
+  const int fits = options_fits(a, ks, va, dev);
+  if (fits < 0) return fits;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  if (fits) {
+    const dim3 grid(unsigned(a.total_tiles)), block(kQuantThreads);
+    if (ks && va) hipLaunchKernelGGL((quantize_options_kernel<true, true>), grid, block, 0, s, a);
+    else if (ks) hipLaunchKernelGGL((quantize_options_kernel<true, false>), grid, block, 0, s, a);
+    else hipLaunchKernelGGL((quantize_options_kernel<false, true>), grid, block, 0, s, a);
+    return NVFP4KV_HIP_OK(hipGetLastError());
+  }
+  // the two passes, after the channel means
+  if (ks) {
+    const int rm = launch_channel_mean(a.t[0].src, a.H, a.T, a.D, k_mean, kmean_ws, stream);
+    if (rm != NVFP4KV_OK) return rm;
+  }
+  a.epoch = 0;
+  return launch_quantize(a, stream);
 }
 
 // ---- same-size streaming reference (a measurement hook, not part of the method)

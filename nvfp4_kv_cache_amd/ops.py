@@ -227,7 +227,8 @@ class KVCache:
         _check(rc, "kvcache_append")
 
     def append_schedule(self, n_frames):
-        """1: single-pass quantizer, 2: two passes, 3: MXFP4 quantizer (see the header)."""
+        """1: single-pass quantizer, 2: two passes, 3: MXFP4 quantizer, 4: single pass
+        with the cache options (see the header)."""
         r = ctypes.c_int32()
         _check(lib().kvcache_append_schedule(self._h, n_frames, ctypes.byref(r)), "kvcache_append_schedule")
         return r.value

@@ -33,6 +33,17 @@ int launch_quantize_noalloc(const QuantArgs &a, void *) {
   return 0;
 }
 int quantize_single_pass(const QuantArgs &a) { return a.epoch > 0 ? 1 : 0; }
+int g_opt_calls = 0;
+// as the library: the options' single pass when given an epoch, which appends always
+// give; the K means are then written by the quantizer itself
+int launch_quantize_options(const QuantArgs &a, float *k_mean, float *, void *) {
+  if (int rc = take_fail()) return rc;
+  g_q = a;
+  g_q.t[0].mean = k_mean;
+  ++g_opt_calls;
+  return 0;
+}
+int quantize_options_single_pass(const QuantArgs &a, bool, bool) { return a.epoch > 0 ? 1 : 0; }
 int launch_stream_reference(const QuantArgs &, void *) { return take_fail(); }
 int g_mx_calls = 0;
 int launch_quantize_mx(const QuantArgs &a, void *) {
@@ -66,7 +77,15 @@ int zero_device_bytes_blocking(void *, size_t) { return 0; }
 using namespace nvfp4kv;
 
 extern "C" {
-int stub_calls(int kind) { return kind == 4 ? g_mx_calls : kind == 3 ? g_mean_calls : g_calls[kind]; }
+int stub_calls(int kind) {
+  return kind == 5 ? g_opt_calls : kind == 4 ? g_mx_calls : kind == 3 ? g_mean_calls : g_calls[kind];
+}
+// slots of the last quantize launch (K-smoothing single pass), as offsets from the
+// storage base, or -1 when null
+int64_t stub_last_quant_slots_ptr(int which) {
+  const void *p = which ? static_cast<const void *>(g_q.sum_slots) : static_cast<const void *>(g_q.cmax_slots);
+  return p ? reinterpret_cast<int64_t>(p) : -1;
+}
 // format seen by the last attention and export launches: 1 / 32 for MXFP4
 int stub_last_attn_mx(void) { return g_a.mx; }
 int stub_last_export_block(void) { return g_e.block; }

@@ -219,13 +219,15 @@ def test_append_wait_fallback_help(ops):
 
 
 @pytest.mark.parametrize("D,T_f,frames", [(128, 40, [2, 1, 3]), (64, 8, [1, 2, 4]), (128, 1560, [3]),
-                                          (64, 64, [4, 1])])
+                                          (64, 64, [4, 1]), (128, 3000, [3]), (64, 5800, [3])])
 def test_append_k_smoothing_and_adaptive_v(ops, D, T_f, frames):
     """Cache appends with K-smoothing and adaptive 4/6 V scales: the channel means
-    (pairwise fp32 tree; token counts 8 to 4680, padded to powers of two), K codes of
+    (pairwise fp32 tree; token counts 8 to 17400, padded to powers of two: up to 64
+    aligned tile nodes per head, i.e. two batches at the top of the tree), K codes of
     x - mean, V codes with the chosen block scales, and both tensor scales equal the
     oracle's bit for bit.  K has per-channel offsets, a constant channel and a -0
-    channel; V has heavy tails so that both scale candidates occur."""
+    channel; V has heavy tails so that both scale candidates occur.  These appends
+    take the single pass with the options (schedule 4)."""
     from gpu_util import dev, host
     from oracle import channel_mean_ref
     rng = np.random.default_rng(D + T_f)
@@ -233,6 +235,7 @@ def test_append_k_smoothing_and_adaptive_v(ops, D, T_f, frames):
     cache = ops.KVCache(H, D, T_f, 1, 6, k_smooth=True, v_adaptive=True)
     chunks = []
     for nf in frames:
+        assert cache.append_schedule(nf) == 4
         T = nf * T_f
         kx = (rng.standard_normal((H, T, D)) + rng.standard_normal((H, 1, D)) * 8).astype(np.float32)
         kx[0, :, 3] = 1.5
@@ -265,6 +268,7 @@ def test_append_adaptive_v_only(ops, D, T_f, frames):
     cache = ops.KVCache(H, D, T_f, 1, 6, v_adaptive=True)
     chunks = []
     for nf in frames:
+        assert cache.append_schedule(nf) == 4
         k = t4_bits(rng, (H, nf * T_f, D), 1.5)
         v = t4_bits(rng, (H, nf * T_f, D), 2.0)
         cache.append(dev(k), dev(v), nf)
@@ -280,9 +284,8 @@ def test_append_adaptive_v_only(ops, D, T_f, frames):
 
 def test_append_k_smoothing_extreme_scales(ops):
     """K-smoothing and adaptive V appends of chunks at extreme scales (1e-20, 3e5,
-    with per-channel offsets in K), under either poll limit (these appends take the
-    two-pass quantizer, which has no wait): codes, scale bytes and tensor scales
-    equal the oracle's."""
+    with per-channel offsets in K), with poll limits 0 (help at once) and 65536:
+    codes, scale bytes and tensor scales equal the oracle's."""
     from gpu_util import dev, host
     from oracle import channel_mean_ref
     H, D, T_f = 3, 128, 256
@@ -308,3 +311,52 @@ def test_append_k_smoothing_extreme_scales(ops):
             kc, ks, vc, vs, sk, sv = r[c]
             assert_codec_equal((kc, ks, sk[0]), wk, f"chunk {c} K")
             assert_codec_equal((vc, vs, sv[0]), wv, f"chunk {c} V")
+
+
+@pytest.mark.parametrize("k_smooth,v_adaptive", [(True, True), (True, False), (False, True)])
+def test_append_options_wait_fallback_help(ops, k_smooth, v_adaptive):
+    """The single pass with the cache options under poll limits 0, 1, 2 and 65536:
+    with a small limit its workgroups help instead of waiting, computing missing
+    tiles' maxima, K channel sums, or max |K - mean| (after the means of that tile's
+    head) in their owners' place.  Means, codes, scale bytes and tensor scales must
+    not change, for a small grid and for the quantize workload's 456 workgroups."""
+    from gpu_util import dev, host
+    from oracle import channel_mean_ref
+    rng = np.random.default_rng(17)
+    H, D, T_f = 4, 128, 256         # 2 tiles per head: 8 K and 8 V workgroups
+    small = []
+    for s in (1.0, 1e-20, 3e5):
+        kx = (rng.standard_normal((H, 2 * T_f, D)) + rng.standard_normal((H, 1, D)) * 8) * s
+        small.append((W.f32_to_bf16_bits(kx.astype(np.float32)), t4_bits(rng, (H, 2 * T_f, D), 1.0 / s)))
+    wl = W.WORKLOADS["quantize"]
+    cases = [(H, D, T_f, 2, small),
+             (wl.n_heads, wl.head_dim, wl.tokens_per_frame, wl.chunk_frames,
+              [W.clean_chunk(wl, c) for c in range(2)])]
+    for H, D, T_f, nf, chunks in cases:
+        results = []
+        for limit in (0, 1, 2, 1 << 16):
+            print(f"[options help] ks={k_smooth} va={v_adaptive} H={H} T_f={T_f} wait limit {limit}", flush=True)
+            ops.set_wait_limit(limit)
+            try:
+                cache = ops.KVCache(H, D, T_f, 2, 4 * nf, k_smooth=k_smooth, v_adaptive=v_adaptive)
+                assert cache.append_schedule(nf) == 4
+                for k, v in chunks:
+                    cache.append(dev(k), dev(v), nf)
+                r = []
+                for c in range(len(chunks)):
+                    mu = host(cache.export_k_mean(c)) if k_smooth else None
+                    r.append((tuple(host(t) for t in cache.export_chunk(c)), mu))
+                results.append(r)
+                cache.close()
+            finally:
+                ops.set_wait_limit(1 << 16)
+        for c, (k, v) in enumerate(chunks):
+            mu_want = channel_mean_ref(k) if k_smooth else None
+            wk = quantize_ref(k, mean=mu_want)
+            wv = quantize_ref(v, adaptive=v_adaptive)
+            for r in results:
+                (kc, ks, vc, vs, sk, sv), mu = r[c]
+                if k_smooth:
+                    assert np.array_equal(mu.view(np.uint32), mu_want.view(np.uint32)), f"chunk {c} means"
+                assert_codec_equal((kc, ks, sk[0]), wk, f"chunk {c} K")
+                assert_codec_equal((vc, vs, sv[0]), wv, f"chunk {c} V")

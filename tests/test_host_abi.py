@@ -121,13 +121,18 @@ def test_storage_bytes_budget(real):
             if fixed is not None:
                 assert rest == fixed      # independent of the cache length
             fixed = rest
-    # K-smoothing adds the fp32 channel means of every scale slot (65 x H x D) and the
+    # K-smoothing adds the fp32 channel means of every scale slot (65 x H x D), the
     # mean reduction's workspace (two buffers of H x D node sums per 256 padded tokens)
+    # and the single pass's exchange words (2048 head words, one per 128-byte line, and
+    # per 256-token tile of the longest chunk, 3 + 9 frames of 1560 tokens = 74 tiles,
+    # H x D tagged channel sums and H x D tagged channel extremes, and 64 words of slack
+    # per tile plus 16)
     plain = real.kvcache_storage_bytes(ctypes.byref(Cfg(12, 128, 1560, 3, 9)))
     smooth = real.kvcache_storage_bytes(ctypes.byref(Cfg(12, 128, 1560, 3, 9, 0, 1)))
     adaptive = real.kvcache_storage_bytes(ctypes.byref(Cfg(12, 128, 1560, 3, 9, 0, 2)))
     assert adaptive == plain
-    assert smooth - plain == 65 * 12 * 128 * 4 + 2 * 12 * (32768 // 256) * 128 * 4
+    slots = (16 * 2048 + 2 * 12 * 74 * 128 + (74 + 16) * 64) * 8
+    assert smooth - plain == 65 * 12 * 128 * 4 + 2 * 12 * (32768 // 256) * 128 * 4 + -(-slots // 256) * 256
     # MXFP4 (option 4): 17/32 byte per cached element (scales per 32 instead of 16);
     # it does not combine with the NVFP4 options; no other option bits exist
     mx = real.kvcache_storage_bytes(ctypes.byref(Cfg(12, 128, 1560, 3, 9, 0, 4)))
@@ -178,6 +183,7 @@ class StubCache:
         self.L, self.cfg = L, cfg
         n = L.kvcache_storage_bytes(ctypes.byref(cfg))
         assert n > 0
+        self.base, self.nbytes = self.BASE, n
         self.h = ctypes.c_void_p()
         assert L.kvcache_create(ctypes.byref(cfg), ctypes.c_void_p(self.BASE), n, ctypes.byref(self.h)) == OK
 
@@ -303,23 +309,36 @@ def test_cache_options_route_to_their_kernels(stub):
     launches carry the format; kvcache_append_schedule reports the same routing."""
     stub.stub_last_attn_k_mean.restype = ctypes.c_int64
     stub.stub_last_quant_epoch.restype = ctypes.c_int64
+    stub.stub_last_quant_slots_ptr.restype = ctypes.c_int64
     d = ctypes.c_void_p(0x1000)
     for opts in (0, 1, 2, 3, 4, 12):
-        before = [stub.stub_calls(k) for k in range(5)]
+        before = [stub.stub_calls(k) for k in range(6)]
         c = StubCache(stub, Cfg(2, 128, 16, 1, 3, 0, opts))
         assert c.append(2) == OK
-        after = [stub.stub_calls(k) for k in range(5)]
+        after = [stub.stub_calls(k) for k in range(6)]
         calls = [a - b for a, b in zip(after, before)]
+        assert calls[3] == 0   # the mean levels are the options launcher's fallback, not the host's
         if opts & 4:
-            assert calls[0] == 0 and calls[4] == 1 and calls[3] == 0
-        else:
-            assert calls[0] == 1 and calls[4] == 0
-            assert calls[3] == (1 if opts & 1 else 0)
+            assert calls[0] == 0 and calls[4] == 1 and calls[5] == 0
+        elif opts:
+            # K-smoothing and adaptive V scales: the options launcher, with an epoch;
+            # K-smoothing caches also hand it their exchange slots (zeroed at create,
+            # inside the storage)
+            assert calls[5] == 1 and calls[0] == 0 and calls[4] == 0
             assert stub.stub_last_quant_options() == opts
-            assert (stub.stub_last_quant_epoch() > 0) == (opts == 0)
+            assert stub.stub_last_quant_epoch() > 0
+            for which in (0, 1):
+                ptr = stub.stub_last_quant_slots_ptr(which)
+                assert (ptr != -1) == bool(opts & 1)
+                if opts & 1:
+                    assert c.base <= ptr < c.base + c.nbytes
+        else:
+            assert calls[0] == 1 and calls[4] == 0 and calls[5] == 0
+            assert stub.stub_last_quant_options() == 0
+            assert stub.stub_last_quant_epoch() > 0
         sched = ctypes.c_int32()
         assert stub.kvcache_append_schedule(c.h, 2, ctypes.byref(sched)) == OK
-        assert sched.value == (3 if opts & 4 else 2 if opts else 1)
+        assert sched.value == (3 if opts & 4 else 4 if opts else 1)
         assert stub.kvcache_append_schedule(c.h, 0, ctypes.byref(sched)) == EINVAL
         assert stub.chunk_attention(c.h, d, d, d, 8, 0.125, d, None) == OK
         assert stub.stub_last_attn_mx() == (2 if opts & 8 else 1 if opts & 4 else 0)
