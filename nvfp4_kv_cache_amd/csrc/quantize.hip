@@ -498,6 +498,9 @@ __global__ __launch_bounds__(kAmaxThreads) void quantize_amax_kernel(QuantArgs a
 // Pass 2: every workgroup loads the pass-1 partials first, then its first tile; it
 // reduces the partials to s_t and fills a per-tensor table of divisors (eff, 1/eff
 // for each of the 128 scale bytes) while the tile is in flight, then encodes.
+// OPT: the tensors may carry K-smoothing means or adaptive V scales (their items need
+// more registers; the plain codec keeps its own instance).
+template <bool OPT>
 __global__ __launch_bounds__(kQuantThreads) void quantize_encode_kernel(QuantArgs a, int g_amax) {
   __shared__ uint32_t s_red[2][kQuantThreads / 64];
   __shared__ float s_st[2];
@@ -546,18 +549,18 @@ __global__ __launch_bounds__(kQuantThreads) void quantize_encode_kernel(QuantArg
       const bool tr = qt.transposed != 0;
       if (tc.xs == 1.0f) {
         if (tr) {
-          if (qt.adaptive) item_transposed<false, true>(a, oc, b, u, tc, tab);
+          if (OPT && qt.adaptive) item_transposed<false, OPT>(a, oc, b, u, tc, tab);
           else item_transposed<false>(a, oc, b, u, tc, tab);
         } else {
-          if (qt.mean) item_canonical<false, true>(a, oc, b, u, tc, tab);
+          if (OPT && qt.mean) item_canonical<false, OPT>(a, oc, b, u, tc, tab);
           else item_canonical<false>(a, oc, b, u, tc, tab);
         }
       } else {
         if (tr) {
-          if (qt.adaptive) item_transposed<true, true>(a, oc, b, u, tc, tab);
+          if (OPT && qt.adaptive) item_transposed<true, OPT>(a, oc, b, u, tc, tab);
           else item_transposed<true>(a, oc, b, u, tc, tab);
         } else {
-          if (qt.mean) item_canonical<true, true>(a, oc, b, u, tc, tab);
+          if (OPT && qt.mean) item_canonical<true, OPT>(a, oc, b, u, tc, tab);
           else item_canonical<true>(a, oc, b, u, tc, tab);
         }
       }
@@ -1690,8 +1693,11 @@ int launch_quantize(const QuantArgs &in, void *stream) {
   // pass 2: one workgroup per tile, up to 16 per CU, then a grid-stride loop
   int64_t g2 = total;
   if (g2 > int64_t(cus) * 16) g2 = int64_t(cus) * 16;
-  hipLaunchKernelGGL(quantize_encode_kernel, dim3(unsigned(g2)), dim3(kQuantThreads), 0, s, a,
-                     int(g1));
+  const bool opt = a.t[0].mean != nullptr || (a.n_tensors > 1 && a.t[1].adaptive);
+  if (opt)
+    hipLaunchKernelGGL(quantize_encode_kernel<true>, dim3(unsigned(g2)), dim3(kQuantThreads), 0, s, a, int(g1));
+  else
+    hipLaunchKernelGGL(quantize_encode_kernel<false>, dim3(unsigned(g2)), dim3(kQuantThreads), 0, s, a, int(g1));
   return NVFP4KV_HIP_OK(hipGetLastError());
 }
 
