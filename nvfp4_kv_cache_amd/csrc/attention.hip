@@ -634,20 +634,6 @@ __device__ __forceinline__ bool next_full(const AttnArgs &a, int &seg, int &k0) 
   return first_full(a, seg + 1, seg, k0);
 }
 
-// next segment at or after `from` with a ragged tail; k0 = first key of the tail
-__device__ __forceinline__ bool first_tail(const AttnArgs &a, int from, int &seg, int &k0, int &nval) {
-  for (int sg = from; sg < a.n_seg; ++sg) {
-    const int r = a.seg[sg].ntok % kBN;
-    if (r) {
-      seg = sg;
-      k0 = a.seg[sg].ntok - r;
-      nval = r;
-      return true;
-    }
-  }
-  return false;
-}
-
 // i-th full cache tile of a query block -> (segment, first key)
 __device__ __forceinline__ void nth_full(const AttnArgs &a, int i, int &seg, int &k0) {
   int sg = 0;
