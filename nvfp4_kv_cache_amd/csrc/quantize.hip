@@ -12,8 +12,8 @@
 //   * Cache appends (quantize_fused_kernel, one pass): every workgroup of a grid
 //     that is resident all at once (the launcher checks the occupancy) loads its
 //     tile into registers, publishes its maxima in an epoch-tagged workspace slot,
-//     waits (bounded) for every slot of the launch and encodes from the registers,
-//     so the chunk is read once.  No cooperative launch is needed.
+//     waits (bounded) for every slot of its tensor (K or V) and encodes from the
+//     registers, so the chunk is read once.  No cooperative launch is needed.
 //   * The standalone codec, and appends with K-smoothing or adaptive V scales,
 //     whose workspace cannot carry epochs or which need the channel means first:
 //     quantize_amax_kernel streams K and V once and writes one partial maximum per
@@ -575,8 +575,9 @@ __global__ __launch_bounds__(kQuantThreads) void quantize_encode_kernel(QuantArg
 
 // Single pass (cache appends): every workgroup loads its tile into registers,
 // publishes its maxima of |x| in its workspace slot tagged with the launch's epoch,
-// waits until every workgroup's slot carries that epoch, and encodes from the
-// registers, so the chunk is read once.  The launcher only takes this path when the
+// waits until the slot of every workgroup of its tensor carries that epoch (K and V
+// do not wait for each other), and encodes from the registers, so the chunk is read
+// once.  The launcher only takes this path when the
 // grid fits on the GPU at once (occupancy), but co-residency is not guaranteed (other
 // streams' kernels may hold CUs), so the wait is bounded (a.spin_limit polls): past
 // it, a waiting workgroup helps instead of waiting.  Each polling round it takes one
@@ -645,15 +646,19 @@ __global__ __launch_bounds__(kQuantThreads) void quantize_fused_kernel(QuantArgs
   }
   __syncthreads();
 
-  // wait for the slots of every workgroup of this launch (bounded; then help)
+  // wait for the slots of every workgroup of this tensor (bounded; then help): the
+  // K tiles come first, [0, nk), then the V tiles
   constexpr int kSlotsPerThread = kMaxQuantGrid / kQuantThreads;
+  const int nk = a.H * a.tiles_per_head;
+  const bool is_k = int(blockIdx.x) < nk;
+  const int lo = is_k ? 0 : nk, hi = is_k ? nk : int(gridDim.x);
   uint32_t gk = 0, gv = 0;
   for (int spin = 0;; ++spin) {
     uint32_t k = 0, v = 0, miss = 0;
 #pragma unroll
     for (int i = 0; i < kSlotsPerThread; ++i) {
-      const int j = tid + i * kQuantThreads;
-      if (j < int(gridDim.x)) {
+      const int j = lo + tid + i * kQuantThreads;
+      if (j < hi) {
         const uint64_t w = __hip_atomic_load(&a.ws->slot[j], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         if ((w >> 30) != a.epoch) miss |= 1u << i;
         k = max(k, uint32_t(w >> 15) & 0x7FFFu);
@@ -692,7 +697,7 @@ __global__ __launch_bounds__(kQuantThreads) void quantize_fused_kernel(QuantArgs
       if (kth >= excl && kth < excl + cnt) {
         uint32_t m = miss;
         for (int r = kth - excl; r > 0; --r) m &= m - 1;   // drop the lower set bits
-        s_help = tid + (__builtin_ctz(m)) * kQuantThreads;
+        s_help = lo + tid + (__builtin_ctz(m)) * kQuantThreads;
       }
       __syncthreads();
       const int tile = s_help;
@@ -720,16 +725,12 @@ __global__ __launch_bounds__(kQuantThreads) void quantize_fused_kernel(QuantArgs
     __syncthreads();
   }
 
+  // this tensor's scale (the other field of its slots is 0): written by its first tile
   const float st0 = bf16_bits_to_float(gk) / 2688.0f, st1 = bf16_bits_to_float(gv) / 2688.0f;
-  if (blockIdx.x == 0 && tid == 0) {
-    *a.t[0].tensor_scale = st0;
-    if (a.n_tensors > 1) *a.t[1].tensor_scale = st1;
-  }
+  if ((int(blockIdx.x) == 0 || int(blockIdx.x) == nk) && tid == 0) *a.t[is_k ? 0 : 1].tensor_scale = is_k ? st0 : st1;
   const TensorConsts tc0 = tensor_consts(st0), tc1 = tensor_consts(st1);
-  for (int e = tid; e < 2 * kScaleCodes; e += kQuantThreads) {
-    const int t = e / kScaleCodes;
-    s_tab[t][e % kScaleCodes] = divisor_entry(e % kScaleCodes, t ? st1 : st0, t ? tc1.xs : tc0.xs);
-  }
+  for (int e = tid; e < kScaleCodes; e += kQuantThreads)
+    s_tab[oc.tensor][e] = divisor_entry(e, oc.tensor ? st1 : st0, oc.tensor ? tc1.xs : tc0.xs);
   __syncthreads();
   if (act) {
     const TensorConsts &tc = oc.tensor ? tc1 : tc0;
