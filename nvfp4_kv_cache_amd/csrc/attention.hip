@@ -1071,10 +1071,10 @@ int launch_attention_d(AttnArgs a, hipStream_t s) {
   a.n_ofull = a.n_q / kBN;
   a.n_otail = a.n_q % kBN ? 1 : 0;
   a.tiles = nf + nt + a.n_ofull + a.n_otail;
-  // measured relative costs: a pipelined NVFP4 tile 16, a pipelined bf16 own tile 20
-  // (its V is transposed in registers), a ragged tail 28 (not pipelined)
+  // measured relative costs: a pipelined NVFP4 tile 16, a pipelined bf16 own tile 14
+  // (no dequantization), a ragged tail 28 (not pipelined)
   a.w_cfull = 16;
-  a.w_ofull = 20;
+  a.w_ofull = 14;
   a.w_tail = 28;
   const int64_t wb = int64_t(nf) * a.w_cfull + int64_t(nt + a.n_otail) * a.w_tail + int64_t(a.n_ofull) * a.w_ofull;
   if (wb >= (int64_t(1) << 31)) return NVFP4KV_EINVAL;
