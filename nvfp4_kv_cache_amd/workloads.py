@@ -38,6 +38,7 @@ class Workload:
     n_chunks: int = 1        # rollout length (streaming workload)
     steps_per_chunk: int = 1
     description: str = ""
+    query_frames: int = 0    # frames of the query chunk (0: chunk_frames)
 
     @property
     def chunk_tokens(self):
@@ -45,7 +46,7 @@ class Workload:
 
     @property
     def n_q(self):
-        return self.chunk_tokens
+        return (self.query_frames or self.chunk_frames) * self.tokens_per_frame
 
     @property
     def softmax_scale(self):
@@ -60,9 +61,10 @@ class Workload:
 
 
 WORKLOADS = {
-    # 1 head, D=64, 64 queries over a 256-token cache (one 4-frame chunk of
-    # 64-token frames: 1 sink + 3 window frames) plus their own 64 tokens.
-    "tiny": Workload("tiny", 1, 1, 64, 64, 1, 3, 4, 1, "normal",
+    # 1 head, D=64, 64 queries (one 64-token frame) over a 256-token cache (one
+    # 4-frame chunk of 64-token frames: 1 sink + 3 window frames) plus their own
+    # 64 tokens.
+    "tiny": Workload("tiny", 1, 1, 64, 64, 1, 3, 4, 1, "normal", query_frames=1,
                      description="1 head, D64, 64 queries over a 256-token NVFP4 cache + 64 own bf16 tokens"),
     # K, V [12, 4680, 128] appended as one 3-frame chunk into a full 3+9 cache.
     "quantize": Workload("quantize", 2, 12, 128, 1560, 3, 9, 3, 4, "t4_outlier_channels",
@@ -127,9 +129,9 @@ def clean_chunk(wl, chunk):
 
 
 def noisy_chunk(wl, chunk, step=0):
-    """Q, K_own, V_own of the noisy chunk ``chunk`` at denoising ``step``."""
-    return (draw_bf16(wl, chunk, step, Q_ID), draw_bf16(wl, chunk, step, K_ID),
-            draw_bf16(wl, chunk, step, V_ID))
+    """Q, K_own, V_own [H, n_q, D] of the noisy chunk ``chunk`` at denoising ``step``."""
+    return (draw_bf16(wl, chunk, step, Q_ID, wl.n_q), draw_bf16(wl, chunk, step, K_ID, wl.n_q),
+            draw_bf16(wl, chunk, step, V_ID, wl.n_q))
 
 
 def attention_flops(n_heads, n_q, n_k, head_dim):
