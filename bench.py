@@ -40,7 +40,7 @@ CSRC = os.path.join(ROOT, "nvfp4_kv_cache_amd", "csrc")
 # kernel sources whose digest a PMC summary in profiles/ records; a summary taken
 # on other sources no longer describes the kernel, and its traffic is not reported
 TRAFFIC_SOURCES = {
-    "attention": ("attention.hip", "device_common.h", "nvfp4kv_internal.h"),
+    "attention": ("attention.hip", "attn_plan.h", "device_common.h", "nvfp4kv_internal.h"),
     "quantize": ("quantize.hip", "device_common.h", "nvfp4kv_internal.h"),
     "quantize_mx": ("quantize.hip", "device_common.h", "nvfp4kv_internal.h"),
 }

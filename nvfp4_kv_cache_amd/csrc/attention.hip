@@ -57,6 +57,8 @@
 //    shares, i.e. mostly one head's keys.
 
 #include "device_common.h"
+#define NVFP4KV_PLAN_FN __host__ __device__ __forceinline__
+#include "attn_plan.h"
 
 namespace nvfp4kv {
 
@@ -71,7 +73,7 @@ typedef int i32x8 __attribute__((ext_vector_type(8)));
 
 namespace {
 
-constexpr int kBN = 64;        // keys per tile
+constexpr int kBN = kAttnKeys;  // keys per tile
 constexpr int kQW = 32;        // queries per wave
 constexpr float kLazy = 8.0f;  // log2 headroom before the running max is raised
 
@@ -657,27 +659,6 @@ __device__ __forceinline__ int nth_tail(const AttnArgs &a, int i) {
   return sg;
 }
 
-// Workgroup whose share [U g / G, U (g+1) / G) holds weighted position x.
-__device__ __forceinline__ int owner_of(int64_t x, int64_t U, int G) {
-  return int(((x + 1) * G + U - 1) / U) - 1;
-}
-
-// Number of a query block's tiles that start before weighted position x (0 <= x <=
-// the block's weight).  Tiles in order: cache full, cache tails, own full, own tail.
-__device__ __forceinline__ int tiles_before(const AttnArgs &a, int x) {
-  int n = 0;
-  auto part = [&](int count, int w) {
-    const int span = count * w;
-    n += x >= span ? count : (x + w - 1) / w;
-    x = max(x - span, 0);
-  };
-  part(a.n_cfull, a.w_cfull);
-  part(a.n_ctail, a.w_tail);
-  part(a.n_ofull, a.w_ofull);
-  part(a.n_otail, a.w_tail);
-  return n;
-}
-
 // Partial result of a range of a query block's tiles: the accumulator in absolute
 // units of V, then per lane the running max and the partial row sum.  Each thread
 // stores and later reads back only its own elements, 16 bytes at a time, so the
@@ -748,8 +729,7 @@ __global__ __launch_bounds__(Cfg<D>::kThreads, Cfg<D>::kWgPerCu) void chunk_atte
   // this workgroup's share [ubeg, u) of the weighted list of all (query block, key
   // tile) pairs; it processes the tiles that start inside its share (every share is
   // at least one tile long, so every workgroup has tiles), one query block at a time
-  // from the share's END: a share usually holds the first tiles of one block and the
-  // last tiles of the one before, so every workgroup starts at key tile 0 and all
+  // from the share's END (next_range): every workgroup starts at key tile 0 and all
   // workgroups of a head stay within a few tiles of each other (their K/V stays in
   // L2).
   const int64_t U = a.work;
@@ -759,14 +739,9 @@ __global__ __launch_bounds__(Cfg<D>::kThreads, Cfg<D>::kWgPerCu) void chunk_atte
   const int64_t ubeg = U * g / G;
   int64_t u = U * (g + 1) / G;
 
-  while (u > ubeg) {
-    const int64_t b64 = (u - 1) / WB;
-    const int b = int(b64);
-    const int p1 = int(u - b64 * WB);
-    const int p0 = int(max(ubeg - b64 * WB, int64_t(0)));
-    u = b64 * WB + p0;
-    const int t0 = tiles_before(a, p0), t1 = tiles_before(a, p1);
-    if (t0 == t1) continue;
+  int b, t0, t1;
+  while (next_range(a, ubeg, u, b, t0, t1)) {
+    const int64_t b64 = b;
     const int h = b / qblocks;
     const int q0 = (b - h * qblocks) * kBM + w * kQW;
     const int qi = q0 + l32;
@@ -1061,34 +1036,10 @@ int attn_cu_count() {
 template <int D>
 int launch_attention_d(AttnArgs a, hipStream_t s) {
   if (!a.partials || !a.flags) return NVFP4KV_EINVAL;
-  int nf = 0, nt = 0;
-  for (int i = 0; i < a.n_seg; ++i) {
-    nf += a.seg[i].ntok / kBN;
-    nt += a.seg[i].ntok % kBN ? 1 : 0;
-  }
-  a.n_cfull = nf;
-  a.n_ctail = nt;
-  a.n_ofull = a.n_q / kBN;
-  a.n_otail = a.n_q % kBN ? 1 : 0;
-  a.tiles = nf + nt + a.n_ofull + a.n_otail;
-  // measured relative costs: a pipelined NVFP4 tile 16, a pipelined bf16 own tile 14
-  // (no dequantization), a ragged tail 28 (not pipelined)
-  a.w_cfull = 16;
-  a.w_ofull = 14;
-  a.w_tail = 28;
-  const int64_t wb = int64_t(nf) * a.w_cfull + int64_t(nt + a.n_otail) * a.w_tail + int64_t(a.n_ofull) * a.w_ofull;
-  if (wb >= (int64_t(1) << 31)) return NVFP4KV_EINVAL;
-  a.w_block = int32_t(wb);
-  const int64_t blocks = int64_t((a.n_q + Cfg<D>::kBM - 1) / Cfg<D>::kBM) * a.H;
-  if (blocks >= (int64_t(1) << 31)) return NVFP4KV_EINVAL;
-  if (blocks * wb >= (int64_t(1) << 52)) return NVFP4KV_EINVAL;   // share bounds U g / G in int64
-  a.work = blocks * wb;
   // one workgroup per resident slot (every CU busy), each with an equal share of the
-  // weighted work; every share must hold at least one tile start
-  int64_t grid = int64_t(min(attn_cu_count(), kAttnMaxCus)) * Cfg<D>::kWgPerCu;
-  const int64_t wmax = a.w_tail;   // the largest weight
-  if (grid > a.work / wmax) grid = a.work / wmax;
-  if (grid < 1) grid = 1;
+  // weighted work
+  const int64_t grid = attn_plan(a, Cfg<D>::kBM, int64_t(min(attn_cu_count(), kAttnMaxCus)) * Cfg<D>::kWgPerCu);
+  if (grid < 0) return int(grid);
   if (a.mx == 2)
     hipLaunchKernelGGL((chunk_attention_kernel<D, true, true>), dim3(unsigned(grid)), dim3(Cfg<D>::kThreads), 0, s, a);
   else if (a.mx == 1)
