@@ -43,7 +43,8 @@
 //  * Work distribution (stream-K style): the (query block, key tile) pairs of all
 //    heads form one list, weighted by the measured cost of each tile kind, that is
 //    cut into one equal share per resident workgroup (every CU busy, whatever the
-//    number of query blocks).  A share usually ends inside a query block.  Each
+//    number of query blocks; the list arithmetic is attn_plan.h, which a CPU check
+//    shares).  A share usually ends inside a query block.  Each
 //    workgroup walks its share from the end, so it starts at key tile 0 of its last
 //    block (keeping all workgroups of a head in step, for L2 reuse) and publishes
 //    that range's partial result (unnormalized output, running max, row sum); the
