@@ -237,7 +237,8 @@ int kvcache_destroy(kvcache *c);
  * sink_frames frames ever appended become sinks; each later frame enters the window,
  * and when the window is full the oldest window frame is evicted first (FIFO).
  * Errors: EINVAL (null or misaligned, n_frames < 1), ECAPACITY (more than window_frames frames of
- * this chunk would enter the window), EHIP. */
+ * this chunk would enter the window), ESTATE (2^31 - 1 chunks already appended to this
+ * cache: chunk numbers and the kernels' epoch tags would repeat), EHIP. */
 int kvcache_append(kvcache *c, const uint16_t *k, const uint16_t *v, int32_t n_frames,
                    void *stream);
 

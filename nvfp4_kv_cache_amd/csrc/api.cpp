@@ -363,6 +363,9 @@ int kvcache_append(kvcache *c, const uint16_t *k, const uint16_t *v, int32_t n_f
   if (n_frames < 1 || n_frames > kMaxFrames) return NVFP4KV_EINVAL;
   const kvcache_config &cfg = c->cfg;
   if (int64_t(n_frames) * cfg.tokens_per_frame > (int64_t(1) << 30)) return NVFP4KV_EINVAL;
+  // chunk numbers are int32, and the quantizers' epoch tags hold the epoch's low 32
+  // bits: both stay unique below 2^31 appends
+  if (c->st.next_chunk == INT32_MAX) return NVFP4KV_ESTATE;
   State s = c->st;   // planned state, committed only if the launch succeeds
   const int32_t to_sink = n_frames < cfg.sink_frames - s.sink_used
                               ? n_frames
