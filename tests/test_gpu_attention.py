@@ -127,6 +127,31 @@ def test_wan_shaped_workloads_whole_output(ops, name):
     run_case(ops, cache, model, q, ko, vo, wl.softmax_scale, what=name)
 
 
+@pytest.mark.parametrize("fmt", [dict(), dict(k_smooth=True, v_adaptive=True), dict(mxfp4=True)],
+                         ids=["nvfp4", "ksmooth-adaptive", "mxfp4"])
+def test_head_dim_64_at_scale(ops, fmt):
+    """head_dim 64 (4-wave workgroups of 128 queries, two per CU) at a size that cuts
+    most query blocks between workgroups: 16 heads, 2085 queries (a ragged last
+    block) over a full 2 + 8-frame cache of 1024-token frames appended as five
+    2-frame chunks (one eviction-free fill), every output against the oracle."""
+    from gpu_util import dev, host, check_attention
+    H, D, T_f, sink, window, n_q = 16, 64, 1024, 2, 8, 2085
+    rng = np.random.default_rng(77)
+    cache = ops.KVCache(H, D, T_f, sink, window, **fmt)
+    model = CacheModel(H, D, T_f, sink, window, **fmt)
+    for _ in range(5):
+        k, v = rand_bits(rng, (H, 2 * T_f, D)), rand_bits(rng, (H, 2 * T_f, D))
+        cache.append(dev(k), dev(v), 2)
+        model.append(k, v)
+    assert model.n_tokens() == (sink + window) * T_f
+    q, ko, vo = (rand_bits(rng, (H, n_q, D)) for _ in range(3))
+    out = host(cache.attention(dev(q), dev(ko), dev(vo), 0.125))
+    ck, cv = model.dequantized_kv()
+    want = chunk_attention_ref(q, ko, vo, ck, cv, 0.125)
+    check_attention(out, want, f"D64 at scale {fmt}")
+    cache.close()
+
+
 def test_attention_deterministic(ops):
     from gpu_util import dev, host
     rng = np.random.default_rng(6)
