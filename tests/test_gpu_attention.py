@@ -127,6 +127,28 @@ def test_wan_shaped_workloads_whole_output(ops, name):
     run_case(ops, cache, model, q, ko, vo, wl.softmax_scale, what=name)
 
 
+def test_wan13b_k_smoothing_adaptive_whole_output(ops):
+    """The 1.3B-shaped workload over a cache with K-smoothing and adaptive V scales
+    (the configuration the bench times as wan13b_k_smooth_v_adaptive): every output
+    of every head against the oracle."""
+    from gpu_util import dev, host, check_attention
+    wl = W.WORKLOADS["wan13b"]
+    cache = ops.KVCache(wl.n_heads, wl.head_dim, wl.tokens_per_frame, wl.sink_frames, wl.window_frames,
+                        k_smooth=True, v_adaptive=True)
+    model = CacheModel(wl.n_heads, wl.head_dim, wl.tokens_per_frame, wl.sink_frames, wl.window_frames,
+                       k_smooth=True, v_adaptive=True)
+    for c in range(wl.n_cache_chunks):
+        k, v = W.clean_chunk(wl, c)
+        cache.append(dev(k), dev(v), wl.chunk_frames)
+        model.append(k, v)
+    q, ko, vo = W.noisy_chunk(wl, wl.n_cache_chunks)
+    out = host(cache.attention(dev(q), dev(ko), dev(vo), wl.softmax_scale))
+    ck, cv = model.dequantized_kv()
+    want = chunk_attention_ref(q, ko, vo, ck, cv, wl.softmax_scale)
+    check_attention(out, want, "wan13b k-smoothing + adaptive V")
+    cache.close()
+
+
 @pytest.mark.parametrize("fmt", [dict(), dict(k_smooth=True, v_adaptive=True), dict(mxfp4=True)],
                          ids=["nvfp4", "ksmooth-adaptive", "mxfp4"])
 def test_head_dim_64_at_scale(ops, fmt):
