@@ -253,3 +253,16 @@ def test_mx_scaled_qk_wan13b_whole_output(ops):
                                 wl.window_frames, chunks)
     q, ko, vo = W.noisy_chunk(wl, wl.n_cache_chunks)
     run_scaled(cache, model, q, ko, vo, wl.softmax_scale, what="mx scaled-qk wan13b")
+
+
+def test_mx_scaled_qk_head_dim_64_at_scale(ops):
+    """head_dim 64 with the MX-scaled QK^T at a size that cuts most query blocks
+    between workgroups (16 heads, 2085 queries over a full 2 + 8-frame cache of
+    1024-token frames): every output of every head."""
+    rng = np.random.default_rng(78)
+    H, D, T_f, sink, window = 16, 64, 1024, 2, 8
+    chunks = [(rand_bits(rng, (H, 2 * T_f, D)), rand_bits(rng, (H, 2 * T_f, D))) for _ in range(5)]
+    cache, model = build_scaled(ops, H, D, T_f, sink, window, chunks)
+    assert model.n_tokens() == (sink + window) * T_f
+    q, ko, vo = (rand_bits(rng, (H, 2085, D)) for _ in range(3))
+    run_scaled(cache, model, q, ko, vo, 0.125, what="mx scaled-qk D64 at scale")
