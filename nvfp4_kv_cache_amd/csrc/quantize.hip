@@ -203,10 +203,10 @@ __device__ __forceinline__ uint32_t cvt_fp4(uint32_t old, float a, float b) {
   return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(old, a, b, 1.0f, SEL);
 }
 
-// Adaptive block scale (V in the cache): squared error of encoding one token's
-// block with scale byte sc, sum over the 16 elements in order of
-// (|x| - value * eff)^2 with eff = E4M3(sc) * s_t, every step an fp32 operation
-// (no contraction: the choice must match the recipe bit for bit).
+// Adaptive block scale (V in the cache), token by token: squared error of encoding one
+// token's block with scale byte sc, summed over its 16 elements in order of
+// (|x| - value * eff)^2 with eff = E4M3(sc) * s_t, every step an fp32 operation (no
+// contraction: the choice must match the recipe bit for bit).
 template <bool SCALED>
 __device__ __forceinline__ float block_sq_error(const float (&x)[16], uint32_t sc, const TensorConsts &tc,
                                                 const float2 *tab) {
@@ -234,6 +234,44 @@ __device__ __forceinline__ uint32_t choose_scale46(const float (&x)[16], float a
   const uint32_t sc4 = scale_code<4>(amax, tc);
   if (sc4 == sc6) return sc6;
   return block_sq_error<SCALED>(x, sc4, tc, tab) < block_sq_error<SCALED>(x, sc6, tc, tab) ? sc4 : sc6;
+}
+
+// The same choice, one token pair (2*SEL, 2*SEL+1) of an octet at a time, keeping the
+// codes: both candidates' codes go straight into byte SEL of their own set of the 16
+// transposed words (o6, o4), each token's two errors are summed exactly as above
+// (element order, no contraction), and keep4 collects the nibbles of the tokens whose
+// 4-candidate won.
+template <int SEL, bool SCALED>
+__device__ __forceinline__ void adaptive_pair(const float (&xa)[16], const float (&xb)[16], float ma, float mb,
+                                              const TensorConsts &tc, const float2 *tab, uint32_t (&o6)[16],
+                                              uint32_t (&o4)[16], uint32_t &keep4, uint32_t &sca,
+                                              uint32_t &scb) {
+#pragma clang fp contract(off)
+  const uint32_t a6 = scale_code(ma, tc), b6 = scale_code(mb, tc);
+  const uint32_t a4 = scale_code<4>(ma, tc), b4 = scale_code<4>(mb, tc);
+  const float2 da6 = tab[a6], db6 = tab[b6], da4 = tab[a4], db4 = tab[b4];
+  const float ea6 = __builtin_amdgcn_cvt_f32_fp8(a6, 0) * tc.st, eb6 = __builtin_amdgcn_cvt_f32_fp8(b6, 0) * tc.st;
+  const float ea4 = __builtin_amdgcn_cvt_f32_fp8(a4, 0) * tc.st, eb4 = __builtin_amdgcn_cvt_f32_fp8(b4, 0) * tc.st;
+  float ra6 = 0.0f, rb6 = 0.0f, ra4 = 0.0f, rb4 = 0.0f;
+#pragma unroll
+  for (int d = 0; d < 16; ++d) {
+    o6[d] = cvt_fp4<SEL>(o6[d], quot<SCALED>(xa[d], da6.x, da6.y, tc.xs), quot<SCALED>(xb[d], db6.x, db6.y, tc.xs));
+    const auto v6 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(o6[d], 1.0f, SEL);
+    const float pa6 = fabsf(xa[d]) - fabsf(v6[0]) * ea6;
+    ra6 = ra6 + pa6 * pa6;
+    const float pb6 = fabsf(xb[d]) - fabsf(v6[1]) * eb6;
+    rb6 = rb6 + pb6 * pb6;
+    o4[d] = cvt_fp4<SEL>(o4[d], quot<SCALED>(xa[d], da4.x, da4.y, tc.xs), quot<SCALED>(xb[d], db4.x, db4.y, tc.xs));
+    const auto v4 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(o4[d], 1.0f, SEL);
+    const float pa4 = fabsf(xa[d]) - fabsf(v4[0]) * ea4;
+    ra4 = ra4 + pa4 * pa4;
+    const float pb4 = fabsf(xb[d]) - fabsf(v4[1]) * eb4;
+    rb4 = rb4 + pb4 * pb4;
+  }
+  const bool wa = ra4 < ra6, wb = rb4 < rb6;
+  sca = wa ? a4 : a6;
+  scb = wb ? b4 : b6;
+  keep4 |= ((wa ? 0x0Fu : 0u) | (wb ? 0xF0u : 0u)) << (8 * SEL);
 }
 
 // Codec layout: one token's 16 values -> 8 bytes (element 2k in the low nibble).
@@ -322,7 +360,11 @@ __device__ __forceinline__ void item_canonical(const QuantArgs &a, const Octet &
 // Transposed item (V in the cache; full octets only): 16 words of 8 tokens, one per
 // d of the block, and the octet's 8 scale bytes of this block.  Token pairs are
 // taken in load order: scale bytes and divisors of a pair right before its codes.
-template <bool SCALED, bool ADAPT = false>
+// ADAPT (adaptive block scales): KEEP takes each token's codes from its winning
+// candidate's error pass (about a fifth fewer VALU operations, 32 words live instead
+// of 16); without it every token's scale byte is chosen first and the octet is then
+// encoded once more with the winners, for kernels that would spill the extra words.
+template <bool SCALED, bool ADAPT = false, bool KEEP = true>
 __device__ __forceinline__ void item_transposed(const QuantArgs &a, const Octet &o, int b,
                                                 const uint4 (&u)[kOctet][2],
                                                 const TensorConsts &tc, const float2 *tab,
@@ -333,50 +375,70 @@ __device__ __forceinline__ void item_transposed(const QuantArgs &a, const Octet 
   uint32_t out[16];
 #pragma unroll
   for (int d = 0; d < 16; ++d) out[d] = 0u;
-  // every scale byte and divisor first when the maxima are at hand, or (adaptive
-  // scales) after choosing each token's byte on its own, one token at a time
-  float2 dvp[kOctet];
-  const bool pre = bmax || ADAPT;
-  if (ADAPT) {
+  if constexpr (ADAPT && KEEP) {
+    uint32_t o4[16], keep4 = 0u;
 #pragma unroll
-    for (int j = 0; j < kOctet; ++j) {
-      float x[16];
-      unpack16(u[j], x);
-      const float m = bmax ? __uint_as_float(bmax[j] << 16) : absmax16(x);
-      sc[j] = choose_scale46<SCALED>(x, m, scale_code(m, tc), tc, tab);
+    for (int d = 0; d < 16; ++d) o4[d] = 0u;
+#define NVFP4KV_APAIR(SEL)                                                                               \
+    {                                                                                                    \
+      float xa[16], xb[16];                                                                              \
+      unpack16(u[2 * SEL], xa);                                                                          \
+      unpack16(u[2 * SEL + 1], xb);                                                                      \
+      const float ma = bmax ? __uint_as_float(bmax[2 * SEL] << 16) : absmax16(xa);                       \
+      const float mb = bmax ? __uint_as_float(bmax[2 * SEL + 1] << 16) : absmax16(xb);                   \
+      adaptive_pair<SEL, SCALED>(xa, xb, ma, mb, tc, tab, out, o4, keep4, sc[2 * SEL], sc[2 * SEL + 1]); \
     }
+    NVFP4KV_APAIR(0)
+    NVFP4KV_APAIR(1)
+    NVFP4KV_APAIR(2)
+    NVFP4KV_APAIR(3)
+#undef NVFP4KV_APAIR
 #pragma unroll
-    for (int j = 0; j < kOctet; ++j) dvp[j] = tab[sc[j]];
-  } else if (bmax) {
+    for (int d = 0; d < 16; ++d) out[d] = (o4[d] & keep4) | (out[d] & ~keep4);
+  } else {
+    // every scale byte and divisor first when the maxima are at hand, or (adaptive
+    // scales) after choosing each token's byte on its own, one token at a time
+    float2 dvp[kOctet];
+    const bool pre = bmax || ADAPT;
+    if (ADAPT) {
 #pragma unroll
-    for (int j = 0; j < kOctet; ++j) sc[j] = scale_code(__uint_as_float(bmax[j] << 16), tc);
+      for (int j = 0; j < kOctet; ++j) {
+        float x[16];
+        unpack16(u[j], x);
+        const float m = bmax ? __uint_as_float(bmax[j] << 16) : absmax16(x);
+        sc[j] = choose_scale46<SCALED>(x, m, scale_code(m, tc), tc, tab);
+      }
 #pragma unroll
-    for (int j = 0; j < kOctet; ++j) dvp[j] = tab[sc[j]];
-  }
-#define NVFP4KV_PAIR(SEL)                                                             \
-  {                                                                                   \
-    float xa[16], xb[16];                                                             \
-    unpack16(u[2 * SEL], xa);                                                         \
-    unpack16(u[2 * SEL + 1], xb);                                                     \
-    float2 da, db;                                                                    \
-    if (pre) {                                                                        \
-      da = dvp[2 * SEL];                                                              \
-      db = dvp[2 * SEL + 1];                                                          \
-    } else {                                                                          \
-      const float ma = bmax ? __uint_as_float(bmax[2 * SEL] << 16) : absmax16(xa);    \
-      const float mb = bmax ? __uint_as_float(bmax[2 * SEL + 1] << 16) : absmax16(xb); \
-      sc[2 * SEL] = scale_code(ma, tc);                                               \
-      sc[2 * SEL + 1] = scale_code(mb, tc);                                           \
-      da = tab[sc[2 * SEL]];                                                          \
-      db = tab[sc[2 * SEL + 1]];                                                      \
-    }                                                                                 \
-    encode_pair_transposed<SEL, SCALED>(xa, xb, da.x, da.y, db.x, db.y, tc.xs, out);  \
-  }
-  NVFP4KV_PAIR(0)
-  NVFP4KV_PAIR(1)
-  NVFP4KV_PAIR(2)
-  NVFP4KV_PAIR(3)
+      for (int j = 0; j < kOctet; ++j) dvp[j] = tab[sc[j]];
+    } else if (bmax) {
+#pragma unroll
+      for (int j = 0; j < kOctet; ++j) sc[j] = scale_code(__uint_as_float(bmax[j] << 16), tc);
+#pragma unroll
+      for (int j = 0; j < kOctet; ++j) dvp[j] = tab[sc[j]];
+    }
+#define NVFP4KV_PAIR(SEL)                                                              \
+    {                                                                                  \
+      float xa[16], xb[16];                                                            \
+      unpack16(u[2 * SEL], xa);                                                        \
+      unpack16(u[2 * SEL + 1], xb);                                                    \
+      float2 da, db;                                                                   \
+      if (pre) {                                                                       \
+        da = dvp[2 * SEL];                                                             \
+        db = dvp[2 * SEL + 1];                                                         \
+      } else {                                                                         \
+        sc[2 * SEL] = scale_code(absmax16(xa), tc);                                    \
+        sc[2 * SEL + 1] = scale_code(absmax16(xb), tc);                                \
+        da = tab[sc[2 * SEL]];                                                         \
+        db = tab[sc[2 * SEL + 1]];                                                     \
+      }                                                                                \
+      encode_pair_transposed<SEL, SCALED>(xa, xb, da.x, da.y, db.x, db.y, tc.xs, out); \
+    }
+    NVFP4KV_PAIR(0)
+    NVFP4KV_PAIR(1)
+    NVFP4KV_PAIR(2)
+    NVFP4KV_PAIR(3)
 #undef NVFP4KV_PAIR
+  }
   if (o.nvalid == kOctet) {
     uint8_t *dst = qt.codes + (int64_t(o.h) * a.D + 16 * b) * (a.rows / 2) + o.row / 2;
 #pragma unroll
@@ -549,7 +611,7 @@ __global__ __launch_bounds__(kQuantThreads) void quantize_encode_kernel(QuantArg
       const bool tr = qt.transposed != 0;
       if (tc.xs == 1.0f) {
         if (tr) {
-          if (OPT && qt.adaptive) item_transposed<false, OPT>(a, oc, b, u, tc, tab);
+          if (OPT && qt.adaptive) item_transposed<false, OPT, false>(a, oc, b, u, tc, tab);
           else item_transposed<false>(a, oc, b, u, tc, tab);
         } else {
           if (OPT && qt.mean) item_canonical<false, OPT>(a, oc, b, u, tc, tab);
@@ -557,7 +619,7 @@ __global__ __launch_bounds__(kQuantThreads) void quantize_encode_kernel(QuantArg
         }
       } else {
         if (tr) {
-          if (OPT && qt.adaptive) item_transposed<true, OPT>(a, oc, b, u, tc, tab);
+          if (OPT && qt.adaptive) item_transposed<true, OPT, false>(a, oc, b, u, tc, tab);
           else item_transposed<true>(a, oc, b, u, tc, tab);
         } else {
           if (OPT && qt.mean) item_canonical<true, OPT>(a, oc, b, u, tc, tab);
@@ -1372,8 +1434,9 @@ __global__ __launch_bounds__(kQuantThreads, 2) void quantize_options_kernel(Quan
       else item_canonical<true>(a, oc, b, u, tc, sh.tab, bm);
     }
   } else {
-    if (tc.xs == 1.0f) item_transposed<false, VA>(a, oc, b, u, tc, sh.tab, bm);
-    else item_transposed<true, VA>(a, oc, b, u, tc, sh.tab, bm);
+    // with K-smoothing the kernel holds more registers elsewhere: kept codes would spill
+    if (tc.xs == 1.0f) item_transposed<false, VA, !KS>(a, oc, b, u, tc, sh.tab, bm);
+    else item_transposed<true, VA, !KS>(a, oc, b, u, tc, sh.tab, bm);
   }
 }
 

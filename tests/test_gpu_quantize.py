@@ -180,6 +180,46 @@ def test_append_extreme_and_special_chunks(ops, D):
         assert_codec_equal((host(vc), host(vs), host(sv)[0]), quantize_ref(v), f"D{D} chunk {c} V")
 
 
+@pytest.mark.parametrize("k_smooth", [False, True])
+def test_append_adaptive_v_extreme_and_special_chunks(ops, k_smooth):
+    """Adaptive-V appends (with and without K-smoothing, i.e. both encodes of the
+    single-pass kernel) of V tensors at extreme scales (s_t below 2^-80 and above
+    2^100, where the encoder rescales x and eff), a subnormal-only tensor, zeros of
+    both signs and special values, with a ragged quantizer tile: V's codes, scale
+    bytes and tensor scales equal the oracle's adaptive codec bit for bit."""
+    from gpu_util import dev, host
+    from oracle import channel_mean_ref
+    H, D, T_f, nf = 3, 128, 40, 2
+    T = nf * T_f
+    rng = np.random.default_rng(31 + k_smooth)
+    cache = ops.KVCache(H, D, T_f, 2, 8, k_smooth=k_smooth, v_adaptive=True)
+    assert cache.append_schedule(nf) == 4
+
+    def special():
+        x = rng.standard_normal((H, T, D)).astype(np.float32)
+        x[0, 0, :16] = 0.0
+        x[0, 1, :16] = -0.0
+        x[1, 2, :] *= 1e-6
+        x[1, 3, :] = np.float32(2.0 ** -130) * rng.integers(-50, 50, D)
+        x[2, 5, 0] = 4096.0
+        return W.f32_to_bf16_bits(x)
+
+    zero = np.zeros((H, T, D), dtype=np.uint16)
+    zero[:, ::3] = 0x8000
+    vs = [t4_bits(rng, (H, T, D), 1e-30), t4_bits(rng, (H, T, D), 1e33), special(),
+          np.full((H, T, D), 0x0001, dtype=np.uint16), zero]
+    chunks = [(t4_bits(rng, (H, T, D)), v) for v in vs]
+    for k, v in chunks:
+        cache.append(dev(k), dev(v), nf)
+    for c, (k, v) in enumerate(chunks):
+        kc, ks, vc, vs_, sk, sv = cache.export_chunk(c)
+        wk = quantize_ref(k, mean=channel_mean_ref(k)) if k_smooth else quantize_ref(k)
+        assert_codec_equal((host(kc), host(ks), host(sk)[0]), wk, f"ks={k_smooth} chunk {c} K")
+        assert_codec_equal((host(vc), host(vs_), host(sv)[0]), quantize_ref(v, adaptive=True),
+                           f"ks={k_smooth} chunk {c} V")
+    cache.close()
+
+
 def test_append_wait_fallback_help(ops):
     """With a zero poll limit, every workgroup of the single-pass append quantizer that
     does not find all maxima published on its first look helps: it computes missing
