@@ -220,6 +220,33 @@ def test_append_adaptive_v_extreme_and_special_chunks(ops, k_smooth):
     cache.close()
 
 
+@pytest.mark.parametrize("k_smooth,v_adaptive", [(False, False), (True, False), (False, True), (True, True)])
+def test_append_two_pass_large_chunk(ops, k_smooth, v_adaptive):
+    """A chunk whose tiles cannot all be resident at once (16 heads x 8192 tokens,
+    1024 workgroups) takes the two-pass quantizer (kvcache_append_schedule 2): the
+    channel means (K-smoothing), the amax pass and the encode pass with each option
+    combination, V written transposed into the cache; codes, scale bytes and tensor
+    scales equal the oracle's bit for bit."""
+    from gpu_util import dev, host
+    from oracle import channel_mean_ref
+    H, D, T_f, nf = 16, 128, 2048, 4
+    rng = np.random.default_rng(140 + 2 * k_smooth + v_adaptive)
+    cache = ops.KVCache(H, D, T_f, 1, 4, k_smooth=k_smooth, v_adaptive=v_adaptive)
+    assert cache.append_schedule(nf) == 2
+    kx = rng.standard_t(4, size=(H, nf * T_f, D)) * 1.5
+    if k_smooth:
+        kx = kx + rng.standard_normal((H, 1, D)) * 6
+    k = W.f32_to_bf16_bits(kx.astype(np.float32))
+    v = t4_bits(rng, (H, nf * T_f, D), 2.0)
+    cache.append(dev(k), dev(v), nf)
+    kc, ks, vc, vs, sk, sv = cache.export_chunk(0)
+    wk = quantize_ref(k, mean=channel_mean_ref(k)) if k_smooth else quantize_ref(k)
+    assert_codec_equal((host(kc), host(ks), host(sk)[0]), wk, f"two-pass ks={k_smooth} va={v_adaptive} K")
+    assert_codec_equal((host(vc), host(vs), host(sv)[0]), quantize_ref(v, adaptive=v_adaptive),
+                       f"two-pass ks={k_smooth} va={v_adaptive} V")
+    cache.close()
+
+
 def test_append_wait_fallback_help(ops):
     """With a zero poll limit, every workgroup of the single-pass append quantizer that
     does not find all maxima published on its first look helps: it computes missing
