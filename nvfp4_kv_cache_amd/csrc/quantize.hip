@@ -143,6 +143,15 @@ __device__ __forceinline__ uint32_t scale_code(float amax, const TensorConsts &t
   return uint32_t(uint16_t(p[0])) & 0xFFu;
 }
 
+// The same from a6 = RN(amax / 6) taken beforehand (amax_bits: the block maximum as
+// bf16 bits): the first quotient of either branch above is that correctly rounded one.
+__device__ __forceinline__ uint32_t scale_code_pre(uint32_t amax_bits, float a6, const TensorConsts &tc) {
+  const float bs = __uint_as_float(amax_bits << 16) >= tc.amin ? div_rn(a6, tc.st, tc.rst) : a6 / tc.st;
+  short2_ p = {0, 0};
+  p = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(p, fminf(bs, 448.0f), 0.0f, 1.0f, false);
+  return uint32_t(uint16_t(p[0])) & 0xFFu;
+}
+
 // Divisor entry of one scale byte: eff = E4M3(sc) * s_t (rounded as fp32, subnormals
 // included), then scaled by xs, and r = RN(1 / eff); r = 0 when eff == 0 (codes keep
 // only the signs).
@@ -167,6 +176,12 @@ __device__ __forceinline__ void unpack16(const uint4 (&u)[2], float (&x)[16]) {
     x[2 * k] = __uint_as_float(w[k] << 16);
     x[2 * k + 1] = __uint_as_float(w[k] & 0xFFFF0000u);
   }
+}
+
+// The same for a token already held as fp32.
+__device__ __forceinline__ void unpack16(const float (&xf)[16], float (&x)[16]) {
+#pragma unroll
+  for (int i = 0; i < 16; ++i) x[i] = xf[i];
 }
 
 // Element i (0..15) of one token's block as fp32 (exact), extracted where it is used.
@@ -309,11 +324,10 @@ struct Octet {
 // Canonical item: per token, block max -> scale byte -> divisor -> 8 code bytes.
 // MEAN: K-smoothing, the block's 16 channel means are subtracted first (fp32).
 // bmax (optional): the tokens' block maxima as bf16 bits, taken before s_t was known.
-template <bool SCALED, bool MEAN = false>
-__device__ __forceinline__ void item_canonical(const QuantArgs &a, const Octet &o, int b,
-                                               const uint4 (&u)[kOctet][2],
+template <bool SCALED, bool MEAN = false, typename U>
+__device__ __forceinline__ void item_canonical(const QuantArgs &a, const Octet &o, int b, const U &u,
                                                const TensorConsts &tc, const float2 *tab,
-                                               const uint32_t *bmax = nullptr) {
+                                               const uint32_t *bmax = nullptr, const float *pre6 = nullptr) {
   const QuantTensor &qt = a.t[o.tensor];
   const int nb = a.D >> 4;
   float mu[16];
@@ -334,7 +348,8 @@ __device__ __forceinline__ void item_canonical(const QuantArgs &a, const Octet &
   float2 dvp[kOctet];
   if (bmax) {
 #pragma unroll
-    for (int j = 0; j < kOctet; ++j) scp[j] = scale_code(__uint_as_float(bmax[j] << 16), tc);
+    for (int j = 0; j < kOctet; ++j)
+      scp[j] = pre6 ? scale_code_pre(bmax[j], pre6[j], tc) : scale_code(__uint_as_float(bmax[j] << 16), tc);
 #pragma unroll
     for (int j = 0; j < kOctet; ++j) dvp[j] = tab[scp[j]];
   }
@@ -364,11 +379,10 @@ __device__ __forceinline__ void item_canonical(const QuantArgs &a, const Octet &
 // candidate's error pass (about a fifth fewer VALU operations, 32 words live instead
 // of 16); without it every token's scale byte is chosen first and the octet is then
 // encoded once more with the winners, for kernels that would spill the extra words.
-template <bool SCALED, bool ADAPT = false, bool KEEP = true>
-__device__ __forceinline__ void item_transposed(const QuantArgs &a, const Octet &o, int b,
-                                                const uint4 (&u)[kOctet][2],
+template <bool SCALED, bool ADAPT = false, bool KEEP = true, typename U>
+__device__ __forceinline__ void item_transposed(const QuantArgs &a, const Octet &o, int b, const U &u,
                                                 const TensorConsts &tc, const float2 *tab,
-                                                const uint32_t *bmax = nullptr) {
+                                                const uint32_t *bmax = nullptr, const float *pre6 = nullptr) {
   const QuantTensor &qt = a.t[o.tensor];
   const int nb = a.D >> 4;
   uint32_t sc[kOctet];
@@ -412,7 +426,8 @@ __device__ __forceinline__ void item_transposed(const QuantArgs &a, const Octet 
       for (int j = 0; j < kOctet; ++j) dvp[j] = tab[sc[j]];
     } else if (bmax) {
 #pragma unroll
-      for (int j = 0; j < kOctet; ++j) sc[j] = scale_code(__uint_as_float(bmax[j] << 16), tc);
+      for (int j = 0; j < kOctet; ++j)
+        sc[j] = pre6 ? scale_code_pre(bmax[j], pre6[j], tc) : scale_code(__uint_as_float(bmax[j] << 16), tc);
 #pragma unroll
       for (int j = 0; j < kOctet; ++j) dvp[j] = tab[sc[j]];
     }
@@ -690,6 +705,18 @@ __global__ __launch_bounds__(kQuantThreads) void quantize_fused_kernel(QuantArgs
     bm[j] = block_max_bits(u[j]);
     mx = max(mx, bm[j]);
   }
+  // work that does not need s_t, done while the exchange is pending: the tokens as
+  // fp32 and the first quotient amax / 6 of each scale byte (kept in registers: the
+  // empty asm statements keep the compiler from moving them after the wait)
+  float xf[kOctet][16], a6[kOctet];
+#pragma unroll
+  for (int j = 0; j < kOctet; ++j) {
+    unpack16(u[j], xf[j]);
+    a6[j] = __uint_as_float(bm[j] << 16) / 6.0f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) asm volatile("" : "+v"(xf[j][i]));
+    asm volatile("" : "+v"(a6[j]));
+  }
   uint32_t mk = wave_max_u32(oc.tensor == 0 ? mx : 0u);
   uint32_t mv = wave_max_u32(oc.tensor == 1 ? mx : 0u);
   if (lane == 0) {
@@ -799,11 +826,11 @@ __global__ __launch_bounds__(kQuantThreads) void quantize_fused_kernel(QuantArgs
     const float2 *tab = s_tab[oc.tensor];
     const bool tr = a.t[oc.tensor].transposed != 0;
     if (tc.xs == 1.0f) {
-      if (tr) item_transposed<false>(a, oc, b, u, tc, tab, bm);
-      else item_canonical<false>(a, oc, b, u, tc, tab, bm);
+      if (tr) item_transposed<false>(a, oc, b, xf, tc, tab, bm, a6);
+      else item_canonical<false>(a, oc, b, xf, tc, tab, bm, a6);
     } else {
-      if (tr) item_transposed<true>(a, oc, b, u, tc, tab, bm);
-      else item_canonical<true>(a, oc, b, u, tc, tab, bm);
+      if (tr) item_transposed<true>(a, oc, b, xf, tc, tab, bm, a6);
+      else item_canonical<true>(a, oc, b, xf, tc, tab, bm, a6);
     }
   }
 }
