@@ -63,3 +63,16 @@ def test_underflowing_remainder_can_miss():
     q1 = rn32(F(float(q0)) - F(float(e)) * F(float(r)))
     want = rn32(F(float(x)) / F(float(b)))
     assert float(want) > 0.25 and float(q1) == 0.25
+
+
+def test_scale_byte_first_quotient_matches_ieee(tmp_path):
+    # The single-pass append takes RN(amax / 6) with an IEEE division before the
+    # maxima exchange; the scale byte's Markstein path formed the same quotient with
+    # two corrections.  Every finite bf16 magnitude >= 2^-90 (and zero) must agree.
+    exe = str(tmp_path / "scale_quotient")
+    src = os.path.join(HERE, "host_checks", "scale_quotient.c")
+    subprocess.run(["gcc", "-O2", "-std=c99", "-ffp-contract=off", "-o", exe, src, "-lm"], check=True)
+    out = subprocess.run([exe], capture_output=True, text=True)
+    print(out.stdout)
+    assert out.returncode == 0, out.stdout
+    assert "27905 magnitudes checked, 0 mismatches" in out.stdout
