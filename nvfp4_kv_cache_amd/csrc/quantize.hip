@@ -7,19 +7,24 @@
 // E4M3 (nearest, ties to even, saturating at 448); eff = E4M3(bs) * s_t;
 // code = E2M1(|x| / eff) (nearest, ties to even, saturating at 6) with x's sign.
 //
-// Two schedules.  The tensor scale needs the amax of the whole chunk tensor (all
+// Schedules.  The tensor scale needs the amax of the whole chunk tensor (all
 // heads) before any block can be encoded.
 //   * Cache appends (quantize_fused_kernel, one pass): every workgroup of a grid
 //     that is resident all at once (the launcher checks the occupancy) loads its
 //     tile into registers, publishes its maxima in an epoch-tagged workspace slot,
-//     waits (bounded) for every slot of its tensor (K or V) and encodes from the
-//     registers, so the chunk is read once.  No cooperative launch is needed.
-//   * The standalone codec, and appends with K-smoothing or adaptive V scales,
-//     whose workspace cannot carry epochs or which need the channel means first:
-//     quantize_amax_kernel streams K and V once and writes one partial maximum per
-//     workgroup (no atomics); quantize_encode_kernel reduces the partials, then
-//     re-reads its tiles (the chunk, 28.8 MB for the 1.3B shape, is still in the
-//     256 MB Infinity Cache) and writes codes and scales.
+//     waits (bounded, then helping) for every slot of its tensor (K or V) and
+//     encodes from the registers, so the chunk is read once.  While it waits it
+//     already holds its values as fp32 and each scale byte's first quotient, so
+//     only the s_t-dependent steps follow the wait.  No cooperative launch.
+//   * Cache appends with K-smoothing and/or adaptive V scales take their own
+//     single-pass kernel (quantize_options_kernel, below), with further exchanges
+//     for the channel means and the heads' maxima of K minus its means.
+//   * The standalone codec (its workspace cannot carry epochs), and appends whose
+//     grid would not be resident at once: quantize_amax_kernel streams K and V once
+//     and writes one partial maximum per workgroup (no atomics);
+//     quantize_encode_kernel reduces the partials, then re-reads its tiles (the
+//     chunk, 28.8 MB for the 1.3B shape, is still in the 256 MB Infinity Cache)
+//     and writes codes and scales.
 //
 // Exact encoding without an IEEE division per element.  The gfx950 converts
 // v_cvt_scalef32_pk_fp4_f32 / _fp8_f32 (scale 1.0) round to nearest-even and
